@@ -1,0 +1,64 @@
+// Internal definitions shared by the dcpmla HIP sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dcpmla.h"
+
+namespace dcpmla {
+
+constexpr int kDqk = 576;          // 512 latent + 64 rope
+constexpr int kDv = 512;
+constexpr int kRopeDims = kDqk - kDv;
+constexpr int kStageTokens = 32;   // tokens per LDS stage = one 32x32 MFMA score tile
+constexpr int kWaveRows = 32;      // head-rows (M) per wave
+constexpr int kWaves = 4;          // waves per attention workgroup
+constexpr int kTileRows = kWaveRows * kWaves;  // head-rows per workgroup (M tile)
+constexpr int kThreads = kWaves * 64;
+constexpr int kSlots = 2;          // partial slots per persistent workgroup
+
+// Work buffer layout (int32): [0] total units U; [1 .. B+1] unit_base[b]
+// (prefix of n_mtiles * stages over sequences, unit_base[B] = U);
+// [B+2 .. 2B+2) stages[b]; [2B+2 .. 3B+2) longest rank-local row length lmax[b];
+// [3B+2 .. 4B+2) the verify row (b*qlen + i) that has that length.  A unit is
+// one 32-token stage of one (sequence, head-row tile).
+__host__ __device__ inline int64_t work_ints(int batch) { return 4 * (int64_t)batch + 2; }
+__host__ __device__ inline int work_unit_base_off() { return 1; }
+__host__ __device__ inline int work_stages_off(int batch) { return batch + 2; }
+__host__ __device__ inline int work_lmax_off(int batch) { return 2 * batch + 2; }
+__host__ __device__ inline int work_lrow_off(int batch) { return 3 * batch + 2; }
+
+__host__ __device__ inline int subpage_size(int block_size) {
+  int low = block_size & (-block_size);
+  return low < 128 ? low : 128;
+}
+
+__host__ __device__ inline int n_mtiles(int qlen, int heads) {
+  int m = qlen * heads;
+  return (m + kTileRows - 1) / kTileRows;
+}
+
+// Workspace: o partials [groups][kSlots][kTileRows][kDv] float, then
+// lse2 partials [groups][kSlots][kTileRows] float.
+__host__ __device__ inline int64_t ws_o_floats(int groups) {
+  return (int64_t)groups * kSlots * kTileRows * kDv;
+}
+__host__ __device__ inline int64_t ws_bytes(int groups) {
+  return (ws_o_floats(groups) + (int64_t)groups * kSlots * kTileRows) * 4;
+}
+
+// Workgroups that actually take work: every one gets at least about
+// kMinUnitsPerGroup stages, because each split costs a 256 KiB fp32 partial
+// (written here, read back by the segment merge).
+constexpr int64_t kMinUnitsPerGroup = 8;
+__host__ __device__ inline int64_t effective_groups(int64_t launched, int64_t U) {
+  int64_t g = (U + kMinUnitsPerGroup - 1) / kMinUnitsPerGroup;
+  if (g < 1) g = 1;
+  return g < launched ? g : launched;
+}
+
+// start unit of persistent workgroup w out of G over U units
+__host__ __device__ inline int64_t group_lo(int64_t w, int64_t U, int64_t G) { return (w * U) / G; }
+
+}  // namespace dcpmla

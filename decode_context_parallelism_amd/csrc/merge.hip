@@ -1,0 +1,227 @@
+// LSE merges: split-KV segments (base-2 statistics -> BF16 output plus
+// natural-log LSE) and DCP ranks (natural-log LSE -> BF16 output).
+//
+// Segment merge: "[ROCm][MLA][DCP] Support causal multi-token verification"
+// (vLLM PR #51705), "Implementation" item 3 and its commit message (decode
+// LSE is natural-log; the segment merge converts the kernel's base-2
+// statistics).  Rank merge: "Context Parallel Guide (PCP & DCP)",
+// enable_project_before_merge (a per-(token, head) scalar weight and a
+// cross-rank sum); an empty rank carries LSE = -inf and adds nothing.
+//
+// Layout of the work: one wave per output row, each lane owning 8 of the 512
+// value dims (16-byte loads and stores), so a row is two fully coalesced
+// 1 KiB (BF16) or 2 KiB (float) transactions per partial.
+#include "common.h"
+#include "launch.h"
+
+namespace dcpmla {
+
+namespace {
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ inline float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  const __bf16 x = (__bf16)a;
+  const __bf16 y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+__device__ inline uint4 pack_bf16x8(const float *v) {
+  return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                    pack_bf16x2(v[6], v[7]));
+}
+
+__device__ inline void unpack_bf16x8(uint4 u, float *v) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[2 * k] = bf16_to_f32(w[k] & 0xFFFFu);
+    v[2 * k + 1] = bf16_to_f32(w[k] >> 16);
+  }
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+}  // namespace
+
+__global__ void __launch_bounds__(256) merge_ranks_kernel(int W, int64_t rows,
+                                                          const uint4 *__restrict__ out_ranks,
+                                                          const float *__restrict__ lse_ranks,
+                                                          uint4 *__restrict__ out,
+                                                          float *__restrict__ lse) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  float mx = kNegInf;
+  for (int r = 0; r < W; ++r) mx = fmaxf(mx, lse_ranks[(int64_t)r * rows + row]);
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float L = kNegInf;
+  if (mx > kNegInf) {
+    float z = 0.f;
+    for (int r = 0; r < W; ++r) {
+      const float l = lse_ranks[(int64_t)r * rows + row];
+      if (!(l > kNegInf)) continue;
+      const float w = fast_exp2((l - mx) * kLog2e);
+      z += w;
+      float v[8];
+      unpack_bf16x8(out_ranks[((int64_t)r * rows + row) * 64 + lane], v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] += w * v[k];
+    }
+    const float inv = 1.f / z;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] *= inv;
+    L = mx + fast_log2(z) * kLn2;
+  }
+  out[row * 64 + lane] = pack_bf16x8(acc);
+  if (lane == 0) lse[row] = L;
+}
+
+__global__ void __launch_bounds__(256) merge_segments_dense_kernel(
+    int64_t rows, int nseg, const float4 *__restrict__ o_seg, const float *__restrict__ lse2_seg,
+    uint4 *__restrict__ out, float *__restrict__ lse) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float *l2 = lse2_seg + row * nseg;
+  float mx = kNegInf;
+  for (int s = 0; s < nseg; ++s) mx = fmaxf(mx, l2[s]);
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float L = kNegInf;
+  if (mx > kNegInf) {
+    float z = 0.f;
+    for (int s = 0; s < nseg; ++s) {
+      const float l = l2[s];
+      if (!(l > kNegInf)) continue;
+      const float w = fast_exp2(l - mx);
+      z += w;
+      const float4 *src = o_seg + ((row * nseg + s) * kDv) / 4 + 2 * lane;
+      const float4 a = src[0], b = src[1];
+      acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
+      acc[4] += w * b.x; acc[5] += w * b.y; acc[6] += w * b.z; acc[7] += w * b.w;
+    }
+    const float inv = 1.f / z;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] *= inv;
+    L = (mx + fast_log2(z)) * kLn2;
+  }
+  out[row * 64 + lane] = pack_bf16x8(acc);
+  if (lane == 0) lse[row] = L;
+}
+
+// Persistent layout: finish every (sequence, head-row tile) whose stages were
+// split over several workgroups, and give sequences with no rank-local token
+// their empty result.  Tiles finished inside one workgroup are left alone.
+__global__ void __launch_bounds__(256) merge_segments_kernel(
+    int B, int qlen, int heads, int n_mt, int G, const int32_t *__restrict__ work,
+    const float4 *__restrict__ ws_o, const float *__restrict__ ws_lse2, uint4 *__restrict__ out,
+    float *__restrict__ lse) {
+  __shared__ int s_src[1024];   // partial index (group * kSlots + slot) of each piece part
+  __shared__ int s_n;
+  const int b = blockIdx.x / n_mt;
+  const int mt = blockIdx.x - b * n_mt;
+  const int M = qlen * heads;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t U = work[0];
+  const int stages = work[work_stages_off(B) + b];
+  const int row0 = mt * kTileRows;
+  const int nrows = min(kTileRows, M - row0);
+  if (stages == 0) {
+    // no rank-local token for the whole sequence: O = 0, LSE = -inf
+    for (int r = wave; r < nrows; r += kWaves) {
+      const int64_t orow = (int64_t)b * M + row0 + r;
+      out[orow * 64 + lane] = make_uint4(0, 0, 0, 0);
+      if (lane == 0) lse[orow] = kNegInf;
+    }
+    return;
+  }
+  const int64_t Geff = effective_groups(G, U);
+  const int64_t u0 = (int64_t)work[work_unit_base_off() + b] + (int64_t)mt * stages;
+  const int64_t u1 = u0 + stages;
+  auto find_group = [&](int64_t u) {
+    int64_t w = (u * Geff) / U;
+    while (w + 1 < Geff && group_lo(w + 1, U, Geff) <= u) ++w;
+    while (w > 0 && group_lo(w, U, Geff) > u) --w;
+    return w;
+  };
+  const int64_t w0 = find_group(u0);
+  const int64_t w1 = find_group(u1 - 1);
+  if (w0 == w1) return;   // finished inside one workgroup
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int64_t w = w0; w <= w1 && n < 1024; ++w) {
+      const int64_t lo = group_lo(w, U, Geff), hi = group_lo(w + 1, U, Geff);
+      if (hi <= lo) continue;   // empty range: wrote nothing
+      const int slot = lo >= u0 ? 0 : 1;
+      s_src[n++] = (int)(w * kSlots + slot);
+    }
+    s_n = n;
+  }
+  __syncthreads();
+  const int n = s_n;
+  for (int r = wave; r < nrows; r += kWaves) {
+    float mx = kNegInf;
+    for (int k = 0; k < n; ++k) mx = fmaxf(mx, ws_lse2[(int64_t)s_src[k] * kTileRows + r]);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float L = kNegInf;
+    if (mx > kNegInf) {
+      float z = 0.f;
+      for (int k = 0; k < n; ++k) {
+        const int64_t pr = (int64_t)s_src[k] * kTileRows + r;
+        const float l = ws_lse2[pr];
+        if (!(l > kNegInf)) continue;
+        const float w = fast_exp2(l - mx);
+        z += w;
+        const float4 *src = ws_o + pr * (kDv / 4) + 2 * lane;
+        const float4 a = src[0], c = src[1];
+        acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
+        acc[4] += w * c.x; acc[5] += w * c.y; acc[6] += w * c.z; acc[7] += w * c.w;
+      }
+      const float inv = 1.f / z;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] *= inv;
+      L = (mx + fast_log2(z)) * kLn2;
+    }
+    const int64_t orow = (int64_t)b * M + row0 + r;
+    out[orow * 64 + lane] = pack_bf16x8(acc);
+    if (lane == 0) lse[orow] = L;
+  }
+}
+
+hipError_t launch_merge_ranks(int world, int64_t rows, const void *out_ranks,
+                              const float *lse_ranks, void *out, float *lse, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const int64_t blocks = (rows + 3) / 4;
+  hipLaunchKernelGGL(merge_ranks_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, world, rows,
+                     (const uint4 *)out_ranks, lse_ranks, (uint4 *)out, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_segments_dense(int64_t rows, int nseg, const float *o_seg,
+                                       const float *lse2_seg, void *out, float *lse,
+                                       hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const int64_t blocks = (rows + 3) / 4;
+  hipLaunchKernelGGL(merge_segments_dense_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     rows, nseg, (const float4 *)o_seg, lse2_seg, (uint4 *)out, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_segments(const dcpmla_geom &g, int groups, const dcpmla_meta &m,
+                                 const void *workspace, void *out_rank, float *lse_rank,
+                                 hipStream_t stream) {
+  const int n_mt = n_mtiles(g.qlen, g.num_heads);
+  const float *ws = (const float *)workspace;
+  hipLaunchKernelGGL(merge_segments_kernel, dim3(g.batch * n_mt), dim3(256), 0, stream, g.batch,
+                     g.qlen, g.num_heads, n_mt, groups, m.work, (const float4 *)ws,
+                     ws + ws_o_floats(groups), (uint4 *)out_rank, lse_rank);
+  return hipGetLastError();
+}
+
+}  // namespace dcpmla

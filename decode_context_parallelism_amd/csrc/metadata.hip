@@ -1,0 +1,135 @@
+// Verify-view builder: per-row causal boundary, rank-local length, bounded
+// subpage expansion, and the split-KV work partition.
+//
+// "[ROCm][MLA][DCP] Support causal multi-token verification" (vLLM PR
+// #51705), "Implementation" items 1, 2 and 5: each verification row gets its
+// own global causal boundary mapped to a rank-local KV length; physical blocks
+// are expanded into bounded subpages; row metadata lives in stable buffers
+// sized by a static bound.  The length formula is the one computed per query
+// in "[Spec decode] Support Kimi-K3 DCP with DSpark" (vLLM PR #52188), review
+// thread.
+#include "common.h"
+#include "launch.h"
+
+namespace dcpmla {
+
+__global__ void __launch_bounds__(256) meta_rows_kernel(
+    int W, int S, int block_size, int qlen, int max_blocks, int max_local_pages,
+    int64_t num_blocks, int rank, const int32_t *__restrict__ ctx_lens,
+    const int32_t *__restrict__ block_table, int32_t *__restrict__ row_len,
+    int32_t *__restrict__ page_table, int32_t *__restrict__ last_len, int32_t *__restrict__ err) {
+  const int row = blockIdx.x;
+  const int b = row / qlen;
+  const int i = row - b * qlen;
+  const int P = subpage_size(block_size);
+  const int ppb = block_size / P;
+  __shared__ int s_np, s_err, s_first_bad;
+  __shared__ int64_t s_len;
+  if (threadIdx.x == 0) {
+    const int64_t ctx = ctx_lens[b];
+    int e = 0;
+    int64_t g = ctx - qlen + 1 + i;        // global causal boundary of verify row i
+    if (ctx < qlen) e |= DCPMLA_ERR_CTX_LT_QLEN;
+    if (g < 0) g = 0;
+    const int64_t span = (int64_t)W * S;
+    int64_t rem = g % span - (int64_t)rank * S;
+    rem = rem < 0 ? 0 : (rem > S ? S : rem);
+    int64_t len = (g / span) * S + rem;    // rank-local tokens visible to the row
+    int64_t np = (len + P - 1) / P;
+    const int64_t cap = (int64_t)max_blocks * ppb;
+    if (np > cap) { np = cap; e |= DCPMLA_ERR_TABLE_CAPACITY; }
+    if (np > max_local_pages) { np = max_local_pages; e |= DCPMLA_ERR_LOCAL_PAGES; }
+    if (len > np * P) len = np * P;
+    s_np = (int)np;
+    s_len = len;
+    s_err = e;
+    s_first_bad = (int)np;
+  }
+  __syncthreads();
+  int np = s_np;
+  const int32_t *bt = block_table + (int64_t)b * max_blocks;
+  // every block id the row uses must name a block of the pool; the load is
+  // bounded by the row's own page count, so unused (poisoned) entries are
+  // never read
+  for (int j = threadIdx.x; j < np; j += blockDim.x) {
+    const int32_t blk = bt[j / ppb];
+    if (blk < 0 || (int64_t)blk >= num_blocks) atomicMin(&s_first_bad, j);
+  }
+  __syncthreads();
+  const int first_bad = s_first_bad;
+  if (first_bad < np) np = first_bad;
+  int64_t len = s_len;
+  if (len > (int64_t)np * P) len = (int64_t)np * P;
+  int32_t *pt = page_table + (int64_t)row * max_local_pages;
+  for (int j = threadIdx.x; j < max_local_pages; j += blockDim.x) {
+    int32_t v = -1;
+    if (j < np) v = bt[j / ppb] * ppb + (j % ppb);
+    pt[j] = v;
+  }
+  if (threadIdx.x == 0) {
+    row_len[row] = (int32_t)len;
+    last_len[row] = np ? (int32_t)(len - (int64_t)(np - 1) * P) : 0;
+    const int e = s_err | (first_bad < s_np ? DCPMLA_ERR_BLOCK_ID : 0);
+    if (e) atomicOr(err, e);
+  }
+}
+
+// One workgroup: longest row per sequence, stages, and the unit prefix.
+__global__ void __launch_bounds__(256) meta_work_kernel(int B, int qlen, int n_mt,
+                                                        const int32_t *__restrict__ row_len,
+                                                        int32_t *__restrict__ work) {
+  __shared__ int s_scan[256];
+  __shared__ int s_carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  for (int base = 0; base < B; base += 256) {
+    const int b = base + tid;
+    int units = 0;
+    if (b < B) {
+      int lm = 0, lrow = b * qlen + qlen - 1;
+      for (int i = 0; i < qlen; ++i) {
+        const int v = row_len[b * qlen + i];
+        if (v > lm) { lm = v; lrow = b * qlen + i; }
+      }
+      const int st = (lm + kStageTokens - 1) / kStageTokens;
+      work[work_lmax_off(B) + b] = lm;
+      work[work_lrow_off(B) + b] = lrow;
+      work[work_stages_off(B) + b] = st;
+      units = st * n_mt;
+    }
+    s_scan[tid] = units;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int v = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += v;
+      __syncthreads();
+    }
+    if (b < B) work[work_unit_base_off() + b] = s_carry + s_scan[tid] - units;
+    __syncthreads();
+    if (tid == 255) s_carry += s_scan[255];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    work[work_unit_base_off() + B] = s_carry;
+    work[0] = s_carry;
+  }
+}
+
+hipError_t launch_build_metadata(const dcpmla_geom &g, int rank, const int32_t *ctx_lens,
+                                 const int32_t *block_table, const dcpmla_meta &m,
+                                 hipStream_t stream) {
+  const int rows = g.batch * g.qlen;
+  hipLaunchKernelGGL(meta_rows_kernel, dim3(rows), dim3(256), 0, stream, g.dcp_world,
+                     g.interleave, g.block_size, g.qlen, g.max_blocks_per_seq, g.max_local_pages,
+                     g.num_blocks, rank, ctx_lens, block_table, m.row_local_len, m.page_table,
+                     m.last_page_len, m.err);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(meta_work_kernel, dim3(1), dim3(256), 0, stream, g.batch, g.qlen,
+                     n_mtiles(g.qlen, g.num_heads), m.row_local_len, m.work);
+  return hipGetLastError();
+}
+
+}  // namespace dcpmla

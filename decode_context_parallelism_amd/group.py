@@ -1,0 +1,79 @@
+"""One GPU playing every rank of a DCP group.
+
+Each rank keeps its own KV pool and verify-view buffers in HBM; the ranks run
+one after another on one stream (KV write, metadata, segmented attention and
+segment merge per rank), and the cross-rank LSE merge then reads all W
+partials from HBM.  In a real deployment each rank is a different GPU and the
+merge input arrives through an all-to-all; the per-rank work is identical.
+
+Buffer layout (all contiguous, allocated once):
+  pools[r]     [num_blocks, block_size, 576]  cache elements (uint8 FP8 codes
+               or bfloat16), filled with a NaN pattern until written, so a
+               read of an unwritten slot cannot go unnoticed
+  meta[r]      verify view of rank r (see ``ops.RankMetadata``)
+  workspace    split-KV partials, shared by the ranks in turn
+  out_ranks    [W, B, qlen, H, 512] bfloat16, lse_ranks [W, B, qlen, H] float
+  out, lse     merged result
+"""
+from __future__ import annotations
+
+import torch
+
+from . import ops
+
+_NAN_FILL = {"fp8_e4m3": 0x7F, "bf16": float("nan")}
+
+
+class DcpGroup:
+    def __init__(self, geom: ops.Geometry, device="cuda"):
+        self.geom = geom
+        self.device = device
+        W, B, q, H = geom.dcp_world, geom.batch, geom.qlen, geom.num_heads
+        self.pools = []
+        for _ in range(W):
+            pool = torch.empty(geom.num_blocks, geom.block_size, ops.D_QK,
+                               dtype=geom.kv_torch_dtype, device=device)
+            pool.fill_(_NAN_FILL[geom.kv_dtype])
+            self.pools.append(pool)
+        self.meta = [ops.RankMetadata(geom, device) for _ in range(W)]
+        self.workspace = ops.alloc_workspace(geom, device)
+        self.out_ranks = torch.empty(W, B, q, H, ops.D_V, dtype=torch.bfloat16, device=device)
+        self.lse_ranks = torch.empty(W, B, q, H, dtype=torch.float32, device=device)
+        self.out = torch.empty(B, q, H, ops.D_V, dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty(B, q, H, dtype=torch.float32, device=device)
+        self.kv_err = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def write_kv(self, seq_ids, positions, latents, block_table, stream=None):
+        """Scatter global latent rows into every rank's pool; returns slot mappings [W, T]."""
+        T = seq_ids.shape[0]
+        slots = torch.empty(self.geom.dcp_world, T, dtype=torch.int32, device=self.device)
+        for r in range(self.geom.dcp_world):
+            ops.write_kv(self.geom, r, seq_ids, positions, latents, block_table, self.pools[r],
+                         slots[r], self.kv_err, stream)
+        return slots
+
+    def build_metadata(self, ctx_lens, block_table, stream=None):
+        for r in range(self.geom.dcp_world):
+            ops.build_metadata(self.geom, r, ctx_lens, block_table, self.meta[r], stream)
+
+    def rank_attention(self, r, q, kv_scale, softmax_scale, stream=None):
+        ops.rank_attention(self.geom, q, self.pools[r], kv_scale, softmax_scale, self.meta[r],
+                           self.workspace, self.out_ranks[r], self.lse_ranks[r], stream)
+
+    def merge(self, stream=None):
+        ops.merge_ranks(self.out_ranks, self.lse_ranks, self.out, self.lse, stream)
+
+    def forward(self, q, ctx_lens, block_table, kv_scale, softmax_scale, stream=None):
+        """One verification step: metadata, every rank's attention, cross-rank merge."""
+        self.build_metadata(ctx_lens, block_table, stream)
+        for r in range(self.geom.dcp_world):
+            self.rank_attention(r, q, kv_scale, softmax_scale, stream)
+        self.merge(stream)
+        return self.out, self.lse
+
+    def errors(self):
+        """OR of every device error word (synchronises)."""
+        e = int(self.kv_err.item())
+        for m in self.meta:
+            e |= int(m.err.item())
+        return e

@@ -122,8 +122,13 @@ def _workers() -> int:
 
 def make_workload(*, name: str, world: int, interleave: int, batch: int, qlen: int, heads: int,
                   block_size: int, kv_format: str, ctx, table: str, max_local_pages: int,
-                  seed: int, extra_cols: int = 1, softmax_scale: float | None = None) -> Workload:
-    """Build one seeded workload.  ``ctx`` is a spec tuple or explicit lengths."""
+                  seed: int, extra_cols: int = 1, softmax_scale: float | None = None,
+                  with_kv: bool = True) -> Workload:
+    """Build one seeded workload.  ``ctx`` is a spec tuple or explicit lengths.
+
+    ``with_kv=False`` skips the latent rows (``kv`` is an empty array and
+    ``kv_scale`` is 1): enough for metadata-only work.
+    """
     if isinstance(ctx, tuple) and isinstance(ctx[0], str):
         ctx_lens = _draw_ctx(ctx, batch, _rng(seed, 0))
     else:
@@ -156,6 +161,16 @@ def make_workload(*, name: str, world: int, interleave: int, batch: int, qlen: i
     seq_start = np.zeros(batch + 1, dtype=np.int64)
     seq_start[1:] = np.cumsum(ctx_lens)
     T = int(seq_start[-1])
+    if not with_kv:
+        return Workload(name=name, world=world, interleave=interleave, batch=batch, qlen=qlen,
+                        heads=heads, block_size=block_size, kv_format=kv_format,
+                        ctx_lens=ctx_lens.astype(np.int32), block_table=block_table,
+                        num_blocks=int(num_blocks), max_local_pages=int(max_local_pages),
+                        q_bits=q_bits, kv=np.zeros((0, D_QK), dtype=np.uint8),
+                        seq_start=seq_start, kv_scale=1.0,
+                        softmax_scale=float(softmax_scale if softmax_scale is not None
+                                            else 1.0 / math.sqrt(192.0)),
+                        seed=seed)
     jobs = []
     for b in range(batch):
         for c in range((int(ctx_lens[b]) + CHUNK_TOKENS - 1) // CHUNK_TOKENS):

@@ -1,0 +1,160 @@
+"""Per-rank segmented attention, segment merge and cross-rank merge on the GPU
+against the float64 oracle.
+
+Tolerances: outputs max-abs 1.5e-2 with an FP8 cache and 5e-3 with a BF16
+cache, on top of the BF16 output format's own rounding (half a BF16 ulp of the
+exact value, and for the merged output also each rank's rounded partial
+weighted by its merge weight); LSE abs 1e-3.  The oracle reads the same
+decoded cache values, so FP8 quantisation is not part of the error; what
+remains is BF16 rounding of the probabilities and of the outputs plus fp32
+accumulation.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from synth import make_config, make_workload
+from gpu_util import (LSE_TOL, bf16_to_f64, oracle_latents, oracle_q, output_bound,
+                      run_group, tolerance)
+
+pytestmark = pytest.mark.gpu
+
+
+def _compare_rank(w, grp, r, rows):
+    o, l = A.verify_attention(oracle_q(w), oracle_latents(w), w.ctx_lens, w.softmax_scale,
+                              world=w.world, interleave=w.interleave, rank=r, rows=rows)
+    go = bf16_to_f64(grp.out_ranks[r])
+    gl = grp.lse_ranks[r].cpu().numpy().astype(np.float64)
+    for b, i in rows:
+        emp = np.isneginf(l[b, i])
+        # empty (row, rank): exactly zero output and -inf LSE
+        assert np.all(np.isneginf(gl[b, i][emp]))
+        assert np.all(go[b, i][emp] == 0.0)
+        assert np.all(np.isfinite(gl[b, i][~emp]))
+        if (~emp).any():
+            ex = o[b, i][~emp]
+            err_o = np.abs(go[b, i][~emp] - ex)
+            bad = err_o > output_bound(w, ex)
+            assert not bad.any(), (r, b, i, err_o.max(), err_o[bad].max())
+            err_l = np.abs(gl[b, i][~emp] - l[b, i][~emp]).max()
+            assert err_l <= LSE_TOL, (r, b, i, err_l)
+
+
+def _compare_merged(w, grp, rows):
+    q, lat = oracle_q(w), oracle_latents(w)
+    o, l = A.verify_attention(q, lat, w.ctx_lens, w.softmax_scale, rows=rows)
+    ro, rl = [], []
+    for r in range(w.world):
+        a, c = A.verify_attention(q, lat, w.ctx_lens, w.softmax_scale, world=w.world,
+                                  interleave=w.interleave, rank=r, rows=rows)
+        ro.append(a)
+        rl.append(c)
+    ro, rl = np.stack(ro), np.stack(rl)
+    go = bf16_to_f64(grp.out)
+    gl = grp.lse.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for b, i in rows:
+        wts = np.where(np.isneginf(rl[:, b, i]), 0.0, np.exp(rl[:, b, i] - l[b, i][None, :]))
+        err = np.abs(go[b, i] - o[b, i])
+        bound = output_bound(w, o[b, i], ro[:, b, i], wts)
+        assert not (err > bound).any(), (b, i, err.max())
+        worst = max(worst, err.max())
+        assert np.abs(gl[b, i] - l[b, i]).max() <= LSE_TOL
+    return worst
+
+
+@pytest.mark.parametrize("k,groups", [(1, 0), (1, 1), (1, 3), (2, 0), (2, 7), (2, 1)])
+def test_small_configs_full(k, groups):
+    w = make_config(k)
+    print(f"config {k} groups {groups}", flush=True)
+    grp, _ = run_group(w, groups=groups)
+    assert grp.errors() == 0
+    rows = [(b, i) for b in range(w.batch) for i in range(w.qlen)]
+    for r in range(w.world):
+        _compare_rank(w, grp, r, rows)
+    _compare_merged(w, grp, rows)
+
+
+def _sample_rows(w, n, seed):
+    rng = np.random.default_rng(seed)
+    bs = rng.choice(w.batch, size=min(n, w.batch), replace=False)
+    return [(int(b), int(rng.integers(w.qlen))) for b in bs] + [(int(bs[0]), w.qlen - 1), (int(bs[0]), 0)]
+
+
+def test_config4_verify_interleave16():
+    # log-uniform contexts, interleave 16, qlen 5: empty (row, rank) pairs occur
+    w = make_config(4)
+    print(f"config 4: {w.name}", flush=True)
+    grp, _ = run_group(w)
+    assert grp.errors() == 0
+    shortest = int(np.argmin(w.ctx_lens))
+    longest = int(np.argmax(w.ctx_lens))
+    rows = sorted(set(_sample_rows(w, 5, 44) + [(shortest, i) for i in range(w.qlen)]
+                      + [(longest, w.qlen - 1)]))
+    for r in (0, 3, 7):
+        _compare_rank(w, grp, r, rows)
+    _compare_merged(w, grp, rows)
+
+
+@pytest.mark.parametrize("k", [3, 5])
+def test_large_configs_sampled(k):
+    w = make_config(k)
+    print(f"config {k}: {w.name}", flush=True)
+    grp, _ = run_group(w)
+    assert grp.errors() == 0
+    rows = _sample_rows(w, 2, 40 + k)
+    for r in (0, w.world - 1):
+        _compare_rank(w, grp, r, rows)
+    _compare_merged(w, grp, rows)
+
+
+def test_ragged_tiles_and_tiny_contexts():
+    # M = 3 * 40 = 120 (one ragged tile); contexts down to qlen (first row sees one token);
+    # interleave 4 over 8 ranks leaves most ranks empty for short rows
+    ctx = np.array([3, 4, 5, 9, 33, 64, 65, 200, 1000])
+    w = make_workload(name="ragged", world=8, interleave=4, batch=len(ctx), qlen=3, heads=40,
+                      block_size=16, kv_format="bf16", ctx=ctx, table="random",
+                      max_local_pages=16, seed=77)
+    for groups in (0, 5):
+        grp, _ = run_group(w, groups=groups)
+        assert grp.errors() == 0
+        rows = [(b, i) for b in range(w.batch) for i in range(w.qlen)]
+        for r in range(w.world):
+            _compare_rank(w, grp, r, rows)
+        _compare_merged(w, grp, rows)
+
+
+def test_all_ranks_but_one_empty():
+    # every context shorter than the interleave: only rank 0 owns tokens
+    ctx = np.array([5, 8, 12, 16])
+    w = make_workload(name="rank0only", world=8, interleave=16, batch=4, qlen=2, heads=16,
+                      block_size=16, kv_format="fp8_e4m3", ctx=ctx, table="shuffled",
+                      max_local_pages=2, seed=78)
+    grp, _ = run_group(w)
+    for r in range(1, 8):
+        assert torch.all(grp.lse_ranks[r] == float("-inf"))
+        assert torch.all(grp.out_ranks[r] == 0)
+    rows = [(b, i) for b in range(w.batch) for i in range(w.qlen)]
+    _compare_rank(w, grp, 0, rows)
+    _compare_merged(w, grp, rows)
+
+
+def test_negative_control_boundary():
+    # the GPU result matches the correct boundary and misses both mutated ones
+    w = make_config(2)
+    grp, _ = run_group(w)
+    rows = [(0, i) for i in range(w.qlen)] + [(1, i) for i in range(w.qlen)]
+    _compare_merged(w, grp, rows)
+    go = bf16_to_f64(grp.out)
+    for mutant in (lambda c, q, i: c - q, lambda c, q, i: c):
+        outs, lses = [], []
+        for r in range(w.world):
+            o, l = A.verify_attention(oracle_q(w), oracle_latents(w), w.ctx_lens, w.softmax_scale,
+                                      world=w.world, interleave=w.interleave, rank=r, rows=rows,
+                                      boundary=mutant)
+            outs.append(o)
+            lses.append(l)
+        mo, _ = A.merge_ranks(np.stack(outs), np.stack(lses))
+        diff = max(np.abs(go[b, i] - mo[b, i]).max() for b, i in rows)
+        assert diff > tolerance(w), diff

@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2,
                     help="workload 1..5 (default 2: dcp=2, qlen=3, 96 heads, batch 8, FP8 KV)")
+    ap.add_argument("--groups", type=int, default=0,
+                    help="persistent workgroups of the attention kernel (0: one per compute unit)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle's timed CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -112,7 +114,7 @@ def main():
     g = ops.Geometry(dcp_world=w.world, interleave=w.interleave, block_size=w.block_size,
                      qlen=w.qlen, num_heads=w.heads, batch=w.batch,
                      max_blocks_per_seq=w.block_table.shape[1], max_local_pages=w.max_local_pages,
-                     kv_dtype=w.kv_format, num_blocks=w.num_blocks)
+                     kv_dtype=w.kv_format, num_blocks=w.num_blocks, groups=args.groups)
     dev = "cuda"
     q = torch.from_numpy(w.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     if w.kv_format == "fp8_e4m3":

@@ -21,17 +21,26 @@
 // depends only on the device, the unit count only on device metadata, so the
 // launch is capture-stable.
 //
-// Inside a workgroup: 4 waves x 32 head-rows.  Each wave keeps its 32 query
-// rows (32 x 576 BF16) in registers as the B operand of S^T = K Q^T
-// (v_mfma_f32_32x32x16_bf16, A = K tile from LDS), so a lane's scores all
-// belong to one head-row and the online softmax needs one cross-half swap.
-// The probabilities P^T stay in registers as the B operand of
-// O^T = V^T P^T; the 512 x 32 output accumulator lives in 16 MFMA
-// accumulators (256 AGPRs).  KV stages are double-buffered in LDS in the
-// cache's own element format (FP8 bytes or BF16), K as [d/16][token][16] and
-// V^T as [token/16][half][d][8] (transposed in registers while staging), and
-// are widened to BF16 in registers right before each MFMA: E4M3 -> BF16 is
-// exact, so the kv scale folds into the score scale and the output.
+// Inside a workgroup: 4 waves x 32 head-rows, one wave per SIMD.  Each wave
+// keeps its 32 query rows (32 x 576 BF16) in registers as the B operand of
+// S^T = K Q^T (v_mfma_f32_32x32x16_bf16, A = K tile read from LDS), so a
+// lane's scores all belong to one head-row and the online softmax needs one
+// cross-half swap.  The probabilities P^T stay in registers as the B operand
+// of O^T = V^T P^T; the 512 x 32 output accumulator lives in 16 MFMA
+// accumulators (256 AGPRs).
+//
+// LDS holds each 32-token stage once, as K blocks [d/16][token][16 elements]
+// (one padded block per 16 dims).  The QK operand is a plain read of that
+// tile; the PV operand V^T (8 tokens of one value dim per lane) is read from
+// the same tile with the gfx950 transposing loads ds_read_b64_tr_b8 /
+// ds_read_b64_tr_b16, so no transposed copy of V is kept.  The tile is stored
+// either as the cache's FP8 bytes (widened to BF16 in registers before each
+// MFMA) or already widened to BF16 while staging; E4M3 -> BF16 is exact, so
+// the kv scale folds into the score scale and the output.
+#include <stdlib.h>
+
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -47,9 +56,6 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;   // keep a stale running max while 2^(s - m) <= 2^8
 
-constexpr int kKElems = (kDqk / 16) * kStageTokens * 16;   // K part of one stage
-constexpr int kVElems = 2 * 2 * kDv * 8;                   // V^T part of one stage
-constexpr int kStageElems = kKElems + kVElems;
 
 struct AttnArgs {
   const uint16_t *q;         // [B, qlen, H, 576] bf16 bits
@@ -68,24 +74,49 @@ struct AttnArgs {
   float out_scale;           // kv_scale
 };
 
+constexpr int kKBlocks = kDqk / 16;                            // 36 blocks of 16 dims
+// Staging: 8 threads per token of a 32-token stage; thread (token tid / 8,
+// lane-in-token c = tid % 8) moves the 8-element pieces c, c + 8, ..., c + 64
+// of its token's 576-element row, so its addresses are one base plus
+// constant offsets and it needs one page id per stage.
+constexpr int kThreadsPerToken = kThreads / kStageTokens;      // 8
+constexpr int kUnitsPerThread = kDqk / 8 / kThreadsPerToken;   // 9
+static_assert(kThreadsPerToken * kStageTokens == kThreads, "staging split");
+
+// LDS tile of one stage with L-byte elements: 36 blocks of [32 token slots]
+// [16 elements].  Every access pattern (QK rows, transposing PV reads,
+// staging stores) covers whole 128-byte bank windows, so blocks need no pad.
+template <int L>
+struct Tile {
+  static constexpr int kRow = 16 * L;
+  static constexpr int kBlock = kStageTokens * kRow;
+  static constexpr int kBytes = kKBlocks * kBlock;
+};
+
 // token (within a 32-token stage) held by register r of a 32x32 accumulator
-// in lane half h: rows 8*(r/4) + 4*h + r%4 of the MFMA output tile
+// in lane half h: rows 8*(r/4) + 4*h + r%4 of the MFMA output tile.  The
+// same map assigns PV k-slot 8*h + e (e < 8) of token half kb to token
+// 16*kb + tau(h, e).
 __device__ inline int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// LDS row slot of stage-token t.  The PV operand of lane half h gathers the
+// eight tokens tau(h, 0..7) = {4h..4h+3, 8+4h..8+4h+3} (+16 for the second
+// token half); storing those eight rows in consecutive slots 8h..8h+7 makes
+// each 16-lane transposing read touch every bank exactly once.  QK reads all
+// 32 rows, in any order, so it does not care.
+__host__ __device__ inline int tok_slot(int t) {
+  return 16 * (t >> 4) + 8 * ((t >> 2) & 1) + 4 * ((t >> 3) & 1) + (t & 3);
+}
+
 template <int E>
-struct Staged;
-
-template <>
-struct Staged<1> {
-  uint2 v[8];
-  uint4 rope;
+struct Staged {
+  typedef typename std::conditional<E == 1, uint2, uint4>::type Unit;   // 8 elements
+  Unit v[kUnitsPerThread];
+  uint32_t keep;   // 1: the token is valid, 0: store zeros
 };
 
-template <>
-struct Staged<2> {
-  uint4 v[8];
-  uint4 rope[2];
-};
+__device__ inline uint2 masked(uint2 v, bool k) { return k ? v : make_uint2(0, 0); }
+__device__ inline uint4 masked(uint4 v, bool k) { return k ? v : make_uint4(0, 0, 0, 0); }
 
 __device__ inline bf16x8 widen_fp8(uint2 raw) {
   const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, false);
@@ -98,202 +129,148 @@ __device__ inline bf16x8 widen_fp8(uint2 raw) {
   return r;
 }
 
-template <int E>
-__device__ inline bf16x8 lds_operand(const uint8_t *p) {
-  if constexpr (E == 1) {
-    return widen_fp8(*(const uint2 *)p);
-  } else {
-    return __builtin_bit_cast(bf16x8, *(const uint4 *)p);
-  }
-}
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef int int2v __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char;
 
-// 8x8 transpose of byte elements held as 8 rows of 64 bits
-__host__ __device__ inline void transpose8x8_b8(uint64_t r[8]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint64_t a = r[j], b = r[j + 4];
-    r[j] = (a & 0x00000000FFFFFFFFull) | (b << 32);
-    r[j + 4] = (a >> 32) | (b & 0xFFFFFFFF00000000ull);
-  }
-#pragma unroll
-  for (int j0 = 0; j0 < 8; j0 += 4) {
-#pragma unroll
-    for (int j = j0; j < j0 + 2; ++j) {
-      const uint64_t a = r[j], b = r[j + 2];
-      r[j] = (a & 0x0000FFFF0000FFFFull) | ((b << 16) & 0xFFFF0000FFFF0000ull);
-      r[j + 2] = ((a >> 16) & 0x0000FFFF0000FFFFull) | (b & 0xFFFF0000FFFF0000ull);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 8; j += 2) {
-    const uint64_t a = r[j], b = r[j + 1];
-    r[j] = (a & 0x00FF00FF00FF00FFull) | ((b << 8) & 0xFF00FF00FF00FF00ull);
-    r[j + 1] = ((a >> 8) & 0x00FF00FF00FF00FFull) | (b & 0xFF00FF00FF00FF00ull);
-  }
-}
-
-// 8x8 transpose of 16-bit elements held as 8 rows of 128 bits (lo, hi words)
-__host__ __device__ inline void transpose8x8_b16(uint64_t lo[8], uint64_t hi[8]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {   // swap 4x4 blocks
-    const uint64_t t = hi[j];
-    hi[j] = lo[j + 4];
-    lo[j + 4] = t;
-  }
-#pragma unroll
-  for (int j0 = 0; j0 < 8; j0 += 4) {
-#pragma unroll
-    for (int j = j0; j < j0 + 2; ++j) {
-      uint64_t a = lo[j], b = lo[j + 2];
-      lo[j] = (a & 0x00000000FFFFFFFFull) | (b << 32);
-      lo[j + 2] = (a >> 32) | (b & 0xFFFFFFFF00000000ull);
-      a = hi[j];
-      b = hi[j + 2];
-      hi[j] = (a & 0x00000000FFFFFFFFull) | (b << 32);
-      hi[j + 2] = (a >> 32) | (b & 0xFFFFFFFF00000000ull);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 8; j += 2) {
-    uint64_t a = lo[j], b = lo[j + 1];
-    lo[j] = (a & 0x0000FFFF0000FFFFull) | ((b << 16) & 0xFFFF0000FFFF0000ull);
-    lo[j + 1] = ((a >> 16) & 0x0000FFFF0000FFFFull) | (b & 0xFFFF0000FFFF0000ull);
-    a = hi[j];
-    b = hi[j + 1];
-    hi[j] = (a & 0x0000FFFF0000FFFFull) | ((b << 16) & 0xFFFF0000FFFF0000ull);
-    hi[j + 1] = ((a >> 16) & 0x0000FFFF0000FFFFull) | (b & 0xFFFF0000FFFF0000ull);
-  }
-}
-
-template <int E>
-struct Stager {
-  // thread roles while staging one 32-token stage:
-  //   wave -> (kb, sh) = 16-token half and lane-half of the V^T layout,
-  //   lane -> 8-dim chunk c of the 512 value dims (the same bytes feed K);
-  //   threads < 128 also move one 16-dim piece of the 64 rope dims.
-  int kb, sh, c, rtok, rpart;
-  __device__ Stager(int tid) {
-    const int wave = tid >> 6;
-    kb = wave >> 1;
-    sh = wave & 1;
-    c = tid & 63;
-    rtok = (tid >> 2) & 31;
-    rpart = tid & 3;
-  }
-  __device__ int token(int j) const { return 16 * kb + 8 * (j >> 2) + 4 * sh + (j & 3); }
+// QK operand (A = K): lane (token l32, half h) reads elements 8h..8h+7 of
+// block kk of its token
+template <int L>
+struct KOp {
+  typedef typename std::conditional<L == 1, uint2, uint4>::type Raw;
 };
 
-template <int E>
-__device__ inline int64_t row_offset(const AttnArgs &a, const int32_t *pt, int t, int32_t *bad) {
-  // element offset of rank-local token t's latent row, or -1 (bad page id)
-  const int j = t >> a.page_shift;
-  const int32_t pg = pt[j];
-  if (pg < 0 || (int64_t)pg >= a.num_pages) {
-    *bad = 1;
-    return -1;
-  }
-  return (((int64_t)pg << a.page_shift) + (t & ((1 << a.page_shift) - 1))) * kDqk;
+template <int L>
+__device__ inline typename KOp<L>::Raw lds_k(const uint8_t *sb, int kk, int slot, int h) {
+  return *(const typename KOp<L>::Raw *)(sb + kk * Tile<L>::kBlock + slot * Tile<L>::kRow + 8 * h * L);
 }
 
+__device__ inline bf16x8 widen_k(uint2 raw) { return widen_fp8(raw); }
+__device__ inline bf16x8 widen_k(uint4 raw) { return __builtin_bit_cast(bf16x8, raw); }
+
+// PV operand (A = V^T): lane (dim 32*dblk + l32, half h) gets tokens
+// 16*kb + tau(h, e), e = 0..7, of that dim, via transposing reads.  Within a
+// 16-lane group the lane that loads address j supplies row j of a 16-row
+// (tr_b8: 8-byte, tr_b16: 4-element) block; result lane i receives column
+// i % (8 / L... ) of the rows the group loaded -- see the per-format maps.
+struct VRaw1 { int2v a; };
+struct VRaw2 { short4v a, b; };
+
+template <int L>
+struct VOp { typedef typename std::conditional<L == 1, VRaw1, VRaw2>::type Raw; };
+
+__device__ inline VRaw1 lds_v1(const uint8_t *sb, int dblk, int kb, int lane) {
+  // tr_b8: result lane 8a+b, byte k = byte b of the row loaded by lane a+2k.
+  // Loader j = a + 2k reads token 16kb + tau(h, k), dims d0 + 8a .. d0 + 8a + 7.
+  const int g = lane >> 4, j = lane & 15;
+  const int h = g >> 1;
+  const int kblk = 2 * dblk + (g & 1);
+  const int k = j >> 1, a = j & 1;
+  const int slot = 16 * kb + 8 * h + k;          // tok_slot(16kb + tau(h, k))
+  const uint8_t *p = sb + kblk * Tile<1>::kBlock + slot * Tile<1>::kRow + 8 * a;
+  VRaw1 r;
+  r.a = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) int2v *)(lds_char *)(size_t)p);
+  return r;
+}
+
+__device__ inline VRaw2 lds_v2(const uint8_t *sb, int dblk, int kb, int lane) {
+  // tr_b16: result lane 4a+b, element k = element b of the row loaded by lane
+  // a+4k.  Loader j = a + 4k reads token 16kb + tau(h, 4r + k), dims
+  // d0 + 4a .. d0 + 4a + 3, for the two halves r = 0, 1 of the 8 k-slots.
+  const int g = lane >> 4, j = lane & 15;
+  const int h = g >> 1;
+  const int kblk = 2 * dblk + (g & 1);
+  const int k = j >> 2, a = j & 3;
+  const uint8_t *base = sb + kblk * Tile<2>::kBlock + 8 * a;
+  const int slot0 = 16 * kb + 8 * h + k;         // tok_slot(16kb + tau(h, k)), k < 4
+  const int slot1 = slot0 + 4;                   // tok_slot(16kb + tau(h, 4 + k))
+  VRaw2 r;
+  r.a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4v *)(lds_char *)(size_t)(base + slot0 * Tile<2>::kRow));
+  r.b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4v *)(lds_char *)(size_t)(base + slot1 * Tile<2>::kRow));
+  return r;
+}
+
+template <int L>
+__device__ inline typename VOp<L>::Raw lds_v(const uint8_t *sb, int dblk, int kb, int lane) {
+  if constexpr (L == 1) return lds_v1(sb, dblk, kb, lane);
+  else return lds_v2(sb, dblk, kb, lane);
+}
+
+__device__ inline bf16x8 widen_v(VRaw1 r) {
+  return widen_fp8(make_uint2((uint32_t)r.a[0], (uint32_t)r.a[1]));
+}
+__device__ inline bf16x8 widen_v(VRaw2 r) {
+  // whole-vector reinterpretation (element-wise short -> __bf16 casts into a
+  // vector are miscompiled to zeros by this toolchain)
+  const uint2 lo = __builtin_bit_cast(uint2, r.a);
+  const uint2 hi = __builtin_bit_cast(uint2, r.b);
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// ---------------------------------------------------------------- staging
+
+// Issue the global loads of stage s for this thread's token.  A token past
+// the longest row, or on a page outside the pool, loads pool row 0 (a valid
+// address) and is marked for zeroing, so the LDS tile never holds stale
+// bytes (an FP8 NaN pattern times a zero probability would poison the
+// output).  Consecutive lanes read consecutive 8-element pieces of a row.
 template <int E>
-__device__ inline void load_stage(const AttnArgs &a, const Stager<E> &sg, const int32_t *pt,
-                                  int s, int lmax, int tid, Staged<E> &st, int32_t *bad) {
-  // Tokens past the sequence's longest row, and tokens on a bad page, load
-  // pool row 0 (always a valid address) and are zeroed, so LDS never holds
-  // stale bytes (an FP8 NaN pattern times a zero probability would poison
-  // the output).
-  const int t0 = s * kStageTokens;
+__device__ inline void load_stage(const AttnArgs &a, int32_t page, int s, int lmax, int tid,
+                                  Staged<E> &st, int32_t *bad) {
+  const int t = s * kStageTokens + tid / kThreadsPerToken;
+  const bool in_seq = t < lmax;
+  const bool ok = page >= 0 && (int64_t)page < a.num_pages;
+  *bad |= (in_seq && !ok) ? 1 : 0;
+  const bool valid = in_seq && ok;
+  const int64_t row = valid ? ((int64_t)page << a.page_shift) + (t & ((1 << a.page_shift) - 1)) : 0;
+  typedef typename Staged<E>::Unit Unit;
+  const Unit *src = (const Unit *)(a.pool + (row * kDqk + 8 * (tid % kThreadsPerToken)) * E);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int t = t0 + sg.token(j);
-    const int64_t off = t < lmax ? row_offset<E>(a, pt, t, bad) : -1;
-    const int64_t src = off >= 0 ? off : 0;
-    const uint32_t keep = off >= 0 ? 0xFFFFFFFFu : 0u;
-    if constexpr (E == 1) {
-      uint2 v = *(const uint2 *)(a.pool + src + 8 * sg.c);
-      v.x &= keep; v.y &= keep;
-      st.v[j] = v;
+  for (int i = 0; i < kUnitsPerThread; ++i) st.v[i] = src[i * kThreadsPerToken];
+  st.keep = valid ? 1u : 0u;
+}
+
+// Write the staged pieces into the LDS tile (widening FP8 to BF16 when L = 2).
+// Piece p = c + 8i lands in block p / 2, half p % 2, row token.
+template <int E, int L>
+__device__ inline void store_stage(uint8_t *sb, int tid, const Staged<E> &st) {
+  const int tok = tid / kThreadsPerToken;
+  const int c = tid % kThreadsPerToken;
+  uint8_t *base = sb + (c >> 1) * Tile<L>::kBlock + tok_slot(tok) * Tile<L>::kRow + 8 * (c & 1) * L;
+  const bool keep = st.keep != 0;
+#pragma unroll
+  for (int i = 0; i < kUnitsPerThread; ++i) {
+    uint8_t *dst = base + 4 * i * Tile<L>::kBlock;
+    const auto v = masked(st.v[i], keep);
+    if constexpr (L == 1) {
+      *(uint2 *)dst = v;
+    } else if constexpr (E == 1) {
+      *(uint4 *)dst = __builtin_bit_cast(uint4, widen_fp8(v));
     } else {
-      uint4 v = *(const uint4 *)(a.pool + 2 * (src + 8 * sg.c));
-      v.x &= keep; v.y &= keep; v.z &= keep; v.w &= keep;
-      st.v[j] = v;
-    }
-  }
-  {
-    const int t = t0 + sg.rtok;
-    const int64_t off = (tid < 128 && t < lmax) ? row_offset<E>(a, pt, t, bad) : -1;
-    const int64_t src = off >= 0 ? off : 0;
-    const uint32_t keep = off >= 0 ? 0xFFFFFFFFu : 0u;
-    if constexpr (E == 1) {
-      uint4 v = *(const uint4 *)(a.pool + src + kDv + 16 * sg.rpart);
-      v.x &= keep; v.y &= keep; v.z &= keep; v.w &= keep;
-      st.rope = v;
-    } else {
-      const uint4 *p = (const uint4 *)(a.pool + 2 * (src + kDv + 16 * sg.rpart));
-      uint4 v0 = p[0], v1 = p[1];
-      v0.x &= keep; v0.y &= keep; v0.z &= keep; v0.w &= keep;
-      v1.x &= keep; v1.y &= keep; v1.z &= keep; v1.w &= keep;
-      st.rope[0] = v0;
-      st.rope[1] = v1;
+      *(uint4 *)dst = v;
     }
   }
 }
 
-template <int E>
-__device__ inline void store_stage(uint8_t *sb, const Stager<E> &sg, int tid, const Staged<E> &st) {
-  // K: [kk = d/16][token][16 elems]; this thread's chunk is half (c & 1) of kk = c/2
-  const int kk = sg.c >> 1;
-  const int half = sg.c & 1;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint8_t *dst = sb + (((kk * kStageTokens + sg.token(j)) * 16 + 8 * half) * E);
-    if constexpr (E == 1) *(uint2 *)dst = st.v[j];
-    else *(uint4 *)dst = st.v[j];
-  }
-  // V^T: [kb][sh][d][8 tokens in accumulator-row order]
-  uint8_t *vt = sb + kKElems * E + (((sg.kb * 2 + sg.sh) * kDv + 8 * sg.c) * 8) * E;
-  if constexpr (E == 1) {
-    uint64_t r[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) r[j] = (uint64_t)st.v[j].x | ((uint64_t)st.v[j].y << 32);
-    transpose8x8_b8(r);
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      *(uint4 *)(vt + 16 * k) = make_uint4((uint32_t)r[2 * k], (uint32_t)(r[2 * k] >> 32),
-                                           (uint32_t)r[2 * k + 1], (uint32_t)(r[2 * k + 1] >> 32));
-  } else {
-    uint64_t lo[8], hi[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      lo[j] = (uint64_t)st.v[j].x | ((uint64_t)st.v[j].y << 32);
-      hi[j] = (uint64_t)st.v[j].z | ((uint64_t)st.v[j].w << 32);
-    }
-    transpose8x8_b16(lo, hi);
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      *(uint4 *)(vt + 16 * k) = make_uint4((uint32_t)lo[k], (uint32_t)(lo[k] >> 32), (uint32_t)hi[k],
-                                           (uint32_t)(hi[k] >> 32));
-  }
-  if (tid < 128) {
-    uint8_t *dst = sb + ((((kDv / 16) + sg.rpart) * kStageTokens + sg.rtok) * 16) * E;
-    if constexpr (E == 1) {
-      *(uint4 *)dst = st.rope;
-    } else {
-      *(uint4 *)dst = st.rope[0];
-      *(uint4 *)(dst + 16) = st.rope[1];
-    }
-  }
+// Page id of this thread's token of stage s (branch-free: a token past the
+// longest row reads slot 0, present whenever the sequence has a token).
+__device__ inline int32_t fetch_page(const AttnArgs &a, const int32_t *pt, int s, int lmax, int tid) {
+  const int t = s * kStageTokens + tid / kThreadsPerToken;
+  return pt[t < lmax ? (t >> a.page_shift) : 0];
 }
 
-template <int E>
+template <int E, int L>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attention_kernel(AttnArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];   // two stage tiles
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int h = lane >> 5;
+  const int kslot = tok_slot(l32);   // LDS slot of the stage token in this lane's score row
   const int64_t U = a.work[0];
   if (U == 0) return;
   const int64_t G = effective_groups(gridDim.x, U);
@@ -302,7 +279,6 @@ attention_kernel(AttnArgs a) {
   const int64_t lo = group_lo(w, U, G);
   const int64_t hi = group_lo(w + 1, U, G);
   const int32_t *unit_base = a.work + work_unit_base_off();
-  const Stager<E> sg(tid);
   int32_t bad = 0;
 
   int slot = 0;
@@ -329,13 +305,16 @@ attention_kernel(AttnArgs a) {
     const int vrow = mvalid ? m / a.H : 0;
     const int rlen = mvalid ? a.row_len[b * a.qlen + vrow] : 0;
 
-    bf16x8 qf[kDqk / 16];
+    // page id of this thread's token in the first stage
+    int32_t page = fetch_page(a, pt, st0, lmax, tid);
+
+    bf16x8 qf[kKBlocks];
     {
       // rows past M read row M-1 (a valid address) and are zeroed
       const uint16_t *qrow = a.q + ((int64_t)b * a.M + (mvalid ? m : a.M - 1)) * kDqk + 8 * h;
       const uint32_t keep = mvalid ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-      for (int kk = 0; kk < kDqk / 16; ++kk) {
+      for (int kk = 0; kk < kKBlocks; ++kk) {
         uint4 v = *(const uint4 *)(qrow + 16 * kk);
         v.x &= keep; v.y &= keep; v.z &= keep; v.w &= keep;
         qf[kk] = __builtin_bit_cast(bf16x8, v);
@@ -352,24 +331,32 @@ attention_kernel(AttnArgs a) {
     float lsum_f = 0.f;  // fp32 sum of the same probabilities before rounding: gives the LSE
 
     Staged<E> st;
-    load_stage<E>(a, sg, pt, st0, lmax, tid, st, &bad);
-    store_stage<E>(lds, sg, tid, st);
+    load_stage<E>(a, page, st0, lmax, tid, st, &bad);
+    if (st0 + 1 < st1) page = fetch_page(a, pt, st0 + 1, lmax, tid);
+    store_stage<E, L>(lds, tid, st);
     __syncthreads();
 
     for (int s = st0; s < st1; ++s) {
       const int cur = (s - st0) & 1;
       const bool more = s + 1 < st1;
-      if (more) load_stage<E>(a, sg, pt, s + 1, lmax, tid, st, &bad);
-      const uint8_t *sb = lds + cur * (kStageElems * E);
+      if (more) load_stage<E>(a, page, s + 1, lmax, tid, st, &bad);
+      if (s + 2 < st1) page = fetch_page(a, pt, s + 2, lmax, tid);
+      const uint8_t *sb = lds + cur * Tile<L>::kBytes;
 
-      // S^T[token, row] = K Q^T over 576 dims
+      // S^T[token, row] = K Q^T over 576 dims; operands prefetched two ahead
       floatx16 sacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+      {
+        typename KOp<L>::Raw kr[2];
+        kr[0] = lds_k<L>(sb, 0, kslot, h);
+        kr[1] = lds_k<L>(sb, 1, kslot, h);
 #pragma unroll
-      for (int kk = 0; kk < kDqk / 16; ++kk) {
-        const bf16x8 kop = lds_operand<E>(sb + ((kk * kStageTokens + l32) * 16 + 8 * h) * E);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[kk], sacc, 0, 0, 0);
+        for (int kk = 0; kk < kKBlocks; ++kk) {
+          const bf16x8 kop = widen_k(kr[kk & 1]);
+          if (kk + 2 < kKBlocks) kr[kk & 1] = lds_k<L>(sb, kk + 2, kslot, h);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[kk], sacc, 0, 0, 0);
+        }
       }
 
       // online softmax in base 2 on this lane's 16 tokens of head-row m
@@ -385,11 +372,14 @@ attention_kernel(AttnArgs a) {
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float mnew = fmaxf(mrun, mx);
       const bool need = mnew > mrun + kRescaleSlack;
-      if (__any(need)) {
-        const float alpha = need ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.0f;
-        if (need) mrun = mnew;
-        lsum *= alpha;
-        lsum_f *= alpha;
+      const float alpha = need ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.0f;
+      // a row that had no visible token yet (mrun = -inf) has O = 0: only rows
+      // with earlier mass need their accumulator rescaled
+      const bool scale_o = need && mrun > kNegInf;
+      if (need) mrun = mnew;
+      lsum *= alpha;
+      lsum_f *= alpha;
+      if (__any(scale_o)) {
         // Rare path.  Each accumulator element is scaled in place (read from
         // its AGPR, multiply, write back) so the 256-element accumulator never
         // has to be copied into VGPRs as a whole; the trailing nops cover the
@@ -421,18 +411,21 @@ attention_kernel(AttnArgs a) {
         lsum_f += p;
       }
 
-      // O^T[d, row] += V^T[d, token] P^T[token, row]
+      // O^T[d, row] += V^T[d, token] P^T[token, row]; operands prefetched two ahead
+      {
+        typename VOp<L>::Raw vr[2];
+        vr[0] = lds_v<L>(sb, 0, 0, lane);
+        vr[1] = lds_v<L>(sb, 0, 1, lane);
 #pragma unroll
-      for (int d = 0; d < kDv / 32; ++d) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 vop =
-              lds_operand<E>(sb + kKElems * E + (((kb * 2 + h) * kDv + 32 * d + l32) * 8) * E);
+        for (int i = 0; i < kDv / 16; ++i) {
+          const int d = i >> 1, kb = i & 1;
+          const bf16x8 vop = widen_v(vr[i & 1]);
+          if (i + 2 < kDv / 16) vr[i & 1] = lds_v<L>(sb, (i + 2) >> 1, (i + 2) & 1, lane);
           oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[kb], oacc[d], 0, 0, 0);
         }
       }
 
-      if (more) store_stage<E>(lds + (cur ^ 1) * (kStageElems * E), sg, tid, st);
+      if (more) store_stage<E, L>(lds + (cur ^ 1) * Tile<L>::kBytes, tid, st);
       __syncthreads();
     }
 
@@ -509,26 +502,42 @@ hipError_t launch_partial_attention(const dcpmla_geom &g, int groups, const void
   a.max_local_pages = g.max_local_pages;
   a.score_scale2 = softmax_scale * kv_scale * 1.44269504088896340736f;
   a.out_scale = kv_scale;
+  const size_t extra = 0;
   if (g.kv_dtype == DCPMLA_KV_FP8_E4M3) {
-    const size_t shmem = 2 * kStageElems * 1;
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void *)attention_kernel<1>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-      if (e != hipSuccess) return e;
-      attr_set = true;
+    // FP8 cache: the LDS tile keeps FP8 bytes (widened per operand) unless
+    // DCPMLA_LDS_BF16=1 asks for widening once while staging
+    static const bool widen_at_stage = getenv("DCPMLA_LDS_BF16") && atoi(getenv("DCPMLA_LDS_BF16")) == 1;
+    if (widen_at_stage) {
+      const size_t shmem = 2 * Tile<2>::kBytes + extra;
+      static bool attr_set = false;
+      if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)attention_kernel<1, 2>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+      }
+      hipLaunchKernelGGL((attention_kernel<1, 2>), dim3(groups), dim3(kThreads), shmem, stream, a);
+    } else {
+      const size_t shmem = 2 * Tile<1>::kBytes + extra;
+      static bool attr_set = false;
+      if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)attention_kernel<1, 1>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+      }
+      hipLaunchKernelGGL((attention_kernel<1, 1>), dim3(groups), dim3(kThreads), shmem, stream, a);
     }
-    hipLaunchKernelGGL(attention_kernel<1>, dim3(groups), dim3(kThreads), shmem, stream, a);
   } else {
-    const size_t shmem = 2 * kStageElems * 2;
+    const size_t shmem = 2 * Tile<2>::kBytes + extra;
     static bool attr_set = false;
     if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void *)attention_kernel<2>,
+      hipError_t e = hipFuncSetAttribute((const void *)attention_kernel<2, 2>,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
       if (e != hipSuccess) return e;
       attr_set = true;
     }
-    hipLaunchKernelGGL(attention_kernel<2>, dim3(groups), dim3(kThreads), shmem, stream, a);
+    hipLaunchKernelGGL((attention_kernel<2, 2>), dim3(groups), dim3(kThreads), shmem, stream, a);
   }
   return hipGetLastError();
 }

@@ -117,21 +117,30 @@ __global__ void __launch_bounds__(256) merge_segments_dense_kernel(
 // Persistent layout: finish every (sequence, head-row tile) whose stages were
 // split over several workgroups, and give sequences with no rank-local token
 // their empty result.  Tiles finished inside one workgroup are left alone.
+// One workgroup per (sequence, tile, group of kMergeRows rows); each wave
+// merges kMergeRows / 4 rows, one row at a time, with the partial loads of a
+// row issued four at a time.
+constexpr int kMergeRows = 16;
+
 __global__ void __launch_bounds__(256) merge_segments_kernel(
     int B, int qlen, int heads, int n_mt, int G, const int32_t *__restrict__ work,
     const float4 *__restrict__ ws_o, const float *__restrict__ ws_lse2, uint4 *__restrict__ out,
     float *__restrict__ lse) {
   __shared__ int s_src[1024];   // partial index (group * kSlots + slot) of each piece part
   __shared__ int s_n;
-  const int b = blockIdx.x / n_mt;
-  const int mt = blockIdx.x - b * n_mt;
+  constexpr int kChunks = kTileRows / kMergeRows;
+  const int chunk = blockIdx.x % kChunks;
+  const int bt = blockIdx.x / kChunks;
+  const int b = bt / n_mt;
+  const int mt = bt - b * n_mt;
   const int M = qlen * heads;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t U = work[0];
   const int stages = work[work_stages_off(B) + b];
-  const int row0 = mt * kTileRows;
-  const int nrows = min(kTileRows, M - row0);
+  const int row0 = mt * kTileRows + chunk * kMergeRows;   // first row of this chunk
+  const int nrows = min(kMergeRows, M - row0);
+  if (nrows <= 0) return;
   if (stages == 0) {
     // no rank-local token for the whole sequence: O = 0, LSE = -inf
     for (int r = wave; r < nrows; r += kWaves) {
@@ -165,27 +174,52 @@ __global__ void __launch_bounds__(256) merge_segments_kernel(
   }
   __syncthreads();
   const int n = s_n;
+  const int tr0 = chunk * kMergeRows;   // row index inside the tile (partial rows)
   for (int r = wave; r < nrows; r += kWaves) {
+    const int pr0 = tr0 + r;
     float mx = kNegInf;
-    for (int k = 0; k < n; ++k) mx = fmaxf(mx, ws_lse2[(int64_t)s_src[k] * kTileRows + r]);
+    for (int k = lane; k < n; k += 64) mx = fmaxf(mx, ws_lse2[(int64_t)s_src[k] * kTileRows + pr0]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     float L = kNegInf;
     if (mx > kNegInf) {
       float z = 0.f;
-      for (int k = 0; k < n; ++k) {
-        const int64_t pr = (int64_t)s_src[k] * kTileRows + r;
+      int k = 0;
+      for (; k + 4 <= n; k += 4) {
+        float wgt[4];
+        float4 va[4], vb[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t pr = (int64_t)s_src[k + q] * kTileRows + pr0;
+          const float l = ws_lse2[pr];
+          wgt[q] = l > kNegInf ? fast_exp2(l - mx) : 0.f;
+          const float4 *src = ws_o + pr * (kDv / 4) + 2 * lane;
+          va[q] = src[0];
+          vb[q] = src[1];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          z += wgt[q];
+          acc[0] += wgt[q] * va[q].x; acc[1] += wgt[q] * va[q].y;
+          acc[2] += wgt[q] * va[q].z; acc[3] += wgt[q] * va[q].w;
+          acc[4] += wgt[q] * vb[q].x; acc[5] += wgt[q] * vb[q].y;
+          acc[6] += wgt[q] * vb[q].z; acc[7] += wgt[q] * vb[q].w;
+        }
+      }
+      for (; k < n; ++k) {
+        const int64_t pr = (int64_t)s_src[k] * kTileRows + pr0;
         const float l = ws_lse2[pr];
-        if (!(l > kNegInf)) continue;
-        const float w = fast_exp2(l - mx);
-        z += w;
+        const float wq = l > kNegInf ? fast_exp2(l - mx) : 0.f;
         const float4 *src = ws_o + pr * (kDv / 4) + 2 * lane;
         const float4 a = src[0], c = src[1];
-        acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
-        acc[4] += w * c.x; acc[5] += w * c.y; acc[6] += w * c.z; acc[7] += w * c.w;
+        z += wq;
+        acc[0] += wq * a.x; acc[1] += wq * a.y; acc[2] += wq * a.z; acc[3] += wq * a.w;
+        acc[4] += wq * c.x; acc[5] += wq * c.y; acc[6] += wq * c.z; acc[7] += wq * c.w;
       }
       const float inv = 1.f / z;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] *= inv;
+      for (int q = 0; q < 8; ++q) acc[q] *= inv;
       L = (mx + fast_log2(z)) * kLn2;
     }
     const int64_t orow = (int64_t)b * M + row0 + r;
@@ -218,7 +252,8 @@ hipError_t launch_merge_segments(const dcpmla_geom &g, int groups, const dcpmla_
                                  hipStream_t stream) {
   const int n_mt = n_mtiles(g.qlen, g.num_heads);
   const float *ws = (const float *)workspace;
-  hipLaunchKernelGGL(merge_segments_kernel, dim3(g.batch * n_mt), dim3(256), 0, stream, g.batch,
+  const int chunks = kTileRows / kMergeRows;
+  hipLaunchKernelGGL(merge_segments_kernel, dim3(g.batch * n_mt * chunks), dim3(256), 0, stream, g.batch,
                      g.qlen, g.num_heads, n_mt, groups, m.work, (const float4 *)ws,
                      ws + ws_o_floats(groups), (uint4 *)out_rank, lse_rank);
   return hipGetLastError();

@@ -29,16 +29,17 @@
 // of O^T = V^T P^T; the 512 x 32 output accumulator lives in 16 MFMA
 // accumulators (256 AGPRs).
 //
-// LDS holds each 32-token stage once, as K blocks [d/16][token][16 elements]
-// (one padded block per 16 dims).  The QK operand is a plain read of that
-// tile; the PV operand V^T (8 tokens of one value dim per lane) is read from
-// the same tile with the gfx950 transposing loads ds_read_b64_tr_b8 /
-// ds_read_b64_tr_b16, so no transposed copy of V is kept.  The tile is stored
-// either as the cache's FP8 bytes (widened to BF16 in registers before each
-// MFMA) or already widened to BF16 while staging; E4M3 -> BF16 is exact, so
-// the kv scale folds into the score scale and the output.
-#include <stdlib.h>
-
+// LDS holds each 32-token stage once, in the cache's own element format, as
+// 36 blocks [16 dims][32 token slots][16 elements].  Stages arrive by direct
+// global->LDS loads (global_load_lds_dwordx4): each lane owns one token row of
+// the stage, so no staging registers or LDS stores are needed, and a token
+// outside the sequence reads a zero row kept in the work buffer.  The QK
+// operand is a plain row read of the tile; the PV operand V^T (8 tokens of
+// one value dim per lane) is read from the same tile with the gfx950
+// transposing loads ds_read_b64_tr_b8 / ds_read_b64_tr_b16, so no transposed
+// copy of V is kept.  FP8 elements are widened to BF16 in registers right
+// before each MFMA; E4M3 -> BF16 is exact, so the kv scale folds into the
+// score scale and the output.
 #include <type_traits>
 
 #include "common.h"
@@ -51,15 +52,20 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef int int2v __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;   // keep a stale running max while 2^(s - m) <= 2^8
 
+constexpr int kKBlocks = kDqk / 16;     // 36 blocks of 16 dims
 
 struct AttnArgs {
   const uint16_t *q;         // [B, qlen, H, 576] bf16 bits
   const uint8_t *pool;       // [num_pages * P, 576] cache elements
+  const uint8_t *zero_row;   // 576 zero elements (either format)
   const int32_t *row_len;    // [B*qlen]
   const int32_t *page_table; // [B*qlen, max_local_pages]
   const int32_t *work;
@@ -74,23 +80,15 @@ struct AttnArgs {
   float out_scale;           // kv_scale
 };
 
-constexpr int kKBlocks = kDqk / 16;                            // 36 blocks of 16 dims
-// Staging: 8 threads per token of a 32-token stage; thread (token tid / 8,
-// lane-in-token c = tid % 8) moves the 8-element pieces c, c + 8, ..., c + 64
-// of its token's 576-element row, so its addresses are one base plus
-// constant offsets and it needs one page id per stage.
-constexpr int kThreadsPerToken = kThreads / kStageTokens;      // 8
-constexpr int kUnitsPerThread = kDqk / 8 / kThreadsPerToken;   // 9
-static_assert(kThreadsPerToken * kStageTokens == kThreads, "staging split");
-
-// LDS tile of one stage with L-byte elements: 36 blocks of [32 token slots]
-// [16 elements].  Every access pattern (QK rows, transposing PV reads,
-// staging stores) covers whole 128-byte bank windows, so blocks need no pad.
-template <int L>
+// LDS tile of one stage with E-byte elements: 36 blocks of [32 token slots]
+// [16 elements], 18 KiB (FP8) or 36 KiB (BF16); no padding (every access
+// pattern below covers whole 128-byte bank windows).
+template <int E>
 struct Tile {
-  static constexpr int kRow = 16 * L;
+  static constexpr int kRow = 16 * E;
   static constexpr int kBlock = kStageTokens * kRow;
   static constexpr int kBytes = kKBlocks * kBlock;
+  static constexpr int kLoads = kBytes / 1024;   // 1 KiB direct loads per stage
 };
 
 // token (within a 32-token stage) held by register r of a 32x32 accumulator
@@ -99,24 +97,14 @@ struct Tile {
 // 16*kb + tau(h, e).
 __device__ inline int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-// LDS row slot of stage-token t.  The PV operand of lane half h gathers the
+// LDS row slot of stage-token t (and, being an involution -- it swaps bits 2
+// and 3 -- the token of slot t).  The PV operand of lane half h gathers the
 // eight tokens tau(h, 0..7) = {4h..4h+3, 8+4h..8+4h+3} (+16 for the second
 // token half); storing those eight rows in consecutive slots 8h..8h+7 makes
-// each 16-lane transposing read touch every bank exactly once.  QK reads all
-// 32 rows, in any order, so it does not care.
+// each 16-lane transposing read touch every bank exactly once.
 __host__ __device__ inline int tok_slot(int t) {
   return 16 * (t >> 4) + 8 * ((t >> 2) & 1) + 4 * ((t >> 3) & 1) + (t & 3);
 }
-
-template <int E>
-struct Staged {
-  typedef typename std::conditional<E == 1, uint2, uint4>::type Unit;   // 8 elements
-  Unit v[kUnitsPerThread];
-  uint32_t keep;   // 1: the token is valid, 0: store zeros
-};
-
-__device__ inline uint2 masked(uint2 v, bool k) { return k ? v : make_uint2(0, 0); }
-__device__ inline uint4 masked(uint4 v, bool k) { return k ? v : make_uint4(0, 0, 0, 0); }
 
 __device__ inline bf16x8 widen_fp8(uint2 raw) {
   const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, false);
@@ -129,61 +117,49 @@ __device__ inline bf16x8 widen_fp8(uint2 raw) {
   return r;
 }
 
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef int int2v __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) char lds_char;
-
-// QK operand (A = K): lane (token l32, half h) reads elements 8h..8h+7 of
-// block kk of its token
-template <int L>
-struct KOp {
-  typedef typename std::conditional<L == 1, uint2, uint4>::type Raw;
-};
-
-template <int L>
-__device__ inline typename KOp<L>::Raw lds_k(const uint8_t *sb, int kk, int slot, int h) {
-  return *(const typename KOp<L>::Raw *)(sb + kk * Tile<L>::kBlock + slot * Tile<L>::kRow + 8 * h * L);
+// ------------------------------------------------------------ QK operands
+//
+// Q is the stationary B operand.  Its k-slot (8h + e) of MFMA step j holds
+// dim qdim(j, h) + e:
+//   FP8 tile:  steps j = 2p + q read one 16-byte tile row per lane (block
+//              2p + h, the same token row for both steps), so
+//              qdim = 32p + 16h + 8q;
+//   BF16 tile: step j reads half h of block j, so qdim = 16j + 8h.
+// K (A operand) follows the same map; any map works as long as both agree.
+template <int E>
+__device__ inline int qdim(int j, int h) {
+  if constexpr (E == 1) return 32 * (j >> 1) + 16 * h + 8 * (j & 1);
+  else return 16 * j + 8 * h;
 }
 
-__device__ inline bf16x8 widen_k(uint2 raw) { return widen_fp8(raw); }
-__device__ inline bf16x8 widen_k(uint4 raw) { return __builtin_bit_cast(bf16x8, raw); }
-
-// PV operand (A = V^T): lane (dim 32*dblk + l32, half h) gets tokens
-// 16*kb + tau(h, e), e = 0..7, of that dim, via transposing reads.  Within a
-// 16-lane group the lane that loads address j supplies row j of a 16-row
-// (tr_b8: 8-byte, tr_b16: 4-element) block; result lane i receives column
-// i % (8 / L... ) of the rows the group loaded -- see the per-format maps.
-struct VRaw1 { int2v a; };
-struct VRaw2 { short4v a, b; };
-
-template <int L>
-struct VOp { typedef typename std::conditional<L == 1, VRaw1, VRaw2>::type Raw; };
-
-__device__ inline VRaw1 lds_v1(const uint8_t *sb, int dblk, int kb, int lane) {
-  // tr_b8: result lane 8a+b, byte k = byte b of the row loaded by lane a+2k.
-  // Loader j = a + 2k reads token 16kb + tau(h, k), dims d0 + 8a .. d0 + 8a + 7.
+// ------------------------------------------------------------ PV operands
+//
+// A = V^T: lane (dim 32*dblk + l32, half h) needs tokens 16*kb + tau(h, e),
+// e = 0..7, of that dim (slots 16*kb + 8h + e).  Transposing reads: within a
+// 16-lane group the lane that loads address j supplies one row;
+//   tr_b8:  result lane 8a+b, byte k = byte b of the row loaded by lane a+2k;
+//   tr_b16: result lane 4a+b, element k = element b of the row loaded by a+4k.
+__device__ inline int2v lds_v1(const uint8_t *sb, int dblk, int kb, int lane) {
   const int g = lane >> 4, j = lane & 15;
   const int h = g >> 1;
   const int kblk = 2 * dblk + (g & 1);
   const int k = j >> 1, a = j & 1;
-  const int slot = 16 * kb + 8 * h + k;          // tok_slot(16kb + tau(h, k))
+  const int slot = 16 * kb + 8 * h + k;
   const uint8_t *p = sb + kblk * Tile<1>::kBlock + slot * Tile<1>::kRow + 8 * a;
-  VRaw1 r;
-  r.a = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) int2v *)(lds_char *)(size_t)p);
-  return r;
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) int2v *)(lds_char *)(size_t)p);
 }
 
+struct VRaw2 { short4v a, b; };
+
 __device__ inline VRaw2 lds_v2(const uint8_t *sb, int dblk, int kb, int lane) {
-  // tr_b16: result lane 4a+b, element k = element b of the row loaded by lane
-  // a+4k.  Loader j = a + 4k reads token 16kb + tau(h, 4r + k), dims
-  // d0 + 4a .. d0 + 4a + 3, for the two halves r = 0, 1 of the 8 k-slots.
   const int g = lane >> 4, j = lane & 15;
   const int h = g >> 1;
   const int kblk = 2 * dblk + (g & 1);
   const int k = j >> 2, a = j & 3;
   const uint8_t *base = sb + kblk * Tile<2>::kBlock + 8 * a;
-  const int slot0 = 16 * kb + 8 * h + k;         // tok_slot(16kb + tau(h, k)), k < 4
-  const int slot1 = slot0 + 4;                   // tok_slot(16kb + tau(h, 4 + k))
+  const int slot0 = 16 * kb + 8 * h + k;         // tokens tau(h, k), k < 4
+  const int slot1 = slot0 + 4;                   // tokens tau(h, 4 + k)
   VRaw2 r;
   r.a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) short4v *)(lds_char *)(size_t)(base + slot0 * Tile<2>::kRow));
@@ -192,14 +168,8 @@ __device__ inline VRaw2 lds_v2(const uint8_t *sb, int dblk, int kb, int lane) {
   return r;
 }
 
-template <int L>
-__device__ inline typename VOp<L>::Raw lds_v(const uint8_t *sb, int dblk, int kb, int lane) {
-  if constexpr (L == 1) return lds_v1(sb, dblk, kb, lane);
-  else return lds_v2(sb, dblk, kb, lane);
-}
-
-__device__ inline bf16x8 widen_v(VRaw1 r) {
-  return widen_fp8(make_uint2((uint32_t)r.a[0], (uint32_t)r.a[1]));
+__device__ inline bf16x8 widen_v(int2v r) {
+  return widen_fp8(make_uint2((uint32_t)r[0], (uint32_t)r[1]));
 }
 __device__ inline bf16x8 widen_v(VRaw2 r) {
   // whole-vector reinterpretation (element-wise short -> __bf16 casts into a
@@ -209,64 +179,94 @@ __device__ inline bf16x8 widen_v(VRaw2 r) {
   return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
-// ---------------------------------------------------------------- staging
-
-// Issue the global loads of stage s for this thread's token.  A token past
-// the longest row, or on a page outside the pool, loads pool row 0 (a valid
-// address) and is marked for zeroing, so the LDS tile never holds stale
-// bytes (an FP8 NaN pattern times a zero probability would poison the
-// output).  Consecutive lanes read consecutive 8-element pieces of a row.
 template <int E>
-__device__ inline void load_stage(const AttnArgs &a, int32_t page, int s, int lmax, int tid,
-                                  Staged<E> &st, int32_t *bad) {
-  const int t = s * kStageTokens + tid / kThreadsPerToken;
+struct VOp { typedef typename std::conditional<E == 1, int2v, VRaw2>::type Raw; };
+
+template <int E>
+__device__ inline typename VOp<E>::Raw lds_v(const uint8_t *sb, int dblk, int kb, int lane) {
+  if constexpr (E == 1) return lds_v1(sb, dblk, kb, lane);
+  else return lds_v2(sb, dblk, kb, lane);
+}
+
+// ---------------------------------------------------------------- staging
+//
+// Direct load i (1 KiB) of a stage fills tile bytes [1024 i, 1024 i + 1024);
+// lane l writes 16 bytes at 1024 i + 16 l.  With the tile layout above that
+// is slot l % 32 of blocks 2i, 2i+1 (FP8) or slot l / 2, half l % 2 of block
+// i (BF16): each lane reads one token row for the whole stage.
+template <int E>
+__device__ inline int stage_slot(int lane) { return E == 1 ? (lane & 31) : (lane >> 1); }
+
+template <int E>
+__device__ inline int stage_byte(int i, int lane) {   // byte offset inside the token row
+  return E == 1 ? 16 * (2 * i + (lane >> 5)) : 32 * i + 16 * (lane & 1);
+}
+
+// Address of this lane's token row for stage s (its page id prefetched one
+// stage earlier), plus the lane's fixed byte offset inside the row.  A token
+// past the longest row, or on a page outside the pool, reads the zero row, so
+// the tile never holds stale bytes (an FP8 NaN pattern times a zero
+// probability would poison the output).
+template <int E>
+__device__ inline const uint8_t *stage_row(const AttnArgs &a, int32_t page, int s, int lmax,
+                                           int lane, int32_t *bad) {
+  const int t = s * kStageTokens + tok_slot(stage_slot<E>(lane));
   const bool in_seq = t < lmax;
   const bool ok = page >= 0 && (int64_t)page < a.num_pages;
   *bad |= (in_seq && !ok) ? 1 : 0;
-  const bool valid = in_seq && ok;
-  const int64_t row = valid ? ((int64_t)page << a.page_shift) + (t & ((1 << a.page_shift) - 1)) : 0;
-  typedef typename Staged<E>::Unit Unit;
-  const Unit *src = (const Unit *)(a.pool + (row * kDqk + 8 * (tid % kThreadsPerToken)) * E);
-#pragma unroll
-  for (int i = 0; i < kUnitsPerThread; ++i) st.v[i] = src[i * kThreadsPerToken];
-  st.keep = valid ? 1u : 0u;
-}
-
-// Write the staged pieces into the LDS tile (widening FP8 to BF16 when L = 2).
-// Piece p = c + 8i lands in block p / 2, half p % 2, row token.
-template <int E, int L>
-__device__ inline void store_stage(uint8_t *sb, int tid, const Staged<E> &st) {
-  const int tok = tid / kThreadsPerToken;
-  const int c = tid % kThreadsPerToken;
-  uint8_t *base = sb + (c >> 1) * Tile<L>::kBlock + tok_slot(tok) * Tile<L>::kRow + 8 * (c & 1) * L;
-  const bool keep = st.keep != 0;
-#pragma unroll
-  for (int i = 0; i < kUnitsPerThread; ++i) {
-    uint8_t *dst = base + 4 * i * Tile<L>::kBlock;
-    const auto v = masked(st.v[i], keep);
-    if constexpr (L == 1) {
-      *(uint2 *)dst = v;
-    } else if constexpr (E == 1) {
-      *(uint4 *)dst = __builtin_bit_cast(uint4, widen_fp8(v));
-    } else {
-      *(uint4 *)dst = v;
-    }
+  const uint8_t *row = a.zero_row;
+  if (in_seq && ok) {
+    const int64_t r = ((int64_t)page << a.page_shift) + (t & ((1 << a.page_shift) - 1));
+    row = a.pool + r * kDqk * E;
   }
+  return row + stage_byte<E>(0, lane);
 }
 
-// Page id of this thread's token of stage s (branch-free: a token past the
-// longest row reads slot 0, present whenever the sequence has a token).
-__device__ inline int32_t fetch_page(const AttnArgs &a, const int32_t *pt, int s, int lmax, int tid) {
-  const int t = s * kStageTokens + tid / kThreadsPerToken;
+template <int E>
+__device__ inline int32_t fetch_page(const AttnArgs &a, const int32_t *pt, int s, int lmax, int lane) {
+  const int t = s * kStageTokens + tok_slot(stage_slot<E>(lane));
   return pt[t < lmax ? (t >> a.page_shift) : 0];
 }
 
-template <int E, int L>
+// One direct load: 64 lanes x 16 bytes from src (per lane) to LDS bytes
+// [lds_addr + 16 lane].  M0 carries the wave-uniform LDS address; one wait
+// state must separate its write from the load.  Issued from asm so the
+// compiler does not pair every later LDS read with a wait on these loads
+// (it cannot tell the two stage tiles apart); completion is awaited
+// explicitly before the barrier that hands a tile to the other waves.
+__device__ inline void dma16(const uint8_t *src, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(lds_addr)
+      : "memory", "m0");
+}
+
+// This wave's share of a stage: loads i = wave + 4 j.  Load i reads row bytes
+// 32 i + (lane part, already in row) and fills tile bytes [1024 i, +1024).
+template <int E>
+__device__ inline void issue_stage(uint32_t tile_lds, const uint8_t *row, int wave_s) {
+  constexpr int kFull = Tile<E>::kLoads / kWaves;
+  constexpr int kRest = Tile<E>::kLoads % kWaves;
+  const uint8_t *src = row + 32 * wave_s;
+  const uint32_t dst = tile_lds + 1024 * wave_s;
+#pragma unroll
+  for (int j = 0; j < kFull; ++j) dma16(src + 128 * j, dst + 4096 * j);
+  if constexpr (kRest != 0) {
+    if (wave_s < kRest) dma16(src + 128 * kFull, dst + 4096 * kFull);
+  }
+}
+
+__device__ inline void wait_direct_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int E>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attention_kernel(AttnArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];   // two stage tiles
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];   // two stage tiles
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int h = lane >> 5;
@@ -279,6 +279,7 @@ attention_kernel(AttnArgs a) {
   const int64_t lo = group_lo(w, U, G);
   const int64_t hi = group_lo(w + 1, U, G);
   const int32_t *unit_base = a.work + work_unit_base_off();
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_char *)lds);
   int32_t bad = 0;
 
   int slot = 0;
@@ -305,19 +306,22 @@ attention_kernel(AttnArgs a) {
     const int vrow = mvalid ? m / a.H : 0;
     const int rlen = mvalid ? a.row_len[b * a.qlen + vrow] : 0;
 
-    // page id of this thread's token in the first stage
-    int32_t page = fetch_page(a, pt, st0, lmax, tid);
+    // first stage: page id, then its direct loads; later stages are fetched
+    // one stage ahead
+    int32_t page = fetch_page<E>(a, pt, st0, lmax, lane);
+    issue_stage<E>(lds_base, stage_row<E>(a, page, st0, lmax, lane, &bad), wave);
+    if (st0 + 1 < st1) page = fetch_page<E>(a, pt, st0 + 1, lmax, lane);
 
     bf16x8 qf[kKBlocks];
     {
       // rows past M read row M-1 (a valid address) and are zeroed
-      const uint16_t *qrow = a.q + ((int64_t)b * a.M + (mvalid ? m : a.M - 1)) * kDqk + 8 * h;
+      const uint16_t *qrow = a.q + ((int64_t)b * a.M + (mvalid ? m : a.M - 1)) * kDqk;
       const uint32_t keep = mvalid ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-      for (int kk = 0; kk < kKBlocks; ++kk) {
-        uint4 v = *(const uint4 *)(qrow + 16 * kk);
+      for (int j = 0; j < kKBlocks; ++j) {
+        uint4 v = *(const uint4 *)(qrow + qdim<E>(j, h));
         v.x &= keep; v.y &= keep; v.z &= keep; v.w &= keep;
-        qf[kk] = __builtin_bit_cast(bf16x8, v);
+        qf[j] = __builtin_bit_cast(bf16x8, v);
       }
     }
 
@@ -330,32 +334,48 @@ attention_kernel(AttnArgs a) {
     float lsum = 0.f;    // sum of the BF16 probabilities fed to the PV MFMAs: normalises O
     float lsum_f = 0.f;  // fp32 sum of the same probabilities before rounding: gives the LSE
 
-    Staged<E> st;
-    load_stage<E>(a, page, st0, lmax, tid, st, &bad);
-    if (st0 + 1 < st1) page = fetch_page(a, pt, st0 + 1, lmax, tid);
-    store_stage<E, L>(lds, tid, st);
+    wait_direct_loads();
     __syncthreads();
 
     for (int s = st0; s < st1; ++s) {
       const int cur = (s - st0) & 1;
       const bool more = s + 1 < st1;
-      if (more) load_stage<E>(a, page, s + 1, lmax, tid, st, &bad);
-      if (s + 2 < st1) page = fetch_page(a, pt, s + 2, lmax, tid);
-      const uint8_t *sb = lds + cur * Tile<L>::kBytes;
+      if (more) {
+        issue_stage<E>(lds_base + (cur ^ 1) * Tile<E>::kBytes,
+                       stage_row<E>(a, page, s + 1, lmax, lane, &bad), wave);
+        if (s + 2 < st1) page = fetch_page<E>(a, pt, s + 2, lmax, lane);
+      }
+      const uint8_t *sb = lds + cur * Tile<E>::kBytes;
 
-      // S^T[token, row] = K Q^T over 576 dims; operands prefetched two ahead
+      // S^T[token, row] = K Q^T over 576 dims
       floatx16 sacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-      {
-        typename KOp<L>::Raw kr[2];
-        kr[0] = lds_k<L>(sb, 0, kslot, h);
-        kr[1] = lds_k<L>(sb, 1, kslot, h);
+      if constexpr (E == 1) {
+        // one 16-byte tile row per lane feeds two MFMA steps
+        const uint8_t *kb0 = sb + h * Tile<1>::kBlock + kslot * Tile<1>::kRow;
+        uint4 kr[2];
+        kr[0] = *(const uint4 *)(kb0);
+        kr[1] = *(const uint4 *)(kb0 + 2 * Tile<1>::kBlock);
 #pragma unroll
-        for (int kk = 0; kk < kKBlocks; ++kk) {
-          const bf16x8 kop = widen_k(kr[kk & 1]);
-          if (kk + 2 < kKBlocks) kr[kk & 1] = lds_k<L>(sb, kk + 2, kslot, h);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[kk], sacc, 0, 0, 0);
+        for (int p = 0; p < kKBlocks / 2; ++p) {
+          const uint4 cur_row = kr[p & 1];
+          if (p + 2 < kKBlocks / 2) kr[p & 1] = *(const uint4 *)(kb0 + 2 * (p + 2) * Tile<1>::kBlock);
+          const bf16x8 k0 = widen_fp8(make_uint2(cur_row.x, cur_row.y));
+          const bf16x8 k1 = widen_fp8(make_uint2(cur_row.z, cur_row.w));
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[2 * p], sacc, 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[2 * p + 1], sacc, 0, 0, 0);
+        }
+      } else {
+        const uint8_t *kb0 = sb + kslot * Tile<2>::kRow + 16 * h;
+        uint4 kr[2];
+        kr[0] = *(const uint4 *)(kb0);
+        kr[1] = *(const uint4 *)(kb0 + Tile<2>::kBlock);
+#pragma unroll
+        for (int j = 0; j < kKBlocks; ++j) {
+          const bf16x8 kop = __builtin_bit_cast(bf16x8, kr[j & 1]);
+          if (j + 2 < kKBlocks) kr[j & 1] = *(const uint4 *)(kb0 + (j + 2) * Tile<2>::kBlock);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[j], sacc, 0, 0, 0);
         }
       }
 
@@ -413,19 +433,21 @@ attention_kernel(AttnArgs a) {
 
       // O^T[d, row] += V^T[d, token] P^T[token, row]; operands prefetched two ahead
       {
-        typename VOp<L>::Raw vr[2];
-        vr[0] = lds_v<L>(sb, 0, 0, lane);
-        vr[1] = lds_v<L>(sb, 0, 1, lane);
+        typename VOp<E>::Raw vr[2];
+        vr[0] = lds_v<E>(sb, 0, 0, lane);
+        vr[1] = lds_v<E>(sb, 0, 1, lane);
 #pragma unroll
         for (int i = 0; i < kDv / 16; ++i) {
           const int d = i >> 1, kb = i & 1;
           const bf16x8 vop = widen_v(vr[i & 1]);
-          if (i + 2 < kDv / 16) vr[i & 1] = lds_v<L>(sb, (i + 2) >> 1, (i + 2) & 1, lane);
+          if (i + 2 < kDv / 16) vr[i & 1] = lds_v<E>(sb, (i + 2) >> 1, (i + 2) & 1, lane);
           oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[kb], oacc[d], 0, 0, 0);
         }
       }
 
-      if (more) store_stage<E, L>(lds + (cur ^ 1) * Tile<L>::kBytes, tid, st);
+      // the next stage's direct loads (this wave's share) have landed; the
+      // barrier makes every wave's share visible and frees the current tile
+      wait_direct_loads();
       __syncthreads();
     }
 
@@ -472,6 +494,20 @@ attention_kernel(AttnArgs a) {
   if (bad) atomicOr(a.err, DCPMLA_ERR_PAGE_RANGE);
 }
 
+template <int E>
+hipError_t launch_tile(const AttnArgs &a, int groups, hipStream_t stream) {
+  const size_t shmem = 2 * Tile<E>::kBytes;
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void *)attention_kernel<E>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(attention_kernel<E>, dim3(groups), dim3(kThreads), shmem, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_partial_attention(const dcpmla_geom &g, int groups, const void *q,
@@ -481,6 +517,7 @@ hipError_t launch_partial_attention(const dcpmla_geom &g, int groups, const void
   AttnArgs a;
   a.q = (const uint16_t *)q;
   a.pool = (const uint8_t *)kv_pool;
+  a.zero_row = (const uint8_t *)(m.work + work_zero_off(g.batch));
   a.row_len = m.row_local_len;
   a.page_table = m.page_table;
   a.work = m.work;
@@ -502,44 +539,8 @@ hipError_t launch_partial_attention(const dcpmla_geom &g, int groups, const void
   a.max_local_pages = g.max_local_pages;
   a.score_scale2 = softmax_scale * kv_scale * 1.44269504088896340736f;
   a.out_scale = kv_scale;
-  const size_t extra = 0;
-  if (g.kv_dtype == DCPMLA_KV_FP8_E4M3) {
-    // FP8 cache: the LDS tile keeps FP8 bytes (widened per operand) unless
-    // DCPMLA_LDS_BF16=1 asks for widening once while staging
-    static const bool widen_at_stage = getenv("DCPMLA_LDS_BF16") && atoi(getenv("DCPMLA_LDS_BF16")) == 1;
-    if (widen_at_stage) {
-      const size_t shmem = 2 * Tile<2>::kBytes + extra;
-      static bool attr_set = false;
-      if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)attention_kernel<1, 2>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-      }
-      hipLaunchKernelGGL((attention_kernel<1, 2>), dim3(groups), dim3(kThreads), shmem, stream, a);
-    } else {
-      const size_t shmem = 2 * Tile<1>::kBytes + extra;
-      static bool attr_set = false;
-      if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)attention_kernel<1, 1>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-      }
-      hipLaunchKernelGGL((attention_kernel<1, 1>), dim3(groups), dim3(kThreads), shmem, stream, a);
-    }
-  } else {
-    const size_t shmem = 2 * Tile<2>::kBytes + extra;
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void *)attention_kernel<2, 2>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
-    hipLaunchKernelGGL((attention_kernel<2, 2>), dim3(groups), dim3(kThreads), shmem, stream, a);
-  }
-  return hipGetLastError();
+  if (g.kv_dtype == DCPMLA_KV_FP8_E4M3) return launch_tile<1>(a, groups, stream);
+  return launch_tile<2>(a, groups, stream);
 }
 
 }  // namespace dcpmla

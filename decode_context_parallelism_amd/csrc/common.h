@@ -23,7 +23,12 @@ constexpr int kSlots = 2;          // partial slots per persistent workgroup
 // [B+2 .. 2B+2) stages[b]; [2B+2 .. 3B+2) longest rank-local row length lmax[b];
 // [3B+2 .. 4B+2) the verify row (b*qlen + i) that has that length.  A unit is
 // one 32-token stage of one (sequence, head-row tile).
-__host__ __device__ inline int64_t work_ints(int batch) { return 4 * (int64_t)batch + 2; }
+// Past the partition, a zero row of kZeroInts int32 (one 576-element latent
+// row in either cache format) that attention reads for tokens outside a
+// sequence; the builder rewrites it with every forward.
+constexpr int kZeroInts = kDqk * 2 / 4;
+__host__ __device__ inline int64_t work_zero_off(int batch) { return ((4 * (int64_t)batch + 2 + 63) / 64) * 64; }
+__host__ __device__ inline int64_t work_ints(int batch) { return work_zero_off(batch) + kZeroInts; }
 __host__ __device__ inline int work_unit_base_off() { return 1; }
 __host__ __device__ inline int work_stages_off(int batch) { return batch + 2; }
 __host__ __device__ inline int work_lmax_off(int batch) { return 2 * batch + 2; }

@@ -115,6 +115,7 @@ __global__ void __launch_bounds__(256) meta_work_kernel(int B, int qlen, int n_m
     work[work_unit_base_off() + B] = s_carry;
     work[0] = s_carry;
   }
+  for (int i = tid; i < kZeroInts; i += 256) work[work_zero_off(B) + i] = 0;
 }
 
 hipError_t launch_build_metadata(const dcpmla_geom &g, int rank, const int32_t *ctx_lens,

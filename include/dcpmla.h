@@ -106,7 +106,9 @@ typedef struct dcpmla_meta {
   int32_t *page_table;      /* [B*qlen, max_local_pages] subpage ids, -1 = unused */
   int32_t *last_page_len;   /* [B*qlen]   tokens in the row's last subpage (0 if none) */
   int32_t *err;             /* [1]        device error word (DCPMLA_ERR_* bits), OR-ed */
-  int32_t *work;            /* [dcpmla_work_ints()] split-KV work partition (opaque) */
+  int32_t *work;            /* [dcpmla_work_ints()] split-KV work partition and one zero
+                               latent row that stands in for tokens outside a sequence
+                               (opaque; written by dcpmla_build_metadata) */
 } dcpmla_meta;
 
 /* Host only.  DCPMLA_OK or DCPMLA_E_INVALID. */

@@ -81,7 +81,8 @@ def test_subpage_size_matches_oracle():
 
 def test_sizes():
     g = _geom(batch=5)
-    assert ops.work_ints(g) == 4 * 5 + 2
+    # partition (4B + 2 ints), padded to 64 ints, then one zero latent row
+    assert ops.work_ints(g) == 64 + 576 * 2 // 4
     ws = ops.workspace_bytes(g)
     assert ws == 4 * 2 * 128 * (512 + 1) * 4
     assert ops.workspace_bytes(_geom(groups=1)) * 4 == ws

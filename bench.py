@@ -1,33 +1,49 @@
 #!/usr/bin/env python
 """Throughput of DCP MLA causal verification on one MI355X.
 
-One step = the whole hot path for one batch, every DCP rank played in turn on
-this GPU: verify-view metadata for each rank, each rank's segmented split-KV
+One step = one pass of the whole hot path over one batch, every DCP rank
+played in turn on this GPU: the verify-view metadata of each rank (row
+boundary, rank-local length, subpage table), each rank's segmented split-KV
 attention and segment merge, then the cross-rank LSE merge.  Inputs (query,
-per-rank KV pools, block tables, contexts) are resident in HBM before the
-timed region; the KV pools are written once, untimed, by the library's
-interleaved KV write.
+per-rank KV pools, block table, contexts) are resident in HBM before the
+timed region; the pools are written once, untimed, by the library's
+interleaved KV write.  When the pools of all ranks together fit in the
+256 MB Infinity Cache, the step rotates over enough copies of the inputs
+that every step reads its KV from HBM.
 
-Prints one JSON line.  ``value`` = KV tokens attended per second on this GPU
-(every global cached token is read once per step, by its owner rank).
-``roofline`` describes the dominant kernel (segmented attention), timed with
-HIP events around each of its launches on the stream it runs on.
-``cpu_baseline`` times the float64 oracle on a bounded sample of the same
-workload (rank 0, first sequences) on the host cores.
+Prints one JSON line:
+  value       global KV tokens attended per second (every cached token of
+              every sequence is read once per step, by its owner rank)
+  roofline    the dominant kernel (segmented attention), timed with HIP
+              events around each launch on the stream it runs on, against
+              the binding published MI355X peak (BF16 MFMA or HBM); traffic
+              = HBM bytes per launch from the rocprofv3 counter summary under
+              profiles/ when that summary was taken from the current kernel
+              source, else null
+  cpu_baseline  the float64 oracle timed on this host over a bounded sample
+              of the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1..5]
 """
 import argparse
+import hashlib
 import json
+import math
 import os
+import re
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
+# published MI355X peaks (dense)
+PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_BF16_TFLOPS = 2500.0
+# flops per clock per CU of dense BF16 MFMA on gfx950 (4 SIMDs x 1024)
+BF16_FLOPS_PER_CLK_CU = 4096
+INFINITY_CACHE_BYTES = 256 << 20
+ATTN_SOURCE = os.path.join(ROOT, "decode_context_parallelism_amd", "csrc", "attention.hip")
 
 
 def parse():
@@ -40,8 +56,10 @@ def parse():
     ap.add_argument("--groups", type=int, default=0,
                     help="persistent workgroups of the attention kernel (0: one per compute unit)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="budget of the oracle's timed CPU sample")
+                    help="target length of the oracle's timed CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rotate", action="store_true",
+                    help="reuse one input set every step (cache-warm KV)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
@@ -60,9 +78,35 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}))
 
 
+def source_digest():
+    with open(ATTN_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic(workload, digest):
+    """HBM bytes per attention launch from the committed counter summary, or None."""
+    path = os.path.join(ROOT, "profiles", f"attention_kernel_{workload}_hbm.md")
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    kv = {}
+    for line in open(path):
+        m = re.match(r"^\s*[-*]?\s*`?([a-z_0-9]+)`?\s*[:=]\s*`?([0-9a-fA-F.e+-]+)`?\s*$", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("kernel_source_sha256") != digest:
+        return None, "kernel changed since the counters were taken"
+    try:
+        fetch = float(kv["fetch_kib_per_launch"]) * 1024 * float(kv["fetch_scale"])
+        write = float(kv["write_kib_per_launch"]) * 1024 * float(kv["write_scale"])
+    except KeyError:
+        return None, "counter summary incomplete"
+    return fetch + write, os.path.relpath(path, ROOT)
+
+
 def cpu_baseline(w, seconds):
-    """Time the float64 oracle on rank 0 of the same workload (a bounded sample)."""
-    import numpy as np
+    """Time the float64 oracle on this host: each rank's partial attention over
+    whole sequences, ranks and sequences in order, repeated until the budget is
+    spent (at least one (rank, sequence) pair)."""
     from threadpoolctl import threadpool_info
 
     from oracle import attention as A
@@ -71,24 +115,30 @@ def cpu_baseline(w, seconds):
     q = formats.decode_bf16(w.q_bits)
     lat = lambda b, pos: formats.decode_cache(w.kv[w.seq_start[b] + pos], w.kv_format, w.kv_scale)
     tokens = 0
-    seqs = 0
+    pairs = 0
     t0 = time.perf_counter()
-    for b in range(w.batch):
-        rows = [(b, i) for i in range(w.qlen)]
-        A.verify_attention(q, lat, w.ctx_lens, w.softmax_scale, world=w.world,
-                           interleave=w.interleave, rank=0, rows=rows)
-        g_last = layout.verify_row_boundary(int(w.ctx_lens[b]), w.qlen, w.qlen - 1)
-        tokens += layout.rank_local_positions(g_last, w.world, w.interleave, 0).shape[0]
-        seqs += 1
-        if time.perf_counter() - t0 > seconds:
-            break
+    done = False
+    while not done:
+        for r in range(w.world):
+            for b in range(w.batch):
+                rows = [(b, i) for i in range(w.qlen)]
+                A.verify_attention(q, lat, w.ctx_lens, w.softmax_scale, world=w.world,
+                                   interleave=w.interleave, rank=r, rows=rows)
+                g_last = layout.verify_row_boundary(int(w.ctx_lens[b]), w.qlen, w.qlen - 1)
+                tokens += layout.rank_local_positions(g_last, w.world, w.interleave, r).shape[0]
+                pairs += 1
+                if time.perf_counter() - t0 > seconds:
+                    done = True
+                    break
+            if done:
+                break
     dt = time.perf_counter() - t0
     threads = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
     return {"value": tokens / dt, "unit": "KV tokens/s", "cores": int(max(threads) if threads else 1),
             "kind": "oracle",
-            "sample": f"float64 oracle, rank 0 of {w.world}, sequences 0..{seqs - 1} of {w.batch}, "
-                      f"all {w.qlen} verify rows x {w.heads} heads ({tokens} rank-local KV tokens, "
-                      f"{dt:.1f} s)"}
+            "sample": f"float64 oracle (numpy BLAS), per-rank partial attention of {pairs} (rank, sequence) "
+                      f"pairs taken in order over {w.world} ranks x {w.batch} sequences, all {w.qlen} verify "
+                      f"rows x {w.heads} heads each: {tokens} rank-local KV tokens in {dt:.1f} s"}
 
 
 def main():
@@ -110,13 +160,14 @@ def main():
     from synth import make_config
 
     torch.cuda.set_device(0)
+    dev_info = ops.device_info(0)
     w = make_config(args.config)
     g = ops.Geometry(dcp_world=w.world, interleave=w.interleave, block_size=w.block_size,
                      qlen=w.qlen, num_heads=w.heads, batch=w.batch,
                      max_blocks_per_seq=w.block_table.shape[1], max_local_pages=w.max_local_pages,
                      kv_dtype=w.kv_format, num_blocks=w.num_blocks, groups=args.groups)
     dev = "cuda"
-    q = torch.from_numpy(w.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    q0 = torch.from_numpy(w.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     if w.kv_format == "fp8_e4m3":
         lat = torch.from_numpy(w.kv).to(dev)
     else:
@@ -128,77 +179,109 @@ def main():
     grp.write_kv(torch.from_numpy(seq_ids).to(dev), torch.from_numpy(positions).to(dev), lat, bt)
     del lat
     torch.cuda.synchronize()
+    if grp.errors() != 0:
+        raise RuntimeError(f"device error word {grp.errors():#x} after the KV write")
 
+    # input sets: the step reads set k % n_sets, so the KV of a step is not
+    # left in the Infinity Cache by the previous one
     W = w.world
+    pool_bytes = sum(p.numel() * p.element_size() for p in grp.pools)
+    n_sets = 1 if args.no_rotate else min(16, max(1, math.ceil(2 * INFINITY_CACHE_BYTES / pool_bytes)))
+    sets = [(grp.pools, q0)]
+    for _ in range(n_sets - 1):
+        sets.append(([p.clone() for p in grp.pools], q0.clone()))
+    torch.cuda.synchronize()
+
     stream = torch.cuda.current_stream()
 
-    def step(events=None):
+    def step(k, events=None):
+        pools, q = sets[k % n_sets]
         for r in range(W):
             ops.build_metadata(g, r, ctx, bt, grp.meta[r], stream)
         for r in range(W):
             if events is not None:
                 events[r][0].record(stream)
-            ops.partial_attention(g, q, grp.pools[r], w.kv_scale, w.softmax_scale, grp.meta[r],
+            ops.partial_attention(g, q, pools[r], w.kv_scale, w.softmax_scale, grp.meta[r],
                                   grp.workspace, grp.out_ranks[r], grp.lse_ranks[r], stream)
             if events is not None:
                 events[r][1].record(stream)
             ops.merge_segments(g, grp.meta[r], grp.workspace, grp.out_ranks[r], grp.lse_ranks[r],
                                stream)
+            if events is not None:
+                events[r][2].record(stream)
         ops.merge_ranks(grp.out_ranks, grp.lse_ranks, grp.out, grp.lse, stream)
 
-    for _ in range(args.warmup):
-        step()
+    for k in range(args.warmup):
+        step(k)
     torch.cuda.synchronize()
     if grp.errors() != 0:
         raise RuntimeError(f"device error word {grp.errors():#x}")
 
-    # algorithmic work per rank launch, from the verify view the kernels consume
+    # algorithmic work of each rank's attention launch, from the verify view
     E = 1 if w.kv_format == "fp8_e4m3" else 2
-    flops, kv_bytes = [], []
+    flops, kv_bytes, lmax_tokens = [], [], []
     for r in range(W):
         lens = grp.meta[r].row_local_len.cpu().numpy().astype(np.int64).reshape(w.batch, w.qlen)
         flops.append(2 * (576 + 512) * w.heads * int(lens.sum()))
-        kv_bytes.append(int(lens.max(axis=1).sum()) * 576 * E)
-    io_bytes = w.batch * w.qlen * w.heads * (576 * 2 + 512 * 2 + 4)
+        lmax_tokens.append(int(lens.max(axis=1).sum()))
+        kv_bytes.append(lmax_tokens[-1] * 576 * E)
+    io_bytes = w.batch * w.qlen * w.heads * (576 * 2 + 512 * 2 + 4) + w.batch * w.qlen * 4
+    alg_bytes = [kb + io_bytes for kb in kv_bytes]
 
-    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-               for _ in range(W)] for _ in range(args.steps)]
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(W)]
+              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(events[k])
+        step(args.warmup + k, events[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    if grp.errors() != 0:
+        raise RuntimeError(f"device error word {grp.errors():#x}")
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    kern_ms = [[events[k][r][0].elapsed_time(events[k][r][1]) for r in range(W)]
-               for k in range(args.steps)]
-    kern_total_ms = float(np.sum(kern_ms))
-    launches = args.steps * W
-    avg_kernel_ms = kern_total_ms / launches
-    total_flops = args.steps * sum(flops)
-    total_bytes = args.steps * (sum(kv_bytes) + W * io_bytes)
-    tflops = total_flops / (kern_total_ms * 1e-3) / 1e12
-    gbs = total_bytes / (kern_total_ms * 1e-3) / 1e9
-    t_mfma = sum(flops) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
-    t_hbm = (sum(kv_bytes) + W * io_bytes) / (HBM_PEAK_GBS * 1e9)
+    attn_ms = np.array([[events[k][r][0].elapsed_time(events[k][r][1]) for r in range(W)]
+                        for k in range(args.steps)])
+    attn_merge_ms = np.array([[events[k][r][0].elapsed_time(events[k][r][2]) for r in range(W)]
+                              for k in range(args.steps)])
+    avg_launch_ms = float(attn_ms.mean())
+    per_rank_ms = attn_ms.mean(axis=0)
+
+    # roofline of the attention kernel against the published peaks
+    t_mfma = sum(flops) / (PEAK_MFMA_BF16_TFLOPS * 1e12)
+    t_hbm = sum(alg_bytes) / (PEAK_HBM_GBS * 1e9)
+    tflops = sum(flops) / (float(per_rank_ms.sum()) * 1e-3) / 1e12
+    gbs = sum(alg_bytes) / (float(per_rank_ms.sum()) * 1e-3) / 1e9
+    digest = source_digest()
+    traffic, traffic_src = read_traffic(w.name, digest)
     if t_mfma >= t_hbm:
-        roof = {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+        roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / PEAK_MFMA_BF16_TFLOPS}
     else:
-        roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": gbs / HBM_PEAK_GBS, "traffic": None}
-    roof.update({"kernel": "attention_kernel (segmented split-KV MLA, one rank)",
-                 "avg_launch_ms": avg_kernel_ms, "launches": launches,
-                 "algorithmic_flops_per_launch": sum(flops) / W,
-                 "algorithmic_bytes_per_launch": (sum(kv_bytes) + W * io_bytes) / W,
-                 "hbm_achieved_GBs": gbs})
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS}
+    roof["traffic"] = traffic
+    roof.update({
+        "kernel": "attention_kernel (segmented split-KV MLA, one rank per launch)",
+        "avg_launch_ms": avg_launch_ms, "launches": int(attn_ms.size),
+        "algorithmic_flops_per_launch": sum(flops) / W,
+        "algorithmic_bytes_per_launch": sum(alg_bytes) / W,
+        "algorithmic_hbm_GBs": gbs,
+        "traffic_source": traffic_src,
+        "kernel_source_sha256": digest,
+    })
+
+    clk_ghz = dev_info["clock_khz"] / 1e6
+    device = dict(dev_info)
+    device["mfma_bf16_peak_tflops_from_clock"] = (dev_info["compute_units"] * clk_ghz * 1e9 *
+                                                  BF16_FLOPS_PER_CLK_CU / 1e12)
+    device["peaks_used"] = {"mfma_bf16_tflops": PEAK_MFMA_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS,
+                            "source": "published MI355X figures"}
 
     kv_tokens = int(w.ctx_lens.astype(np.int64).sum())
-    value = kv_tokens / (ms_per_step * 1e-3)
     out = {
         "metric": "DCP-MLA verify: KV tokens/s per GPU and % of binding roofline (HBM or MFMA)",
-        "value": value,
+        "value": kv_tokens / (ms_per_step * 1e-3),
         "unit": "KV tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -212,9 +295,18 @@ def main():
         "config": {"workload": w.name, "dcp_world": W, "interleave": w.interleave,
                    "batch": w.batch, "qlen": w.qlen, "heads": w.heads,
                    "block_size": w.block_size, "kv_cache": w.kv_format,
-                   "kv_tokens_per_step": kv_tokens, "ranks_per_step": W},
+                   "kv_tokens_per_step": kv_tokens, "ranks_per_step": W, "input_sets": n_sets},
         "verify_rows_per_s": w.batch * w.qlen / (ms_per_step * 1e-3),
+        "per_rank": {
+            "attention_us_mean": float(per_rank_ms.mean() * 1e3),
+            "attention_us_max": float(per_rank_ms.max() * 1e3),
+            "attention_plus_segment_merge_us_mean": float(attn_merge_ms.mean(axis=0).mean() * 1e3),
+            "attention_plus_segment_merge_us_max": float(attn_merge_ms.mean(axis=0).max() * 1e3),
+            "local_kv_tokens_per_s": float(np.mean([lmax_tokens[r] / (per_rank_ms[r] * 1e-3)
+                                                    for r in range(W)])),
+        },
         "roofline": roof,
+        "device": device,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

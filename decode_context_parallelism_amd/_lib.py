@@ -62,6 +62,13 @@ _I64 = ctypes.c_int64
 _F = ctypes.c_float
 
 #: every entry point of include/dcpmla.h with (restype, argtypes)
+class DeviceInfo(ctypes.Structure):
+    """Mirror of ``dcpmla_device_info``."""
+    _fields_ = [("compute_units", ctypes.c_int32), ("clock_khz", ctypes.c_int32),
+                ("memory_clock_khz", ctypes.c_int32), ("memory_bus_bits", ctypes.c_int32),
+                ("lds_bytes_per_block", ctypes.c_int64), ("arch", ctypes.c_char * 64)]
+
+
 SIGNATURES = {
     "dcpmla_validate": (ctypes.c_int, [_G]),
     "dcpmla_subpage_size": (_I32, [_I32]),
@@ -75,6 +82,7 @@ SIGNATURES = {
     "dcpmla_merge_ranks": (ctypes.c_int, [_I32, _I64, _P, _P, _P, _P, _P]),
     "dcpmla_merge_segments_dense": (ctypes.c_int, [_I64, _I32, _P, _P, _P, _P, _P]),
     "dcpmla_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "dcpmla_get_device_info": (ctypes.c_int, [_I32, ctypes.c_void_p]),
 }
 
 

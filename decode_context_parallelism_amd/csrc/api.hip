@@ -1,6 +1,8 @@
 // C ABI entry points: argument validation, aliasing checks, launches.
 #include <string.h>
 
+#include <cstring>
+
 #include "common.h"
 #include "launch.h"
 
@@ -254,6 +256,21 @@ const char *dcpmla_strerror(int status) {
     case DCPMLA_E_HIP: return "HIP runtime error";
     default: return "unknown status";
   }
+}
+
+
+int dcpmla_get_device_info(int32_t device, dcpmla_device_info *out) {
+  if (!out) return DCPMLA_E_INVALID;
+  hipDeviceProp_t p;
+  if (hipGetDeviceProperties(&p, device) != hipSuccess) return DCPMLA_E_HIP;
+  out->compute_units = p.multiProcessorCount;
+  out->clock_khz = p.clockRate;
+  out->memory_clock_khz = p.memoryClockRate;
+  out->memory_bus_bits = p.memoryBusWidth;
+  out->lds_bytes_per_block = (int64_t)p.sharedMemPerBlock;
+  std::memset(out->arch, 0, sizeof(out->arch));
+  std::strncpy(out->arch, p.gcnArchName, sizeof(out->arch) - 1);
+  return DCPMLA_OK;
 }
 
 }  // extern "C"

@@ -106,6 +106,28 @@ __host__ __device__ inline int tok_slot(int t) {
   return 16 * (t >> 4) + 8 * ((t >> 2) & 1) + 4 * ((t >> 3) & 1) + (t & 3);
 }
 
+// Value of lane l ^ 32 (the other half of the 32x32 accumulator column),
+// from v_permlane32_swap: it exchanges the upper half of its first operand
+// with the lower half of its second, so for lanes below 32 the second result
+// holds the upper half's value and for the others the first result holds the
+// lower half's.  The first operand goes through an empty asm so the compiler
+// sees two distinct inputs and keeps both results.
+__device__ inline float other_half(float x, int h) {
+  uint32_t y = __builtin_bit_cast(uint32_t, x);
+  asm volatile("" : "+v"(y));
+  const auto r = __builtin_amdgcn_permlane32_swap(y, __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, h ? r[0] : r[1]);
+}
+
+// acc + both BF16 values of a packed pair (a dot product with (1, 1): the
+// products are exact)
+__device__ inline float sum_bf16_pair(uint32_t pair, float acc) {
+  bf16x2 one;
+  one[0] = (__bf16)1.0f;
+  one[1] = (__bf16)1.0f;
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+}
+
 __device__ inline bf16x8 widen_fp8(uint2 raw) {
   const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, false);
   const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, true);
@@ -229,19 +251,24 @@ __device__ inline int32_t fetch_page(const AttnArgs &a, const int32_t *pt, int s
 }
 
 // One direct load: 64 lanes x 16 bytes from src (per lane) to LDS bytes
-// [lds_addr + 16 lane].  M0 carries the wave-uniform LDS address; one wait
-// state must separate its write from the load.  Issued from asm so the
-// compiler does not pair every later LDS read with a wait on these loads
-// (it cannot tell the two stage tiles apart); completion is awaited
-// explicitly before the barrier that hands a tile to the other waves.
+// [lds_addr + 16 lane].  M0 carries the wave-uniform LDS address (one wait
+// state between its write and the load); the block restores the caller's M0,
+// which the compiler treats as a reserved register.  Issued from asm so the
+// compiler does not pair every later LDS read with a wait on these loads (it
+// cannot tell the stage tiles apart); completion is awaited explicitly before
+// the barrier that hands a tile to the other waves.
 __device__ inline void dma16(const uint8_t *src, uint32_t lds_addr) {
+  uint32_t saved;
   asm volatile(
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
       : "v"(src), "s"(lds_addr)
-      : "memory", "m0");
+      : "memory");
 }
 
 // This wave's share of a stage: loads i = wave + 4 j.  Load i reads row bytes
@@ -304,7 +331,9 @@ attention_kernel(AttnArgs a) {
     const int m = mt * kTileRows + wave * kWaveRows + l32;
     const bool mvalid = m < a.M;
     const int vrow = mvalid ? m / a.H : 0;
-    const int rlen = mvalid ? a.row_len[b * a.qlen + vrow] : 0;
+    // rows past M (zero queries) see every token: their results are never
+    // stored, and they keep the wave on the unmasked path
+    const int rlen = mvalid ? a.row_len[b * a.qlen + vrow] : 0x3FFFFFFF;
 
     // first stage: page id, then its direct loads; later stages are fetched
     // one stage ahead
@@ -379,17 +408,27 @@ attention_kernel(AttnArgs a) {
         }
       }
 
-      // online softmax in base 2 on this lane's 16 tokens of head-row m
+      // online softmax in base 2 on this lane's 16 tokens of head-row m.  The
+      // raw scores are kept: the max commutes with the positive scale, which
+      // is applied inside the exponent.  Register r holds token
+      // t0 + 4h + row_of(r) with row_of(r) = 8(r/4) + r%4 <= 27, so a stage
+      // lies wholly inside every row window of the wave when
+      // rlen - t0 - 4h > 27 on all lanes; only the last stages of a window
+      // need the per-token mask.
       const int t0 = s * kStageTokens;
+      const int lim = rlen - t0 - 4 * h;
       float sv[16];
+      if (__all(lim > 27)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sv[r] = sacc[r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sv[r] = (8 * (r >> 2) + (r & 3)) < lim ? sacc[r] : kNegInf;
+      }
       float mx = kNegInf;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool valid = t0 + acc_row(r, h) < rlen;
-        sv[r] = valid ? sacc[r] * a.score_scale2 : kNegInf;
-        mx = fmaxf(mx, sv[r]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[r]);
+      mx = fmaxf(mx, other_half(mx, h)) * a.score_scale2;
       const float mnew = fmaxf(mrun, mx);
       const bool need = mnew > mrun + kRescaleSlack;
       const float alpha = need ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.0f;
@@ -420,15 +459,23 @@ attention_kernel(AttnArgs a) {
           }
         }
       }
+      // p = 2^(score * scale - mrun); masked scores give 2^-inf = 0, and a row
+      // with nothing visible yet subtracts 0 instead of -inf
+      const float msub = mrun > kNegInf ? mrun : 0.f;
       bf16x8 pb[2];
-      const bool live = mrun > kNegInf;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = live ? __builtin_amdgcn_exp2f(sv[r] - mrun) : 0.f;
-        const __bf16 pr = (__bf16)p;
-        pb[r >> 3][r & 7] = pr;
-        lsum += (float)pr;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], a.score_scale2, -msub));
+        pb[r >> 3][r & 7] = (__bf16)p;
         lsum_f += p;
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint4 w4 = __builtin_bit_cast(uint4, pb[j]);
+        lsum = sum_bf16_pair(w4.x, lsum);
+        lsum = sum_bf16_pair(w4.y, lsum);
+        lsum = sum_bf16_pair(w4.z, lsum);
+        lsum = sum_bf16_pair(w4.w, lsum);
       }
 
       // O^T[d, row] += V^T[d, token] P^T[token, row]; operands prefetched two ahead
@@ -452,8 +499,8 @@ attention_kernel(AttnArgs a) {
     }
 
     // finish the piece
-    const float ltot = lsum + __shfl_xor(lsum, 32);
-    const float ltot_f = lsum_f + __shfl_xor(lsum_f, 32);
+    const float ltot = lsum + other_half(lsum, h);
+    const float ltot_f = lsum_f + other_half(lsum_f, h);
     const bool has = ltot > 0.f;
     const float inv = has ? a.out_scale / ltot : 0.f;
     const float lse2 = has ? mrun + __builtin_amdgcn_logf(ltot_f) : kNegInf;

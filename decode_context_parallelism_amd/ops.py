@@ -224,3 +224,12 @@ def merge_segments_dense(o_seg, lse2_seg, out, lse, stream=None) -> None:
     _check(lib.dcpmla_merge_segments_dense(rows, nseg, _ptr(o_seg), _ptr(lse2_seg), _ptr(out),
                                            _ptr(lse), _stream(stream)),
            "dcpmla_merge_segments_dense")
+
+
+def device_info(device: int = 0) -> dict:
+    """CU count, clocks and memory interface of a HIP device (host query)."""
+    info = _lib.DeviceInfo()
+    _check(_lib.lib.dcpmla_get_device_info(int(device), ctypes.byref(info)), "dcpmla_get_device_info")
+    return {"compute_units": info.compute_units, "clock_khz": info.clock_khz,
+            "memory_clock_khz": info.memory_clock_khz, "memory_bus_bits": info.memory_bus_bits,
+            "lds_bytes_per_block": info.lds_bytes_per_block, "arch": info.arch.decode()}

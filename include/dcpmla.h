@@ -226,6 +226,23 @@ int dcpmla_merge_segments_dense(int64_t rows, int32_t nseg, const float *o_seg,
 /* Static description of a status code. */
 const char *dcpmla_strerror(int status);
 
+/*
+ * Device description used to state roofline peaks next to measurements (the
+ * measurement of the segmented kernel is judged against the binding HBM or
+ * MFMA roofline; the peaks are the chip's, not the pages').  Fills *out for
+ * HIP device `device`; DCPMLA_E_INVALID for a null pointer, DCPMLA_E_HIP if
+ * the runtime cannot describe the device.  Host call, no kernel launch.
+ */
+typedef struct dcpmla_device_info {
+  int32_t compute_units;      /* multiProcessorCount */
+  int32_t clock_khz;          /* peak shader clock */
+  int32_t memory_clock_khz;   /* memory clock as reported by the runtime */
+  int32_t memory_bus_bits;    /* memory interface width */
+  int64_t lds_bytes_per_block;
+  char arch[64];              /* gcnArchName, NUL-terminated */
+} dcpmla_device_info;
+int dcpmla_get_device_info(int32_t device, dcpmla_device_info *out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -76,6 +76,7 @@ struct AttnArgs {
   int32_t *err;
   int64_t num_pages;
   int B, qlen, H, M, n_mt, page_shift, max_local_pages;
+  int part_ints;             // 4B+2 partition ints + B*qlen row lengths (staged in LDS)
   float score_scale2;        // softmax_scale * kv_scale * log2(e)
   float out_scale;           // kv_scale
 };
@@ -288,10 +289,12 @@ __device__ inline void issue_stage(uint32_t tile_lds, const uint8_t *row, int wa
 
 __device__ inline void wait_direct_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <int E>
+// LDS: two stage tiles, then (PartLds) the work partition and the row
+// lengths, so locating a piece costs no global round trips.
+template <int E, bool PartLds>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attention_kernel(AttnArgs a) {
-  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];   // two stage tiles
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int lane = tid & 63;
@@ -301,12 +304,26 @@ attention_kernel(AttnArgs a) {
   const int64_t U = a.work[0];
   if (U == 0) return;
   const int64_t G = effective_groups(gridDim.x, U);
-  const int64_t w = blockIdx.x;
-  if (w >= G) return;
+  if ((int64_t)blockIdx.x >= G) return;
+  const int64_t w = xcd_group(blockIdx.x, G);
   const int64_t lo = group_lo(w, U, G);
   const int64_t hi = group_lo(w + 1, U, G);
-  const int32_t *unit_base = a.work + work_unit_base_off();
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_char *)lds);
+  int32_t *part = (int32_t *)(lds + 2 * Tile<E>::kBytes);
+  const int nwork = 4 * a.B + 2;
+  if constexpr (PartLds) {
+    for (int i = tid; i < nwork; i += kThreads) part[i] = a.work[i];
+    for (int i = tid; i < a.B * a.qlen; i += kThreads) part[nwork + i] = a.row_len[i];
+    __syncthreads();
+  }
+  auto work_at = [&](int i) -> int32_t {
+    if constexpr (PartLds) return part[i];
+    else return a.work[i];
+  };
+  auto row_len_at = [&](int i) -> int32_t {
+    if constexpr (PartLds) return part[nwork + i];
+    else return a.row_len[i];
+  };
   int32_t bad = 0;
 
   int slot = 0;
@@ -315,17 +332,17 @@ attention_kernel(AttnArgs a) {
     int blo = 0, bhi = a.B;   // unit_base[blo] <= u < unit_base[bhi]
     while (bhi - blo > 1) {
       const int mid = (blo + bhi) >> 1;
-      if ((int64_t)unit_base[mid] <= u) blo = mid; else bhi = mid;
+      if ((int64_t)work_at(work_unit_base_off() + mid) <= u) blo = mid; else bhi = mid;
     }
     const int b = blo;
-    const int stages = a.work[work_stages_off(a.B) + b];
-    const int64_t rem = u - unit_base[b];
+    const int stages = work_at(work_stages_off(a.B) + b);
+    const int64_t rem = u - work_at(work_unit_base_off() + b);
     const int mt = (int)(rem / stages);
     const int st0 = (int)(rem - (int64_t)mt * stages);
     const int st1 = (int)min((int64_t)stages, st0 + (hi - u));
     const bool complete = st0 == 0 && st1 == stages;
-    const int lmax = a.work[work_lmax_off(a.B) + b];
-    const int32_t *pt = a.page_table + (int64_t)a.work[work_lrow_off(a.B) + b] * a.max_local_pages;
+    const int lmax = work_at(work_lmax_off(a.B) + b);
+    const int32_t *pt = a.page_table + (int64_t)work_at(work_lrow_off(a.B) + b) * a.max_local_pages;
 
     // this lane's head-row and its verify-row window
     const int m = mt * kTileRows + wave * kWaveRows + l32;
@@ -333,13 +350,7 @@ attention_kernel(AttnArgs a) {
     const int vrow = mvalid ? m / a.H : 0;
     // rows past M (zero queries) see every token: their results are never
     // stored, and they keep the wave on the unmasked path
-    const int rlen = mvalid ? a.row_len[b * a.qlen + vrow] : 0x3FFFFFFF;
-
-    // first stage: page id, then its direct loads; later stages are fetched
-    // one stage ahead
-    int32_t page = fetch_page<E>(a, pt, st0, lmax, lane);
-    issue_stage<E>(lds_base, stage_row<E>(a, page, st0, lmax, lane, &bad), wave);
-    if (st0 + 1 < st1) page = fetch_page<E>(a, pt, st0 + 1, lmax, lane);
+    const int rlen = mvalid ? row_len_at(b * a.qlen + vrow) : 0x3FFFFFFF;
 
     bf16x8 qf[kKBlocks];
     {
@@ -353,6 +364,12 @@ attention_kernel(AttnArgs a) {
         qf[j] = __builtin_bit_cast(bf16x8, v);
       }
     }
+
+    // first stage: page id, then its direct loads; later stages are fetched
+    // one stage ahead
+    int32_t page = fetch_page<E>(a, pt, st0, lmax, lane);
+    issue_stage<E>(lds_base, stage_row<E>(a, page, st0, lmax, lane, &bad), wave);
+    if (st0 + 1 < st1) page = fetch_page<E>(a, pt, st0 + 1, lmax, lane);
 
     floatx16 oacc[kDv / 32];
 #pragma unroll
@@ -521,7 +538,8 @@ attention_kernel(AttnArgs a) {
         }
         if (h == 0) a.lse[(int64_t)b * a.M + m] = has ? lse2 * kLn2 : kNegInf;
       }
-    } else {
+    } else if (mvalid) {
+      // rows past M are never merged: no partial for them
       const int64_t prow = (w * kSlots + slot) * kTileRows + wave * kWaveRows + l32;
       float *orow = a.ws_o + prow * kDv;
 #pragma unroll
@@ -541,18 +559,32 @@ attention_kernel(AttnArgs a) {
   if (bad) atomicOr(a.err, DCPMLA_ERR_PAGE_RANGE);
 }
 
-template <int E>
-hipError_t launch_tile(const AttnArgs &a, int groups, hipStream_t stream) {
-  const size_t shmem = 2 * Tile<E>::kBytes;
+constexpr size_t kLdsLimit = 160 * 1024;   // gfx950 LDS per workgroup
+
+template <int E, bool PartLds>
+hipError_t launch_variant(const AttnArgs &a, int groups, size_t shmem, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void *)attention_kernel<E>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    const size_t cap = PartLds ? kLdsLimit : 2 * Tile<E>::kBytes;
+    const hipError_t e = hipFuncSetAttribute((const void *)attention_kernel<E, PartLds>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)cap);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(attention_kernel<E>, dim3(groups), dim3(kThreads), shmem, stream, a);
+  hipLaunchKernelGGL((attention_kernel<E, PartLds>), dim3(groups), dim3(kThreads), shmem, stream, a);
   return hipGetLastError();
+}
+
+template <int E>
+hipError_t launch_tile(AttnArgs a, int groups, hipStream_t stream) {
+  const size_t tiles = 2 * Tile<E>::kBytes;
+  const size_t part = (size_t)(4 * (int64_t)a.B + 2 + (int64_t)a.B * a.qlen) * 4;
+  if (tiles + part <= kLdsLimit) {
+    a.part_ints = (int)(part / 4);
+    return launch_variant<E, true>(a, groups, tiles + part, stream);
+  }
+  a.part_ints = 0;
+  return launch_variant<E, false>(a, groups, tiles, stream);
 }
 
 }  // namespace

@@ -66,4 +66,16 @@ __host__ __device__ inline int64_t effective_groups(int64_t launched, int64_t U)
 // start unit of persistent workgroup w out of G over U units
 __host__ __device__ inline int64_t group_lo(int64_t w, int64_t U, int64_t G) { return (w * U) / G; }
 
+// The dispatcher places workgroup i on XCD i % 8.  Logical group numbers
+// (which fix the unit range) are handed out so that each XCD runs one
+// contiguous range of them: neighbouring ranges share a sequence's query
+// rows and KV pages, which then stay in that XCD's L2.  A bijection on
+// [0, G) for workgroups i < G.
+constexpr int64_t kXcds = 8;
+__host__ __device__ inline int64_t xcd_group(int64_t i, int64_t G) {
+  const int64_t x = i % kXcds, k = i / kXcds;
+  const int64_t q = G / kXcds, r = G % kXcds;
+  return x * q + (x < r ? x : r) + k;
+}
+
 }  // namespace dcpmla

@@ -54,6 +54,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef int int2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -69,8 +70,9 @@ struct AttnArgs {
   const int32_t *row_len;    // [B*qlen]
   const int32_t *page_table; // [B*qlen, max_local_pages]
   const int32_t *work;
-  float *ws_o;               // [G][2][128][512]
+  void *ws_o;                // [G][2][128][512] fp16 (FP8 cache) or float (BF16 cache)
   float *ws_lse2;            // [G][2][128]
+  float *ws_scale;           // scale of the fp16 partials
   uint16_t *out;             // [B, qlen, H, 512] bf16 bits
   float *lse;                // [B, qlen, H]
   int32_t *err;
@@ -301,6 +303,7 @@ attention_kernel(AttnArgs a) {
   const int l32 = lane & 31;
   const int h = lane >> 5;
   const int kslot = tok_slot(l32);   // LDS slot of the stage token in this lane's score row
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.ws_scale = a.out_scale;
   const int64_t U = a.work[0];
   if (U == 0) return;
   const int64_t G = effective_groups(gridDim.x, U);
@@ -541,14 +544,34 @@ attention_kernel(AttnArgs a) {
     } else if (mvalid) {
       // rows past M are never merged: no partial for them
       const int64_t prow = (w * kSlots + slot) * kTileRows + wave * kWaveRows + l32;
-      float *orow = a.ws_o + prow * kDv;
+      if constexpr (E == 1) {
+        // fp16 partial of o / kv_scale: a weighted mean of E4M3 values, so
+        // |value| <= 448 and fp16 keeps 11 significant bits of it
+        const float invr = has ? 1.0f / ltot : 0.f;
+        uint2 *orow = (uint2 *)((_Float16 *)a.ws_o + prow * kDv);
 #pragma unroll
-      for (int d = 0; d < kDv / 32; ++d) {
+        for (int d = 0; d < kDv / 32; ++d) {
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int dim = 32 * d + 8 * g4 + 4 * h;
-          *(float4 *)(orow + dim) = make_float4(oacc[d][4 * g4 + 0] * inv, oacc[d][4 * g4 + 1] * inv,
-                                                oacc[d][4 * g4 + 2] * inv, oacc[d][4 * g4 + 3] * inv);
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int dim = 32 * d + 8 * g4 + 4 * h;
+            half2v lo, hi;
+            lo[0] = (_Float16)(oacc[d][4 * g4 + 0] * invr);
+            lo[1] = (_Float16)(oacc[d][4 * g4 + 1] * invr);
+            hi[0] = (_Float16)(oacc[d][4 * g4 + 2] * invr);
+            hi[1] = (_Float16)(oacc[d][4 * g4 + 3] * invr);
+            orow[dim / 4] = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+          }
+        }
+      } else {
+        float *orow = (float *)a.ws_o + prow * kDv;
+#pragma unroll
+        for (int d = 0; d < kDv / 32; ++d) {
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int dim = 32 * d + 8 * g4 + 4 * h;
+            *(float4 *)(orow + dim) = make_float4(oacc[d][4 * g4 + 0] * inv, oacc[d][4 * g4 + 1] * inv,
+                                                  oacc[d][4 * g4 + 2] * inv, oacc[d][4 * g4 + 3] * inv);
+          }
         }
       }
       if (h == 0) a.ws_lse2[prow] = lse2;
@@ -600,8 +623,9 @@ hipError_t launch_partial_attention(const dcpmla_geom &g, int groups, const void
   a.row_len = m.row_local_len;
   a.page_table = m.page_table;
   a.work = m.work;
-  a.ws_o = (float *)workspace;
+  a.ws_o = workspace;
   a.ws_lse2 = (float *)workspace + ws_o_floats(groups);
+  a.ws_scale = (float *)workspace + ws_scale_off(groups);
   a.out = (uint16_t *)out_rank;
   a.lse = lse_rank;
   a.err = m.err;

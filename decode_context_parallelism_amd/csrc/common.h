@@ -44,14 +44,18 @@ __host__ __device__ inline int n_mtiles(int qlen, int heads) {
   return (m + kTileRows - 1) / kTileRows;
 }
 
-// Workspace: o partials [groups][kSlots][kTileRows][kDv] float, then
-// lse2 partials [groups][kSlots][kTileRows] float.
+// Workspace: o partials [groups][kSlots][kTileRows][kDv], then lse2 partials
+// [groups][kSlots][kTileRows] float, then the partials' scale (one float,
+// padded to 16 bytes).  With an FP8 cache the o partials are fp16 values of
+// o / kv_scale (bounded by the E4M3 maximum 448) and the scale is kv_scale;
+// with a BF16 cache they are float values of o and the scale is unused.
 __host__ __device__ inline int64_t ws_o_floats(int groups) {
   return (int64_t)groups * kSlots * kTileRows * kDv;
 }
-__host__ __device__ inline int64_t ws_bytes(int groups) {
-  return (ws_o_floats(groups) + (int64_t)groups * kSlots * kTileRows) * 4;
+__host__ __device__ inline int64_t ws_scale_off(int groups) {
+  return ws_o_floats(groups) + (int64_t)groups * kSlots * kTileRows;
 }
+__host__ __device__ inline int64_t ws_bytes(int groups) { return (ws_scale_off(groups) + 4) * 4; }
 
 // Workgroups that actually take work: every one gets at least about
 // kMinUnitsPerGroup stages, because each split costs a 256 KiB fp32 partial

@@ -117,15 +117,29 @@ __global__ void __launch_bounds__(256) merge_segments_dense_kernel(
 // Persistent layout: finish every (sequence, head-row tile) whose stages were
 // split over several workgroups, and give sequences with no rank-local token
 // their empty result.  Tiles finished inside one workgroup are left alone.
-// One workgroup per (sequence, tile, group of kMergeRows rows); each wave
-// merges kMergeRows / 4 rows, one row at a time, with the partial loads of a
-// row issued four at a time.
-constexpr int kMergeRows = 16;
+// One workgroup per (sequence, tile, group of kMergeRows rows), one row per
+// wave; the partials of a row are requested kMergeBatch at a time so a row
+// costs few dependent memory round trips.
+constexpr int kMergeRows = 4;
+constexpr int kMergeBatch = 8;
 
+// Partial loads: 8 value dims of one partial row for this lane.
+__device__ inline void load_partial8(const float *row, int lane, float v[8]) {
+  const float4 a = ((const float4 *)row)[2 * lane], b = ((const float4 *)row)[2 * lane + 1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ inline void load_partial8(const _Float16 *row, int lane, float v[8]) {
+  typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+  const half8v h = __builtin_bit_cast(half8v, ((const uint4 *)row)[lane]);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = (float)h[k];
+}
+
+template <typename PT>
 __global__ void __launch_bounds__(256) merge_segments_kernel(
     int B, int qlen, int heads, int n_mt, int G, const int32_t *__restrict__ work,
-    const float4 *__restrict__ ws_o, const float *__restrict__ ws_lse2, uint4 *__restrict__ out,
-    float *__restrict__ lse) {
+    const PT *__restrict__ ws_o, const float *__restrict__ ws_lse2, const float *__restrict__ ws_scale,
+    uint4 *__restrict__ out, float *__restrict__ lse) {
   __shared__ int s_src[1024];   // partial index (group * kSlots + slot) of each piece part
   __shared__ int s_n;
   constexpr int kChunks = kTileRows / kMergeRows;
@@ -143,8 +157,8 @@ __global__ void __launch_bounds__(256) merge_segments_kernel(
   if (nrows <= 0) return;
   if (stages == 0) {
     // no rank-local token for the whole sequence: O = 0, LSE = -inf
-    for (int r = wave; r < nrows; r += kWaves) {
-      const int64_t orow = (int64_t)b * M + row0 + r;
+    if (wave < nrows) {
+      const int64_t orow = (int64_t)b * M + row0 + wave;
       out[orow * 64 + lane] = make_uint4(0, 0, 0, 0);
       if (lane == 0) lse[orow] = kNegInf;
     }
@@ -173,59 +187,45 @@ __global__ void __launch_bounds__(256) merge_segments_kernel(
     s_n = n;
   }
   __syncthreads();
+  if (wave >= nrows) return;
   const int n = s_n;
-  const int tr0 = chunk * kMergeRows;   // row index inside the tile (partial rows)
-  for (int r = wave; r < nrows; r += kWaves) {
-    const int pr0 = tr0 + r;
-    float mx = kNegInf;
-    for (int k = lane; k < n; k += 64) mx = fmaxf(mx, ws_lse2[(int64_t)s_src[k] * kTileRows + pr0]);
+  const int pr0 = chunk * kMergeRows + wave;   // row index inside the tile (partial rows)
+  float mx = kNegInf;
+  for (int k = lane; k < n; k += 64) mx = fmaxf(mx, ws_lse2[(int64_t)s_src[k] * kTileRows + pr0]);
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    float L = kNegInf;
-    if (mx > kNegInf) {
-      float z = 0.f;
-      int k = 0;
-      for (; k + 4 <= n; k += 4) {
-        float wgt[4];
-        float4 va[4], vb[4];
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float L = kNegInf;
+  if (mx > kNegInf) {
+    float z = 0.f;
+    for (int k = 0; k < n; k += kMergeBatch) {
+      float wgt[kMergeBatch];
+      float v[kMergeBatch][8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t pr = (int64_t)s_src[k + q] * kTileRows + pr0;
-          const float l = ws_lse2[pr];
-          wgt[q] = l > kNegInf ? fast_exp2(l - mx) : 0.f;
-          const float4 *src = ws_o + pr * (kDv / 4) + 2 * lane;
-          va[q] = src[0];
-          vb[q] = src[1];
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          z += wgt[q];
-          acc[0] += wgt[q] * va[q].x; acc[1] += wgt[q] * va[q].y;
-          acc[2] += wgt[q] * va[q].z; acc[3] += wgt[q] * va[q].w;
-          acc[4] += wgt[q] * vb[q].x; acc[5] += wgt[q] * vb[q].y;
-          acc[6] += wgt[q] * vb[q].z; acc[7] += wgt[q] * vb[q].w;
-        }
-      }
-      for (; k < n; ++k) {
-        const int64_t pr = (int64_t)s_src[k] * kTileRows + pr0;
+      for (int q = 0; q < kMergeBatch; ++q) {
+        // entries past n repeat the last partial with weight 0 (a valid address)
+        const int kk = k + q < n ? k + q : n - 1;
+        const int64_t pr = (int64_t)s_src[kk] * kTileRows + pr0;
         const float l = ws_lse2[pr];
-        const float wq = l > kNegInf ? fast_exp2(l - mx) : 0.f;
-        const float4 *src = ws_o + pr * (kDv / 4) + 2 * lane;
-        const float4 a = src[0], c = src[1];
-        z += wq;
-        acc[0] += wq * a.x; acc[1] += wq * a.y; acc[2] += wq * a.z; acc[3] += wq * a.w;
-        acc[4] += wq * c.x; acc[5] += wq * c.y; acc[6] += wq * c.z; acc[7] += wq * c.w;
+        wgt[q] = (k + q < n && l > kNegInf) ? fast_exp2(l - mx) : 0.f;
+        load_partial8(ws_o + pr * kDv, lane, v[q]);
       }
-      const float inv = 1.f / z;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] *= inv;
-      L = (mx + fast_log2(z)) * kLn2;
+      for (int q = 0; q < kMergeBatch; ++q) {
+        z += wgt[q];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += wgt[q] * v[q][e];
+      }
     }
-    const int64_t orow = (int64_t)b * M + row0 + r;
-    out[orow * 64 + lane] = pack_bf16x8(acc);
-    if (lane == 0) lse[orow] = L;
+    // fp16 partials carry o / kv_scale
+    const float inv = (sizeof(PT) == 2 ? *ws_scale : 1.f) / z;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] *= inv;
+    L = (mx + fast_log2(z)) * kLn2;
   }
+  const int64_t orow = (int64_t)b * M + row0 + wave;
+  out[orow * 64 + lane] = pack_bf16x8(acc);
+  if (lane == 0) lse[orow] = L;
 }
 
 hipError_t launch_merge_ranks(int world, int64_t rows, const void *out_ranks,
@@ -253,9 +253,16 @@ hipError_t launch_merge_segments(const dcpmla_geom &g, int groups, const dcpmla_
   const int n_mt = n_mtiles(g.qlen, g.num_heads);
   const float *ws = (const float *)workspace;
   const int chunks = kTileRows / kMergeRows;
-  hipLaunchKernelGGL(merge_segments_kernel, dim3(g.batch * n_mt * chunks), dim3(256), 0, stream, g.batch,
-                     g.qlen, g.num_heads, n_mt, groups, m.work, (const float4 *)ws,
-                     ws + ws_o_floats(groups), (uint4 *)out_rank, lse_rank);
+  const dim3 grid(g.batch * n_mt * chunks);
+  if (g.kv_dtype == DCPMLA_KV_FP8_E4M3) {
+    hipLaunchKernelGGL(merge_segments_kernel<_Float16>, grid, dim3(256), 0, stream, g.batch, g.qlen,
+                       g.num_heads, n_mt, groups, m.work, (const _Float16 *)workspace,
+                       ws + ws_o_floats(groups), ws + ws_scale_off(groups), (uint4 *)out_rank, lse_rank);
+  } else {
+    hipLaunchKernelGGL(merge_segments_kernel<float>, grid, dim3(256), 0, stream, g.batch, g.qlen,
+                       g.num_heads, n_mt, groups, m.work, ws, ws + ws_o_floats(groups),
+                       ws + ws_scale_off(groups), (uint4 *)out_rank, lse_rank);
+  }
   return hipGetLastError();
 }
 

@@ -171,7 +171,9 @@ int dcpmla_build_metadata(const dcpmla_geom *geom, int32_t rank, const int32_t *
  * Segmented split-KV MLA attention for one rank (PR #51705, "Implementation"
  * item 3): each (sequence, head-row tile, KV range) piece produces either the
  * finished rank output or an unreduced partial with base-2 softmax
- * statistics in the workspace.  Scores are q . k * softmax_scale over all 576
+ * statistics in the workspace (partial outputs as fp16 values of o / kv_scale
+ * with an FP8 cache, whose magnitude the E4M3 maximum 448 bounds, and as float
+ * with a BF16 cache).  Scores are q . k * softmax_scale over all 576
  * dims; the cached elements are multiplied by kv_scale (1 for BF16 caches).
  * q [B, qlen, H, 576] bf16; kv_pool [num_blocks, block_size, 576] in
  * geom->kv_dtype; out_rank [B, qlen, H, 512] bf16 and lse_rank [B, qlen, H]

@@ -84,8 +84,9 @@ def test_sizes():
     # partition (4B + 2 ints), padded to 64 ints, then one zero latent row
     assert ops.work_ints(g) == 64 + 576 * 2 // 4
     ws = ops.workspace_bytes(g)
-    assert ws == 4 * 2 * 128 * (512 + 1) * 4
-    assert ops.workspace_bytes(_geom(groups=1)) * 4 == ws
+    # per group: 2 slots x 128 rows x (512 partial values + 1 lse2) floats; then a 16-byte scale slot
+    assert ws == 4 * 2 * 128 * (512 + 1) * 4 + 16
+    assert (ops.workspace_bytes(_geom(groups=1)) - 16) * 4 == ws - 16
 
 
 def test_strerror():

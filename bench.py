@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target length of the oracle's timed CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--row-boundary", choices=("causal", "block"), default="causal",
+                    help="causal verify rows (default) or a bidirectional draft block "
+                         "(every row sees the whole cache)")
     ap.add_argument("--no-rotate", action="store_true",
                     help="reuse one input set every step (cache-warm KV)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -165,7 +168,8 @@ def main():
     g = ops.Geometry(dcp_world=w.world, interleave=w.interleave, block_size=w.block_size,
                      qlen=w.qlen, num_heads=w.heads, batch=w.batch,
                      max_blocks_per_seq=w.block_table.shape[1], max_local_pages=w.max_local_pages,
-                     kv_dtype=w.kv_format, num_blocks=w.num_blocks, groups=args.groups)
+                     kv_dtype=w.kv_format, num_blocks=w.num_blocks, groups=args.groups,
+                     row_boundary=args.row_boundary)
     dev = "cuda"
     q0 = torch.from_numpy(w.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     if w.kv_format == "fp8_e4m3":
@@ -295,7 +299,8 @@ def main():
         "config": {"workload": w.name, "dcp_world": W, "interleave": w.interleave,
                    "batch": w.batch, "qlen": w.qlen, "heads": w.heads,
                    "block_size": w.block_size, "kv_cache": w.kv_format,
-                   "kv_tokens_per_step": kv_tokens, "ranks_per_step": W, "input_sets": n_sets},
+                   "kv_tokens_per_step": kv_tokens, "ranks_per_step": W, "input_sets": n_sets,
+                   "row_boundary": args.row_boundary},
         "verify_rows_per_s": w.batch * w.qlen / (ms_per_step * 1e-3),
         "per_rank": {
             "attention_us_mean": float(per_rank_ms.mean() * 1e3),

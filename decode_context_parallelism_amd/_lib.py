@@ -12,6 +12,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdcpmla.s
 
 KV_BF16 = 0
 KV_FP8_E4M3 = 1
+BOUNDARY_CAUSAL = 0
+BOUNDARY_BLOCK = 1
 
 OK = 0
 E_INVALID = -1
@@ -41,6 +43,7 @@ class Geom(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("groups", ctypes.c_int32),
         ("num_blocks", ctypes.c_int64),
+        ("row_boundary", ctypes.c_int32),
     ]
 
 

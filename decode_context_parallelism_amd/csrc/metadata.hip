@@ -15,7 +15,7 @@ namespace dcpmla {
 
 __global__ void __launch_bounds__(256) meta_rows_kernel(
     int W, int S, int block_size, int qlen, int max_blocks, int max_local_pages,
-    int64_t num_blocks, int rank, const int32_t *__restrict__ ctx_lens,
+    int64_t num_blocks, int rank, int block_rows, const int32_t *__restrict__ ctx_lens,
     const int32_t *__restrict__ block_table, int32_t *__restrict__ row_len,
     int32_t *__restrict__ page_table, int32_t *__restrict__ last_len, int32_t *__restrict__ err) {
   const int row = blockIdx.x;
@@ -28,7 +28,9 @@ __global__ void __launch_bounds__(256) meta_rows_kernel(
   if (threadIdx.x == 0) {
     const int64_t ctx = ctx_lens[b];
     int e = 0;
-    int64_t g = ctx - qlen + 1 + i;        // global causal boundary of verify row i
+    // global boundary of row i: causal verify, or the whole cache for a
+    // bidirectional draft block
+    int64_t g = block_rows ? ctx : ctx - qlen + 1 + i;
     if (ctx < qlen) e |= DCPMLA_ERR_CTX_LT_QLEN;
     if (g < 0) g = 0;
     const int64_t span = (int64_t)W * S;
@@ -124,7 +126,8 @@ hipError_t launch_build_metadata(const dcpmla_geom &g, int rank, const int32_t *
   const int rows = g.batch * g.qlen;
   hipLaunchKernelGGL(meta_rows_kernel, dim3(rows), dim3(256), 0, stream, g.dcp_world,
                      g.interleave, g.block_size, g.qlen, g.max_blocks_per_seq, g.max_local_pages,
-                     g.num_blocks, rank, ctx_lens, block_table, m.row_local_len, m.page_table,
+                     g.num_blocks, rank, g.row_boundary == DCPMLA_BOUNDARY_BLOCK ? 1 : 0, ctx_lens,
+                     block_table, m.row_local_len, m.page_table,
                      m.last_page_len, m.err);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -65,11 +65,13 @@ class Geometry:
     kv_dtype: str              # "bf16" | "fp8_e4m3"
     num_blocks: int
     groups: int = 0
+    row_boundary: str = "causal"   # "causal" verify rows | "block" (bidirectional draft block)
 
     def c(self) -> _lib.Geom:
         return _lib.Geom(self.dcp_world, self.interleave, self.block_size, self.qlen,
                          self.num_heads, self.batch, self.max_blocks_per_seq,
-                         self.max_local_pages, self.kv_code, self.groups, self.num_blocks)
+                         self.max_local_pages, self.kv_code, self.groups, self.num_blocks,
+                         {"causal": _lib.BOUNDARY_CAUSAL, "block": _lib.BOUNDARY_BLOCK}[self.row_boundary])
 
     @property
     def kv_code(self) -> int:

@@ -64,6 +64,19 @@ enum {
   DCPMLA_KV_FP8_E4M3 = 1  /* OCP FP8 E4M3 (max 448) with one per-tensor float scale */
 };
 
+/*
+ * Which global positions a row sees.  CAUSAL: verify row i of a sequence with
+ * ctx cached tokens sees [0, ctx - qlen + 1 + i) ("[ROCm][MLA][DCP] Support
+ * causal multi-token verification", "Implementation" item 1).  BLOCK: a
+ * bidirectional draft block -- every row sees the whole cache [0, ctx)
+ * ("Context Parallel Guide (PCP & DCP)", "DSpark (Kimi-K3)": the draft block
+ * attends the whole block, so no mask is placed on global positions).
+ */
+enum {
+  DCPMLA_BOUNDARY_CAUSAL = 0,
+  DCPMLA_BOUNDARY_BLOCK = 1
+};
+
 /* Bits of the device error word. */
 enum {
   DCPMLA_ERR_CTX_LT_QLEN = 1,    /* ctx < qlen: rows whose boundary would be < 1 get no tokens */
@@ -93,6 +106,7 @@ typedef struct dcpmla_geom {
   int32_t groups;             /* persistent workgroups of the attention kernel; 0 = one per
                                  compute unit of the current device */
   int64_t num_blocks;         /* physical blocks in each rank's pool */
+  int32_t row_boundary;       /* DCPMLA_BOUNDARY_CAUSAL (default) or DCPMLA_BOUNDARY_BLOCK */
 } dcpmla_geom;
 
 /*

@@ -42,6 +42,16 @@ def verify_row_boundary(ctx: int, qlen: int, i: int) -> int:
     return ctx - qlen + 1 + i
 
 
+def block_row_boundary(ctx: int, qlen: int, i: int) -> int:
+    """Row boundary of a bidirectional draft block: every row sees the whole cache.
+
+    "Context Parallel Guide (PCP & DCP)", "DSpark (Kimi-K3)": the draft block
+    is not causal -- each draft position attends the whole block -- so no row
+    gets a boundary of its own.
+    """
+    return ctx
+
+
 def rank_local_positions(g: int, world: int, interleave: int, rank: int) -> np.ndarray:
     """Global positions < g owned by ``rank``, ascending (the rank-local order)."""
     p = np.arange(max(g, 0), dtype=np.int64)
@@ -69,7 +79,7 @@ def physical_rows(local_index: np.ndarray, block_table_row: np.ndarray, block_si
 
 
 def row_metadata(ctx_lens, block_table, *, world, interleave, block_size, qlen, rank,
-                 max_local_pages):
+                 max_local_pages, boundary=verify_row_boundary):
     """Expected verify view for one rank.
 
     Returns ``(row_local_len[B*q], page_table[B*q, max_local_pages],
@@ -88,7 +98,7 @@ def row_metadata(ctx_lens, block_table, *, world, interleave, block_size, qlen, 
     for b in range(B):
         for i in range(qlen):
             row = b * qlen + i
-            g = verify_row_boundary(int(ctx_lens[b]), qlen, i)
+            g = boundary(int(ctx_lens[b]), qlen, i)
             pos = rank_local_positions(g, world, interleave, rank)
             n = pos.shape[0]
             lens[row] = n

@@ -14,6 +14,7 @@ import pytest
 import torch
 
 from oracle import attention as A
+from oracle import layout
 from synth import make_config, make_workload
 from gpu_util import (LSE_TOL, bf16_to_f64, oracle_latents, oracle_q, output_bound,
                       run_group, tolerance)
@@ -21,9 +22,10 @@ from gpu_util import (LSE_TOL, bf16_to_f64, oracle_latents, oracle_q, output_bou
 pytestmark = pytest.mark.gpu
 
 
-def _compare_rank(w, grp, r, rows):
+def _compare_rank(w, grp, r, rows, boundary=layout.verify_row_boundary):
     o, l = A.verify_attention(oracle_q(w), oracle_latents(w), w.ctx_lens, w.softmax_scale,
-                              world=w.world, interleave=w.interleave, rank=r, rows=rows)
+                              world=w.world, interleave=w.interleave, rank=r, rows=rows,
+                              boundary=boundary)
     go = bf16_to_f64(grp.out_ranks[r])
     gl = grp.lse_ranks[r].cpu().numpy().astype(np.float64)
     for b, i in rows:
@@ -41,13 +43,13 @@ def _compare_rank(w, grp, r, rows):
             assert err_l <= LSE_TOL, (r, b, i, err_l)
 
 
-def _compare_merged(w, grp, rows):
+def _compare_merged(w, grp, rows, boundary=layout.verify_row_boundary):
     q, lat = oracle_q(w), oracle_latents(w)
-    o, l = A.verify_attention(q, lat, w.ctx_lens, w.softmax_scale, rows=rows)
+    o, l = A.verify_attention(q, lat, w.ctx_lens, w.softmax_scale, rows=rows, boundary=boundary)
     ro, rl = [], []
     for r in range(w.world):
         a, c = A.verify_attention(q, lat, w.ctx_lens, w.softmax_scale, world=w.world,
-                                  interleave=w.interleave, rank=r, rows=rows)
+                                  interleave=w.interleave, rank=r, rows=rows, boundary=boundary)
         ro.append(a)
         rl.append(c)
     ro, rl = np.stack(ro), np.stack(rl)
@@ -158,3 +160,19 @@ def test_negative_control_boundary():
         mo, _ = A.merge_ranks(np.stack(outs), np.stack(lses))
         diff = max(np.abs(go[b, i] - mo[b, i]).max() for b, i in rows)
         assert diff > tolerance(w), diff
+
+
+# ------------------------------------------------ bidirectional draft block ----
+
+@pytest.mark.parametrize("k,groups", [(1, 0), (2, 0), (2, 7)])
+def test_block_rows_full(k, groups):
+    # every row of a sequence sees the whole cache ("Context Parallel Guide",
+    # DSpark): same kernels, degenerate row boundary
+    w = make_config(k)
+    print(f"config {k} groups {groups} block rows", flush=True)
+    grp, _ = run_group(w, groups=groups, row_boundary="block")
+    assert grp.errors() == 0
+    rows = [(b, i) for b in range(w.batch) for i in range(w.qlen)]
+    for r in range(w.world):
+        _compare_rank(w, grp, r, rows, boundary=layout.block_row_boundary)
+    _compare_merged(w, grp, rows, boundary=layout.block_row_boundary)

@@ -124,3 +124,21 @@ def test_write_kv_slots_and_pool(k):
         src = d["latents"][torch.from_numpy(owned).cuda().long()]
         assert torch.equal(got.view(torch.uint8) if got.dtype == torch.uint8 else got.view(torch.int16),
                            src.view(torch.uint8) if src.dtype == torch.uint8 else src.view(torch.int16))
+
+
+@pytest.mark.parametrize("k", [1, 2, 4])
+def test_metadata_block_rows(k):
+    # bidirectional draft block: every row gets the whole cache ("Context
+    # Parallel Guide", DSpark), bit-exact against the brute-force oracle
+    w = make_config(k, with_kv=False)
+    print(f"config {k}: {w.name} block rows", flush=True)
+    for r in range(w.world):
+        meta = _gpu_meta(w, r, row_boundary="block")
+        lens, table, last = layout.row_metadata(
+            w.ctx_lens, w.block_table, world=w.world, interleave=w.interleave,
+            block_size=w.block_size, qlen=w.qlen, rank=r, max_local_pages=w.max_local_pages,
+            boundary=layout.block_row_boundary)
+        assert np.array_equal(meta.row_local_len.cpu().numpy(), lens)
+        assert np.array_equal(meta.page_table.cpu().numpy(), table)
+        assert np.array_equal(meta.last_page_len.cpu().numpy(), last)
+        assert int(meta.err.item()) == 0

@@ -73,6 +73,13 @@ def test_validate_rejects_bad_dtype():
     assert _lib.lib.dcpmla_validate(ctypes.byref(g)) == _lib.E_INVALID
 
 
+def test_validate_row_boundary():
+    assert ops.validate(_geom(row_boundary="block")) == _lib.OK
+    g = _geom().c()
+    g.row_boundary = 2
+    assert _lib.lib.dcpmla_validate(ctypes.byref(g)) == _lib.E_INVALID
+
+
 def test_subpage_size_matches_oracle():
     for bs in range(1, 1100):
         assert ops.subpage_size(bs) == layout.subpage_size(bs)

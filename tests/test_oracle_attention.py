@@ -266,3 +266,31 @@ def test_pins_catch_mutants(monkeypatch):
 def _page_len(g, rank, W, S):
     span = W * S
     return g // span * S + min(max(g % span - rank * S, 0), S)
+
+
+def _sdpa_full_prefix(q, X, ctx, scale):
+    """Unmasked attention of every row over positions [0, ctx) (torch SDPA, float64)."""
+    qlen, H, _ = q.shape
+    qt = torch.from_numpy(q).permute(1, 0, 2).unsqueeze(0)
+    k = torch.from_numpy(X[:ctx]).unsqueeze(0).unsqueeze(0).expand(1, H, ctx, 576)
+    v = torch.from_numpy(X[:ctx, :512]).unsqueeze(0).unsqueeze(0).expand(1, H, ctx, 512)
+    out = torch.nn.functional.scaled_dot_product_attention(qt, k, v, scale=scale)
+    lse = torch.logsumexp((qt @ k.transpose(-1, -2)) * scale, dim=-1)
+    return out[0].permute(1, 0, 2).numpy(), lse[0].permute(1, 0).numpy()
+
+
+@pytest.mark.parametrize("seed,qlen,ctx,W,S", [(0, 3, 37, 2, 1), (1, 5, 64, 8, 16), (2, 2, 9, 4, 2)])
+def test_block_rows_match_unmasked_sdpa(seed, qlen, ctx, W, S):
+    # "Context Parallel Guide", DSpark: a bidirectional draft block has no mask
+    # on global positions -- plain attention over the whole cache for every row,
+    # and the rank split still merges back to it
+    q, X = _tiny(seed, qlen=qlen, H=3, ctx=ctx)
+    scale = 1 / math.sqrt(192)
+    lat = _latents_of(X)
+    out, lse = A.verify_attention(q, lat, [ctx], scale, boundary=layout.block_row_boundary)
+    ro, rl = _sdpa_full_prefix(q[0], X, ctx, scale)
+    assert np.abs(out[0] - ro).max() < 1e-12 and np.abs(lse[0] - rl).max() < 1e-12
+    parts = [A.verify_attention(q, lat, [ctx], scale, world=W, interleave=S, rank=r,
+                                boundary=layout.block_row_boundary) for r in range(W)]
+    mo, ml = A.merge_ranks(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    assert np.abs(mo - out).max() < 1e-12 and np.abs(ml - lse).max() < 1e-12

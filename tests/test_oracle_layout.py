@@ -219,3 +219,31 @@ def test_row_metadata_small_sweep(bs):
                         assert table[row, : len(pages)].tolist() == pages
                         assert np.all(table[row, len(pages):] == -1)
                         assert last[row] == lastc
+
+
+# -------------------------------------------------- bidirectional draft block ----
+
+@pytest.mark.parametrize("W,S", [(1, 1), (2, 1), (8, 1), (4, 4), (8, 16)])
+def test_block_rows_see_whole_cache(W, S):
+    # "Context Parallel Guide", DSpark: the draft block attends the whole block,
+    # so every row of a sequence gets the same window [0, ctx); with S = 1 the
+    # rank-local length is the printed ceil((L - rank) / dcp)
+    rng = np.random.default_rng(W * 100 + S)
+    B, q, bs = 3, 4, 16 * S
+    ctx = rng.integers(q, 6 * bs * W, size=B)
+    ncol = int(max(-(-c // (bs * W)) for c in ctx)) + 1
+    bt = rng.permutation(B * ncol).reshape(B, ncol).astype(np.int64)
+    for r in range(W):
+        lens, table, last = layout.row_metadata(ctx, bt, world=W, interleave=S, block_size=bs, qlen=q,
+                                                rank=r, max_local_pages=4 * ncol,
+                                                boundary=layout.block_row_boundary)
+        causal = layout.row_metadata(ctx, bt, world=W, interleave=S, block_size=bs, qlen=q, rank=r,
+                                     max_local_pages=4 * ncol)
+        for b in range(B):
+            rows = slice(b * q, (b + 1) * q)
+            # every row equals the last causal row, whose window is [0, ctx)
+            assert np.all(lens[rows] == causal[0][b * q + q - 1])
+            assert np.all(table[rows] == causal[1][b * q + q - 1])
+            assert np.all(last[rows] == causal[2][b * q + q - 1])
+            if S == 1:
+                assert np.all(lens[rows] == _page_local_rows_s1(int(ctx[b]), r, W))

@@ -61,6 +61,10 @@ def parse():
     ap.add_argument("--row-boundary", choices=("causal", "block"), default="causal",
                     help="causal verify rows (default) or a bidirectional draft block "
                          "(every row sees the whole cache)")
+    ap.add_argument("--merge", choices=("direct", "a2a", "pbm"), default="direct",
+                    help="cross-rank combine: direct LSE merge of all partials (default); a2a pack, "
+                         "exchange and local combine; or pbm (project each partial through a "
+                         "synthetic W_V [H, 512 -> 128] before the a2a)")
     ap.add_argument("--no-rotate", action="store_true",
                     help="reuse one input set every step (cache-warm KV)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -198,6 +202,36 @@ def main():
 
     stream = torch.cuda.current_stream()
 
+    # exchange buffers for the a2a / pbm combines: the all-to-all between
+    # ranks is one transposing copy here (block p of rank r -> block r of p)
+    T, H = w.batch * w.qlen, w.heads
+    Hl = H // W
+    if args.merge != "direct":
+        D = 128 if args.merge == "pbm" else 512
+        msg = ops.a2a_message_elems(D)
+        send = torch.empty(W, W, T, Hl, msg, dtype=torch.bfloat16, device=dev)
+        recv = torch.empty_like(send)
+        comb_o = torch.empty(W, T, Hl, D, dtype=torch.bfloat16, device=dev)
+        comb_l = torch.empty(W, T, Hl, dtype=torch.float32, device=dev)
+        if args.merge == "pbm":
+            gw = torch.Generator().manual_seed(7)
+            wvt = (torch.randn(H, D, 512, generator=gw) / 512 ** 0.5).to(torch.bfloat16).to(dev)
+            proj = torch.empty(W, T, H, D, dtype=torch.bfloat16, device=dev)
+
+    def combine():
+        if args.merge == "direct":
+            ops.merge_ranks(grp.out_ranks, grp.lse_ranks, grp.out, grp.lse, stream)
+            return
+        for r in range(W):
+            src = grp.out_ranks[r].view(T, H, 512)
+            if args.merge == "pbm":
+                ops.project_heads(src, wvt, proj[r], stream)
+                src = proj[r]
+            ops.a2a_pack(W, src, grp.lse_ranks[r].view(T, H), send[r], stream)
+        recv.copy_(send.transpose(0, 1))
+        for p in range(W):
+            ops.a2a_combine(recv[p], comb_o[p], comb_l[p], stream)
+
     def step(k, events=None):
         pools, q = sets[k % n_sets]
         for r in range(W):
@@ -213,7 +247,7 @@ def main():
                                stream)
             if events is not None:
                 events[r][2].record(stream)
-        ops.merge_ranks(grp.out_ranks, grp.lse_ranks, grp.out, grp.lse, stream)
+        combine()
 
     for k in range(args.warmup):
         step(k)
@@ -300,7 +334,7 @@ def main():
                    "batch": w.batch, "qlen": w.qlen, "heads": w.heads,
                    "block_size": w.block_size, "kv_cache": w.kv_format,
                    "kv_tokens_per_step": kv_tokens, "ranks_per_step": W, "input_sets": n_sets,
-                   "row_boundary": args.row_boundary},
+                   "row_boundary": args.row_boundary, "merge": args.merge},
         "verify_rows_per_s": w.batch * w.qlen / (ms_per_step * 1e-3),
         "per_rank": {
             "attention_us_mean": float(per_rank_ms.mean() * 1e3),

@@ -248,6 +248,50 @@ int dcpmla_merge_segments_dense(int64_t rows, int32_t nseg, const float *o_seg,
   return hip_status(launch_merge_segments_dense(rows, nseg, o_seg, lse2_seg, out, lse, stream));
 }
 
+int64_t dcpmla_a2a_message_elems(int32_t dim) {
+  if (dim < 8 || dim > kDv || dim % 8 != 0) return DCPMLA_E_INVALID;
+  return (int64_t)dim + 8;
+}
+
+int dcpmla_a2a_pack(int32_t dcp_world, int64_t tokens, int32_t heads, int32_t dim, const void *out_rank,
+                    const float *lse_rank, void *send, hipStream_t stream) {
+  if (dcp_world < 1 || tokens < 0 || heads < 1 || heads % dcp_world != 0) return DCPMLA_E_INVALID;
+  if (dim < 8 || dim > kDv || dim % 8 != 0) return DCPMLA_E_INVALID;
+  if (tokens > 0 && (!out_rank || !lse_rank || !send)) return DCPMLA_E_INVALID;
+  const int64_t rows = tokens * heads;
+  if (rows * (dim + 8) >= ((int64_t)1 << 40)) return DCPMLA_E_INVALID;
+  const Range ins[] = {{out_rank, rows * dim * 2}, {lse_rank, rows * 4}};
+  const Range outs[] = {{send, rows * (dim + 8) * 2}};
+  if (any_alias(outs, 1, ins, 2)) return DCPMLA_E_ALIAS;
+  return hip_status(launch_a2a_pack(dcp_world, tokens, heads, dim, out_rank, lse_rank, send, stream));
+}
+
+int dcpmla_a2a_combine(int32_t dcp_world, int64_t tokens, int32_t heads_local, int32_t dim,
+                       const void *recv, void *out, float *lse, hipStream_t stream) {
+  if (dcp_world < 1 || tokens < 0 || heads_local < 1) return DCPMLA_E_INVALID;
+  if (dim < 8 || dim > kDv || dim % 8 != 0) return DCPMLA_E_INVALID;
+  if (tokens > 0 && (!recv || !out || !lse)) return DCPMLA_E_INVALID;
+  const int64_t rows = tokens * heads_local;
+  if ((int64_t)dcp_world * rows * (dim + 8) >= ((int64_t)1 << 40)) return DCPMLA_E_INVALID;
+  const Range ins[] = {{recv, (int64_t)dcp_world * rows * (dim + 8) * 2}};
+  const Range outs[] = {{out, rows * dim * 2}, {lse, rows * 4}};
+  if (any_alias(outs, 2, ins, 1)) return DCPMLA_E_ALIAS;
+  return hip_status(launch_a2a_combine(dcp_world, tokens, heads_local, dim, recv, out, lse, stream));
+}
+
+int dcpmla_project_heads(int64_t tokens, int32_t heads, int32_t v_head_dim, const void *o,
+                         const void *w_v_t, void *out, hipStream_t stream) {
+  if (tokens < 0 || heads < 1 || v_head_dim < 32 || v_head_dim % 32 != 0 || v_head_dim > kDv)
+    return DCPMLA_E_INVALID;
+  if (tokens > 0 && (!o || !w_v_t || !out)) return DCPMLA_E_INVALID;
+  if (tokens * heads * kDv >= ((int64_t)1 << 40)) return DCPMLA_E_INVALID;
+  if (heads > 65535) return DCPMLA_E_INVALID;
+  const Range ins[] = {{o, tokens * heads * kDv * 2}, {w_v_t, (int64_t)heads * v_head_dim * kDv * 2}};
+  const Range outs[] = {{out, tokens * heads * v_head_dim * 2}};
+  if (any_alias(outs, 1, ins, 2)) return DCPMLA_E_ALIAS;
+  return hip_status(launch_project_heads(tokens, heads, v_head_dim, o, w_v_t, out, stream));
+}
+
 const char *dcpmla_strerror(int status) {
   switch (status) {
     case DCPMLA_OK: return "success";

@@ -32,4 +32,13 @@ hipError_t launch_merge_segments_dense(int64_t rows, int nseg, const float *o_se
                                        const float *lse2_seg, void *out, float *lse,
                                        hipStream_t stream);
 
+hipError_t launch_a2a_pack(int world, int64_t tokens, int heads, int dim, const void *out_rank,
+                           const float *lse_rank, void *send, hipStream_t stream);
+
+hipError_t launch_a2a_combine(int world, int64_t tokens, int heads_local, int dim, const void *recv,
+                              void *out, float *lse, hipStream_t stream);
+
+hipError_t launch_project_heads(int64_t tokens, int heads, int dv, const void *o, const void *wvt,
+                                void *out, hipStream_t stream);
+
 }  // namespace dcpmla

@@ -235,3 +235,41 @@ def device_info(device: int = 0) -> dict:
     return {"compute_units": info.compute_units, "clock_khz": info.clock_khz,
             "memory_clock_khz": info.memory_clock_khz, "memory_bus_bits": info.memory_bus_bits,
             "lds_bytes_per_block": info.lds_bytes_per_block, "arch": info.arch.decode()}
+
+
+def a2a_message_elems(dim: int) -> int:
+    n = int(lib.dcpmla_a2a_message_elems(int(dim)))
+    _check(min(n, 0), "dcpmla_a2a_message_elems")
+    return n
+
+
+def a2a_pack(world: int, out_rank, lse_rank, send, stream=None) -> None:
+    """``out_rank [T, H, D]`` bf16, ``lse_rank [T, H]`` f32 -> ``send [W, T, H/W, D + 8]`` bf16."""
+    T, H, D = out_rank.shape
+    _need(out_rank, torch.bfloat16, (T, H, D), "out_rank")
+    _need(lse_rank, torch.float32, (T, H), "lse_rank")
+    _need(send, torch.bfloat16, (world, T, H // world, a2a_message_elems(D)), "send")
+    _check(lib.dcpmla_a2a_pack(world, T, H, D, _ptr(out_rank), _ptr(lse_rank), _ptr(send), _stream(stream)),
+           "dcpmla_a2a_pack")
+
+
+def a2a_combine(recv, out, lse, stream=None) -> None:
+    """``recv [W, T, Hl, D + 8]`` bf16 -> ``out [T, Hl, D]`` bf16, ``lse [T, Hl]`` f32."""
+    W, T, Hl, _ = recv.shape
+    D = out.shape[-1]
+    _need(recv, torch.bfloat16, (W, T, Hl, a2a_message_elems(D)), "recv")
+    _need(out, torch.bfloat16, (T, Hl, D), "out")
+    _need(lse, torch.float32, (T, Hl), "lse")
+    _check(lib.dcpmla_a2a_combine(W, T, Hl, D, _ptr(recv), _ptr(out), _ptr(lse), _stream(stream)),
+           "dcpmla_a2a_combine")
+
+
+def project_heads(o, w_v_t, out, stream=None) -> None:
+    """``o [T, H, 512]`` bf16, ``w_v_t [H, DV, 512]`` bf16 -> ``out [T, H, DV]`` bf16."""
+    T, H, _ = o.shape
+    DV = w_v_t.shape[1]
+    _need(o, torch.bfloat16, (T, H, D_V), "o")
+    _need(w_v_t, torch.bfloat16, (H, DV, D_V), "w_v_t")
+    _need(out, torch.bfloat16, (T, H, DV), "out")
+    _check(lib.dcpmla_project_heads(T, H, DV, _ptr(o), _ptr(w_v_t), _ptr(out), _stream(stream)),
+           "dcpmla_project_heads")

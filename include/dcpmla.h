@@ -239,6 +239,52 @@ int dcpmla_merge_segments_dense(int64_t rows, int32_t nseg, const float *o_seg,
                                 const float *lse2_seg, void *out, float *lse,
                                 hipStream_t stream);
 
+/*
+ * The exchange around the cross-rank merge ("Context Parallel Guide (PCP &
+ * DCP)", comm_backend a2a): each rank sends every peer that peer's slice of
+ * heads of its partial, with the fp32 LSE packed alongside as two 16-bit
+ * halves of the bf16 message (an exact round trip), and the combine is done
+ * locally.  A message row is dim bf16 values, then the LSE's low and high 16
+ * bits, then six zeros: dcpmla_a2a_message_elems(dim) = dim + 8 elements
+ * (16-byte aligned).  The all-to-all itself is a collective outside this
+ * library: block p of rank r's send buffer becomes block r of rank p's receive
+ * buffer.
+ */
+int64_t dcpmla_a2a_message_elems(int32_t dim);
+
+/*
+ * Pack one rank's partial: out_rank [tokens, heads, dim] bf16 and lse_rank
+ * [tokens, heads] float (natural log) -> send [W][tokens][heads/W][dim + 8]
+ * bf16, block p holding heads [p*heads/W, (p+1)*heads/W).  heads % W == 0,
+ * dim a multiple of 8 in [8, 512] (512 = latent output, smaller = projected
+ * by dcpmla_project_heads).  DCPMLA_E_ALIAS if send overlaps an input.
+ */
+int dcpmla_a2a_pack(int32_t dcp_world, int64_t tokens, int32_t heads, int32_t dim, const void *out_rank,
+                    const float *lse_rank, void *send, hipStream_t stream);
+
+/*
+ * Local combine after the exchange: recv [W][tokens][heads_local][dim + 8]
+ * (block r from rank r) -> out [tokens, heads_local, dim] bf16 and lse
+ * [tokens, heads_local] float: L = ln sum_r e^LSE_r, O = sum_r e^(LSE_r - L) O_r,
+ * ranks with LSE = -inf weigh nothing; rows with no mass anywhere get O = 0,
+ * LSE = -inf.  Same arithmetic, in the same order, as dcpmla_merge_ranks().
+ */
+int dcpmla_a2a_combine(int32_t dcp_world, int64_t tokens, int32_t heads_local, int32_t dim,
+                       const void *recv, void *out, float *lse, hipStream_t stream);
+
+/*
+ * Project before merge ("Context Parallel Guide (PCP & DCP)",
+ * enable_project_before_merge): W_V is a per-head linear map and the merge is
+ * a per-(token, head) scalar weighting plus a cross-rank sum, so W_V can be
+ * applied to each rank's partial first and the exchange carries v_head_dim
+ * values per head instead of 512.  out [tokens, heads, v_head_dim] bf16 =
+ * o [tokens, heads, 512] bf16 times W_V[h] [512, v_head_dim], with W_V given
+ * transposed as w_v_t [heads, v_head_dim, 512] bf16; fp32 accumulation.
+ * v_head_dim a multiple of 32 up to 512.
+ */
+int dcpmla_project_heads(int64_t tokens, int32_t heads, int32_t v_head_dim, const void *o,
+                         const void *w_v_t, void *out, hipStream_t stream);
+
 /* Static description of a status code. */
 const char *dcpmla_strerror(int status);
 

@@ -24,6 +24,8 @@ Modules:
   layout     -- ownership, rank-local token lists, subpage size, metadata and
                 KV slots, all by brute-force enumeration of global positions
   attention  -- global causal attention, per-rank split, LSE merges (float64)
+  exchange   -- the a2a message layout (LSE as two 16-bit halves) and the
+                per-head W_V projection of project-before-merge
 
 Every function is pinned by ``tests/test_oracle_*.py`` against what the pages
 and mathematics fix (printed examples, closed forms, library routines,

@@ -13,11 +13,13 @@
 //
 // Work decomposition (persistent, stream-K style).  A unit is one 32-token
 // stage of one (sequence b, tile of 128 head-rows).  Units are ordered
-// sequence-major, tile, stage; workgroup w of G takes units
-// [w*U/G, (w+1)*U/G).  A (b, tile) whose stages all fall inside one workgroup
+// sequence-major, tile, stage, and split into G contiguous ranges of equal
+// cost, where each (b, tile) item adds a fixed overhead to its stage count
+// (its query load and output stores), so a workgroup given many short items
+// takes fewer stages.  A (b, tile) whose stages all fall inside one workgroup
 // is finished here (BF16 output + natural-log LSE); otherwise each workgroup
-// writes an unreduced partial (normalised fp32 output + base-2 LSE) to one of
-// its two workspace slots and the segment merge finishes the row.  The grid
+// writes an unreduced partial (normalised output + base-2 LSE) to one of its
+// two workspace slots and the segment merge finishes the row.  The grid
 // depends only on the device, the unit count only on device metadata, so the
 // launch is capture-stable.
 //
@@ -291,8 +293,71 @@ __device__ inline void issue_stage(uint32_t tile_lds, const uint8_t *row, int wa
 
 __device__ inline void wait_direct_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// LDS: two stage tiles, then (PartLds) the work partition and the row
-// lengths, so locating a piece costs no global round trips.
+// Output staging.  The accumulator leaves the MFMA with 4 consecutive dims of
+// one head-row per lane, so storing it directly would touch 32 rows per
+// store.  Instead each wave moves its 32 x 512 block in passes of 128 dims
+// through its own LDS area: written in the accumulator layout, read back as
+// 16-byte pieces of rows, and stored as whole 256- or 512-byte row segments.
+// Rows are padded by 16 bytes so the accumulator-layout writes spread over
+// all banks.  Waves never share an area, so no barrier is needed.
+template <int E>
+struct Staging {
+  static constexpr int kPassDims = 128;
+  static constexpr int kRowBytes = kPassDims * (E == 1 ? 2 : 4) + 16;   // widest element stored
+  static constexpr int kWaveBytes = kWaveRows * kRowBytes;
+  static constexpr int kBytes = kWaves * kWaveBytes;
+};
+
+// rows[r * kDv + c] = T(acc(row r, dim c) * sc) for rows r < nrows; T is
+// __bf16, _Float16 or float.
+template <int E, typename T>
+__device__ inline void store_rows(const floatx16 (&acc)[kDv / 32], float sc, uint8_t *stg, T *rows,
+                                  int nrows, int lane) {
+  // addresses derived from the lane are recomputed per call, not hoisted
+  // out of the piece loop (where they would stay live through the stages)
+  asm volatile("" : "+v"(lane));
+  constexpr int kRow = Staging<E>::kRowBytes;
+  constexpr int kSegBytes = Staging<E>::kPassDims * (int)sizeof(T);
+  constexpr int kLanesPerRow = kSegBytes / 16;
+  constexpr int kRowsPerRead = 64 / kLanesPerRow;
+  const int l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int pass = 0; pass < kDv / Staging<E>::kPassDims; ++pass) {
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd) {
+      const int d = 4 * pass + dd;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        uint8_t *dst = stg + l32 * kRow + (32 * dd + 8 * g4 + 4 * h) * (int)sizeof(T);
+        const float v0 = acc[d][4 * g4 + 0] * sc, v1 = acc[d][4 * g4 + 1] * sc;
+        const float v2 = acc[d][4 * g4 + 2] * sc, v3 = acc[d][4 * g4 + 3] * sc;
+        if constexpr (sizeof(T) == 4) {
+          *(float4 *)dst = make_float4(v0, v1, v2, v3);
+        } else {
+          const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, (T)v0) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, (T)v1) << 16);
+          const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, (T)v2) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, (T)v3) << 16);
+          *(uint2 *)dst = make_uint2(w0, w1);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < kWaveRows / kRowsPerRead; ++i) {
+      const int r = i * kRowsPerRead + lane / kLanesPerRow;
+      const int c = lane % kLanesPerRow;
+      const uint4 v = *(const uint4 *)(stg + r * kRow + 16 * c);
+      if (r < nrows)
+        *(uint4 *)((uint8_t *)(rows + (int64_t)r * kDv + pass * Staging<E>::kPassDims) + 16 * c) = v;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// LDS: two stage tiles, the four waves' output staging areas, then
+// (PartLds) the work partition and the row lengths, so locating a piece
+// costs no global round trips.
 template <int E, bool PartLds>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attention_kernel(AttnArgs a) {
@@ -309,44 +374,136 @@ attention_kernel(AttnArgs a) {
   const int64_t G = effective_groups(gridDim.x, U);
   if ((int64_t)blockIdx.x >= G) return;
   const int64_t w = xcd_group(blockIdx.x, G);
-  const int64_t lo = group_lo(w, U, G);
-  const int64_t hi = group_lo(w + 1, U, G);
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_char *)lds);
-  int32_t *part = (int32_t *)(lds + 2 * Tile<E>::kBytes);
+  int32_t *part = (int32_t *)(lds + 2 * Tile<E>::kBytes + Staging<E>::kBytes);
   const int nwork = 4 * a.B + 2;
   if constexpr (PartLds) {
     for (int i = tid; i < nwork; i += kThreads) part[i] = a.work[i];
     for (int i = tid; i < a.B * a.qlen; i += kThreads) part[nwork + i] = a.row_len[i];
     __syncthreads();
   }
+  // partition values are the same for the whole workgroup: keep them in
+  // scalar registers
   auto work_at = [&](int i) -> int32_t {
-    if constexpr (PartLds) return part[i];
-    else return a.work[i];
+    if constexpr (PartLds) return __builtin_amdgcn_readfirstlane(part[i]);
+    else return __builtin_amdgcn_readfirstlane(a.work[i]);
   };
   auto row_len_at = [&](int i) -> int32_t {
     if constexpr (PartLds) return part[nwork + i];
     else return a.row_len[i];
   };
+  // units whose cost position is below x (the unit index at cost x)
+  const int64_t C = total_cost(U, a.n_mt, a.B);
+  auto units_before = [&](int64_t x) -> int64_t {
+    if (x >= C) return U;
+    int blo = 0, bhi = a.B;   // seq_cost(blo) <= x < seq_cost(bhi)
+    while (bhi - blo > 1) {
+      const int mid = (blo + bhi) >> 1;
+      if (seq_cost(work_at(work_unit_base_off() + mid), a.n_mt, mid) <= x) blo = mid; else bhi = mid;
+    }
+    const int64_t base = work_at(work_unit_base_off() + blo);
+    const int64_t st = work_at(work_stages_off(a.B) + blo);
+    const int64_t rem = x - seq_cost(base, a.n_mt, blo);
+    const int64_t mt = rem / (st + kPieceCost);
+    const int64_t off = rem - mt * (st + kPieceCost) - kPieceCost;
+    return base + mt * st + (off > 0 ? off : 0);
+  };
+  const int64_t lo = units_before(group_cost_lo(w, C, G));
+  const int64_t hi = units_before(group_cost_lo(w + 1, C, G));
+  if (lo >= hi) return;   // a cost range of piece overheads only
   int32_t bad = 0;
 
-  int slot = 0;
-  for (int64_t u = lo; u < hi;) {
-    // locate the (sequence, tile) piece that holds unit u
+  // The group's units [lo, hi) are walked as one stream of (piece, stage)
+  // cursors.  A piece is one (sequence, tile) and the run of its stages this
+  // group owns; the tile of the next unit -- in this piece or the next --
+  // is loaded while the current one is computed, so a new piece waits only
+  // for its query rows.
+  struct Cursor {
+    int b, mt, s;          // sequence, head-row tile, stage
+    int st_begin, st_end;  // this group's stages of the piece
+    int stages;            // stages of sequence b
+  };
+  auto locate = [&](int64_t u) {
     int blo = 0, bhi = a.B;   // unit_base[blo] <= u < unit_base[bhi]
     while (bhi - blo > 1) {
       const int mid = (blo + bhi) >> 1;
       if ((int64_t)work_at(work_unit_base_off() + mid) <= u) blo = mid; else bhi = mid;
     }
-    const int b = blo;
-    const int stages = work_at(work_stages_off(a.B) + b);
-    const int64_t rem = u - work_at(work_unit_base_off() + b);
-    const int mt = (int)(rem / stages);
-    const int st0 = (int)(rem - (int64_t)mt * stages);
-    const int st1 = (int)min((int64_t)stages, st0 + (hi - u));
-    const bool complete = st0 == 0 && st1 == stages;
-    const int lmax = work_at(work_lmax_off(a.B) + b);
-    const int32_t *pt = a.page_table + (int64_t)work_at(work_lrow_off(a.B) + b) * a.max_local_pages;
+    Cursor c;
+    c.b = blo;
+    c.stages = work_at(work_stages_off(a.B) + blo);
+    const int64_t rem = u - work_at(work_unit_base_off() + blo);
+    c.mt = (int)(rem / c.stages);
+    c.s = (int)(rem - (int64_t)c.mt * c.stages);
+    c.st_begin = c.s;
+    c.st_end = (int)min((int64_t)c.stages, c.s + (hi - u));
+    return c;
+  };
+  // cursor of unit u + 1 from that of unit u (u + 1 < hi)
+  auto advance = [&](Cursor c, int64_t u_next) {
+    if (++c.s < c.st_end) return c;
+    if (++c.mt >= a.n_mt) {
+      c.mt = 0;
+      do { ++c.b; } while (work_at(work_stages_off(a.B) + c.b) == 0);
+    }
+    c.stages = work_at(work_stages_off(a.B) + c.b);
+    c.s = 0;
+    c.st_begin = 0;
+    c.st_end = (int)min((int64_t)c.stages, hi - u_next);
+    return c;
+  };
+  auto lmax_of = [&](const Cursor &c) { return work_at(work_lmax_off(a.B) + c.b); };
+  auto pt_of = [&](const Cursor &c) {
+    return a.page_table + (int64_t)work_at(work_lrow_off(a.B) + c.b) * a.max_local_pages;
+  };
+  auto page_of = [&](const Cursor &c) { return fetch_page<E>(a, pt_of(c), c.s, lmax_of(c), lane); };
+  auto load_stage = [&](const Cursor &c, int32_t page, int buf) {
+    issue_stage<E>(lds_base + buf * Tile<E>::kBytes, stage_row<E>(a, page, c.s, lmax_of(c), lane, &bad), wave);
+  };
+  bf16x8 qf[kKBlocks];
+  // this lane's head-row of the piece at c, and the query row it loads
+  auto load_q = [&](const Cursor &c) {
+    const int m = c.mt * kTileRows + wave * kWaveRows + l32;
+    const bool mvalid = m < a.M;
+    // rows past M read row M-1 (a valid address) and are zeroed
+    const uint16_t *qrow = a.q + ((int64_t)c.b * a.M + (mvalid ? m : a.M - 1)) * kDqk;
+    const uint32_t keep = mvalid ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int j = 0; j < kKBlocks; ++j) {
+      uint4 v = *(const uint4 *)(qrow + qdim<E>(j, h));
+      v.x &= keep; v.y &= keep; v.z &= keep; v.w &= keep;
+      qf[j] = __builtin_bit_cast(bf16x8, v);
+    }
+  };
 
+  Cursor P = locate(lo);
+  Cursor nx = P;       // cursor of the unit whose tile is in flight
+  int32_t page = 0;    // page id of the unit after nx
+  load_stage(P, page_of(P), 0);
+  if (lo + 1 < hi) {
+    nx = advance(P, lo + 1);
+    page = page_of(nx);
+  }
+
+  floatx16 oacc[kDv / 32];
+#pragma unroll
+  for (int d = 0; d < kDv / 32; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
+  float mrun = kNegInf;
+  float lsum = 0.f;    // sum of the BF16 probabilities fed to the PV MFMAs: normalises O
+  float lsum_f = 0.f;  // fp32 sum of the same probabilities before rounding: gives the LSE
+  int cur = 0;
+  int64_t u = lo;
+
+  wait_direct_loads();
+  __syncthreads();
+
+  while (true) {
+    load_q(P);
+    const int b = P.b;
+    const int mt = P.mt;
+    const bool complete = P.st_begin == 0 && P.st_end == P.stages;
     // this lane's head-row and its verify-row window
     const int m = mt * kTileRows + wave * kWaveRows + l32;
     const bool mvalid = m < a.M;
@@ -354,45 +511,19 @@ attention_kernel(AttnArgs a) {
     // rows past M (zero queries) see every token: their results are never
     // stored, and they keep the wave on the unmasked path
     const int rlen = mvalid ? row_len_at(b * a.qlen + vrow) : 0x3FFFFFFF;
+    const int nst = P.st_end - P.st_begin;
+    Cursor following = P;   // first unit after this piece, when there is one
 
-    bf16x8 qf[kKBlocks];
-    {
-      // rows past M read row M-1 (a valid address) and are zeroed
-      const uint16_t *qrow = a.q + ((int64_t)b * a.M + (mvalid ? m : a.M - 1)) * kDqk;
-      const uint32_t keep = mvalid ? 0xFFFFFFFFu : 0u;
-#pragma unroll
-      for (int j = 0; j < kKBlocks; ++j) {
-        uint4 v = *(const uint4 *)(qrow + qdim<E>(j, h));
-        v.x &= keep; v.y &= keep; v.z &= keep; v.w &= keep;
-        qf[j] = __builtin_bit_cast(bf16x8, v);
-      }
-    }
-
-    // first stage: page id, then its direct loads; later stages are fetched
-    // one stage ahead
-    int32_t page = fetch_page<E>(a, pt, st0, lmax, lane);
-    issue_stage<E>(lds_base, stage_row<E>(a, page, st0, lmax, lane, &bad), wave);
-    if (st0 + 1 < st1) page = fetch_page<E>(a, pt, st0 + 1, lmax, lane);
-
-    floatx16 oacc[kDv / 32];
-#pragma unroll
-    for (int d = 0; d < kDv / 32; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
-    float mrun = kNegInf;
-    float lsum = 0.f;    // sum of the BF16 probabilities fed to the PV MFMAs: normalises O
-    float lsum_f = 0.f;  // fp32 sum of the same probabilities before rounding: gives the LSE
-
-    wait_direct_loads();
-    __syncthreads();
-
-    for (int s = st0; s < st1; ++s) {
-      const int cur = (s - st0) & 1;
-      const bool more = s + 1 < st1;
-      if (more) {
-        issue_stage<E>(lds_base + (cur ^ 1) * Tile<E>::kBytes,
-                       stage_row<E>(a, page, s + 1, lmax, lane, &bad), wave);
-        if (s + 2 < st1) page = fetch_page<E>(a, pt, s + 2, lmax, lane);
+    for (int k = 0; k < nst; ++k) {
+      const int s = P.st_begin + k;
+      const int64_t uu = u + k;
+      if (uu + 1 < hi) {
+        load_stage(nx, page, cur ^ 1);
+        if (k == nst - 1) following = nx;
+        if (uu + 2 < hi) {
+          nx = advance(nx, uu + 2);
+          page = page_of(nx);
+        }
       }
       const uint8_t *sb = lds + cur * Tile<E>::kBytes;
 
@@ -512,72 +643,49 @@ attention_kernel(AttnArgs a) {
         }
       }
 
-      // the next stage's direct loads (this wave's share) have landed; the
+      // the next unit's direct loads (this wave's share) have landed; the
       // barrier makes every wave's share visible and frees the current tile
       wait_direct_loads();
       __syncthreads();
+      cur ^= 1;
     }
-
+    u += nst;
+    const bool more = u < hi;
     // finish the piece
     const float ltot = lsum + other_half(lsum, h);
     const float ltot_f = lsum_f + other_half(lsum_f, h);
     const bool has = ltot > 0.f;
     const float inv = has ? a.out_scale / ltot : 0.f;
     const float lse2 = has ? mrun + __builtin_amdgcn_logf(ltot_f) : kNegInf;
+    // rows of this wave that exist (m < M)
+    const int nrows = min(kWaveRows, a.M - (mt * kTileRows + wave * kWaveRows));
+    uint8_t *stg = lds + 2 * Tile<E>::kBytes + wave * Staging<E>::kWaveBytes;
     if (complete) {
-      if (mvalid) {
-        uint16_t *orow = a.out + ((int64_t)b * a.M + m) * kDv;
-#pragma unroll
-        for (int d = 0; d < kDv / 32; ++d) {
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int dim = 32 * d + 8 * g4 + 4 * h;
-            uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(oacc[d][4 * g4 + 0] * inv)) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(oacc[d][4 * g4 + 1] * inv)) << 16);
-            uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(oacc[d][4 * g4 + 2] * inv)) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(oacc[d][4 * g4 + 3] * inv)) << 16);
-            *(uint2 *)(orow + dim) = make_uint2(w0, w1);
-          }
-        }
-        if (h == 0) a.lse[(int64_t)b * a.M + m] = has ? lse2 * kLn2 : kNegInf;
-      }
-    } else if (mvalid) {
+      __bf16 *orow0 = (__bf16 *)a.out + ((int64_t)b * a.M + mt * kTileRows + wave * kWaveRows) * kDv;
+      store_rows<E>(oacc, inv, stg, orow0, nrows, lane);
+      if (mvalid && h == 0) a.lse[(int64_t)b * a.M + m] = has ? lse2 * kLn2 : kNegInf;
+    } else {
       // rows past M are never merged: no partial for them
-      const int64_t prow = (w * kSlots + slot) * kTileRows + wave * kWaveRows + l32;
+      const int64_t prow0 = (w * kSlots + piece_slot(P.st_begin)) * kTileRows + wave * kWaveRows;
       if constexpr (E == 1) {
         // fp16 partial of o / kv_scale: a weighted mean of E4M3 values, so
         // |value| <= 448 and fp16 keeps 11 significant bits of it
         const float invr = has ? 1.0f / ltot : 0.f;
-        uint2 *orow = (uint2 *)((_Float16 *)a.ws_o + prow * kDv);
-#pragma unroll
-        for (int d = 0; d < kDv / 32; ++d) {
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int dim = 32 * d + 8 * g4 + 4 * h;
-            half2v lo, hi;
-            lo[0] = (_Float16)(oacc[d][4 * g4 + 0] * invr);
-            lo[1] = (_Float16)(oacc[d][4 * g4 + 1] * invr);
-            hi[0] = (_Float16)(oacc[d][4 * g4 + 2] * invr);
-            hi[1] = (_Float16)(oacc[d][4 * g4 + 3] * invr);
-            orow[dim / 4] = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-          }
-        }
+        store_rows<E>(oacc, invr, stg, (_Float16 *)a.ws_o + prow0 * kDv, nrows, lane);
       } else {
-        float *orow = (float *)a.ws_o + prow * kDv;
-#pragma unroll
-        for (int d = 0; d < kDv / 32; ++d) {
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int dim = 32 * d + 8 * g4 + 4 * h;
-            *(float4 *)(orow + dim) = make_float4(oacc[d][4 * g4 + 0] * inv, oacc[d][4 * g4 + 1] * inv,
-                                                  oacc[d][4 * g4 + 2] * inv, oacc[d][4 * g4 + 3] * inv);
-          }
-        }
+        store_rows<E>(oacc, inv, stg, (float *)a.ws_o + prow0 * kDv, nrows, lane);
       }
-      if (h == 0) a.ws_lse2[prow] = lse2;
+      if (mvalid && h == 0) a.ws_lse2[prow0 + l32] = lse2;
     }
-    u += st1 - st0;
-    slot = 1;
+    if (!more) break;
+    P = following;
+#pragma unroll
+    for (int d = 0; d < kDv / 32; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
+    mrun = kNegInf;
+    lsum = 0.f;
+    lsum_f = 0.f;
   }
   if (bad) atomicOr(a.err, DCPMLA_ERR_PAGE_RANGE);
 }
@@ -588,7 +696,7 @@ template <int E, bool PartLds>
 hipError_t launch_variant(const AttnArgs &a, int groups, size_t shmem, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    const size_t cap = PartLds ? kLdsLimit : 2 * Tile<E>::kBytes;
+    const size_t cap = PartLds ? kLdsLimit : 2 * Tile<E>::kBytes + Staging<E>::kBytes;
     const hipError_t e = hipFuncSetAttribute((const void *)attention_kernel<E, PartLds>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)cap);
     if (e != hipSuccess) return e;
@@ -600,7 +708,7 @@ hipError_t launch_variant(const AttnArgs &a, int groups, size_t shmem, hipStream
 
 template <int E>
 hipError_t launch_tile(AttnArgs a, int groups, hipStream_t stream) {
-  const size_t tiles = 2 * Tile<E>::kBytes;
+  const size_t tiles = 2 * Tile<E>::kBytes + Staging<E>::kBytes;
   const size_t part = (size_t)(4 * (int64_t)a.B + 2 + (int64_t)a.B * a.qlen) * 4;
   if (tiles + part <= kLdsLimit) {
     a.part_ints = (int)(part / 4);

@@ -67,8 +67,30 @@ __host__ __device__ inline int64_t effective_groups(int64_t launched, int64_t U)
   return g < launched ? g : launched;
 }
 
-// start unit of persistent workgroup w out of G over U units
-__host__ __device__ inline int64_t group_lo(int64_t w, int64_t U, int64_t G) { return (w * U) / G; }
+// Scheduling cost.  Besides its stages, every (sequence, head-row tile) item
+// costs kPieceCost stage-equivalents for its query load and output stores,
+// which dominate when sequences are short.  Items are laid out on a cost
+// axis in (sequence, tile) order, each as kPieceCost of overhead followed by
+// its stages: item (b, mt) starts at
+//   item_cost(b, mt) = unit_base[b] + kPieceCost * n_mt * b + mt * (stages[b] + kPieceCost)
+// and its stage s sits at item_cost + kPieceCost + s.  Workgroup w of G owns
+// the units whose cost position lies in [w C / G, (w + 1) C / G) with
+// C = U + kPieceCost * n_mt * B.  Every group's cost range is non-empty
+// (G <= U <= C), but it may hold only overhead and so no unit.
+constexpr int64_t kPieceCost = 6;
+__host__ __device__ inline int64_t total_cost(int64_t U, int n_mt, int batch) {
+  return U + kPieceCost * n_mt * (int64_t)batch;
+}
+__host__ __device__ inline int64_t seq_cost(int64_t unit_base_b, int n_mt, int b) {
+  return unit_base_b + kPieceCost * n_mt * (int64_t)b;
+}
+__host__ __device__ inline int64_t group_cost_lo(int64_t w, int64_t C, int64_t G) { return (w * C) / G; }
+// the group whose cost range holds position x (0 <= x < C)
+__host__ __device__ inline int64_t cost_group(int64_t x, int64_t C, int64_t G) { return ((x + 1) * G - 1) / C; }
+// Partial slots: a piece that starts inside its item is its group's first
+// piece (slot 0); a split piece that starts at the item's first stage ends
+// inside the item and so is its group's last piece (slot 1).
+__host__ __device__ inline int piece_slot(int first_stage) { return first_stage > 0 ? 0 : 1; }
 
 // The dispatcher places workgroup i on XCD i % 8.  Logical group numbers
 // (which fix the unit range) are handed out so that each XCD runs one

@@ -140,8 +140,6 @@ __global__ void __launch_bounds__(256) merge_segments_kernel(
     int B, int qlen, int heads, int n_mt, int G, const int32_t *__restrict__ work,
     const PT *__restrict__ ws_o, const float *__restrict__ ws_lse2, const float *__restrict__ ws_scale,
     uint4 *__restrict__ out, float *__restrict__ lse) {
-  __shared__ int s_src[1024];   // partial index (group * kSlots + slot) of each piece part
-  __shared__ int s_n;
   constexpr int kChunks = kTileRows / kMergeRows;
   const int chunk = blockIdx.x % kChunks;
   const int bt = blockIdx.x / kChunks;
@@ -164,34 +162,22 @@ __global__ void __launch_bounds__(256) merge_segments_kernel(
     }
     return;
   }
+  // the groups holding this item's first and last stage (cost positions
+  // x0 and x0 + stages - 1); when they differ, the first of them wrote its
+  // share to its slot 1 and each later one to its slot 0
   const int64_t Geff = effective_groups(G, U);
-  const int64_t u0 = (int64_t)work[work_unit_base_off() + b] + (int64_t)mt * stages;
-  const int64_t u1 = u0 + stages;
-  auto find_group = [&](int64_t u) {
-    int64_t w = (u * Geff) / U;
-    while (w + 1 < Geff && group_lo(w + 1, U, Geff) <= u) ++w;
-    while (w > 0 && group_lo(w, U, Geff) > u) --w;
-    return w;
-  };
-  const int64_t w0 = find_group(u0);
-  const int64_t w1 = find_group(u1 - 1);
+  const int64_t C = total_cost(U, n_mt, B);
+  const int64_t x0 = seq_cost(work[work_unit_base_off() + b], n_mt, b) +
+                     (int64_t)mt * (stages + kPieceCost) + kPieceCost;
+  const int64_t w0 = cost_group(x0, C, Geff);
+  const int64_t w1 = cost_group(x0 + stages - 1, C, Geff);
   if (w0 == w1) return;   // finished inside one workgroup
-  if (threadIdx.x == 0) {
-    int n = 0;
-    for (int64_t w = w0; w <= w1 && n < 1024; ++w) {
-      const int64_t lo = group_lo(w, U, Geff), hi = group_lo(w + 1, U, Geff);
-      if (hi <= lo) continue;   // empty range: wrote nothing
-      const int slot = lo >= u0 ? 0 : 1;
-      s_src[n++] = (int)(w * kSlots + slot);
-    }
-    s_n = n;
-  }
-  __syncthreads();
   if (wave >= nrows) return;
-  const int n = s_n;
+  const int n = (int)(w1 - w0 + 1);
+  auto src_of = [&](int k) { return (w0 + k) * kSlots + (k == 0 ? piece_slot(0) : piece_slot(1)); };
   const int pr0 = chunk * kMergeRows + wave;   // row index inside the tile (partial rows)
   float mx = kNegInf;
-  for (int k = lane; k < n; k += 64) mx = fmaxf(mx, ws_lse2[(int64_t)s_src[k] * kTileRows + pr0]);
+  for (int k = lane; k < n; k += 64) mx = fmaxf(mx, ws_lse2[src_of(k) * kTileRows + pr0]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -205,7 +191,7 @@ __global__ void __launch_bounds__(256) merge_segments_kernel(
       for (int q = 0; q < kMergeBatch; ++q) {
         // entries past n repeat the last partial with weight 0 (a valid address)
         const int kk = k + q < n ? k + q : n - 1;
-        const int64_t pr = (int64_t)s_src[kk] * kTileRows + pr0;
+        const int64_t pr = src_of(kk) * kTileRows + pr0;
         const float l = ws_lse2[pr];
         wgt[q] = (k + q < n && l > kNegInf) ? fast_exp2(l - mx) : 0.f;
         load_partial8(ws_o + pr * kDv, lane, v[q]);

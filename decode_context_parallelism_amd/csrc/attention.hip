@@ -56,6 +56,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef int int2v __attribute__((ext_vector_type(2)));
+typedef int int4v __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_char;
 
@@ -293,6 +294,10 @@ __device__ inline void issue_stage(uint32_t tile_lds, const uint8_t *row, int wa
 
 __device__ inline void wait_direct_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Word 3 of a raw (unswizzled, stride 0) buffer resource: 32-bit data
+// format, all other fields zero; num_records then counts bytes.
+constexpr int kRawBufferFlags = 0x00020000;
+
 // Output staging.  The accumulator leaves the MFMA with 4 consecutive dims of
 // one head-row per lane, so storing it directly would touch 32 rows per
 // store.  Instead each wave moves its 32 x 512 block in passes of 128 dims
@@ -309,18 +314,26 @@ struct Staging {
 };
 
 // rows[r * kDv + c] = T(acc(row r, dim c) * sc) for rows r < nrows; T is
-// __bf16, _Float16 or float.
+// __bf16, _Float16 or float.  The row stores are raw buffer stores whose
+// resource covers only the nrows valid rows, so rows past the end are
+// dropped by the range check instead of being branched around: a branch per
+// store makes the compiler keep values across it in scratch, and each
+// reload's wait would then also wait for every store issued before it.
 template <int E, typename T>
 __device__ inline void store_rows(const floatx16 (&acc)[kDv / 32], float sc, uint8_t *stg, T *rows,
                                   int nrows, int lane) {
-  // addresses derived from the lane are recomputed per call, not hoisted
-  // out of the piece loop (where they would stay live through the stages)
-  asm volatile("" : "+v"(lane));
   constexpr int kRow = Staging<E>::kRowBytes;
   constexpr int kSegBytes = Staging<E>::kPassDims * (int)sizeof(T);
   constexpr int kLanesPerRow = kSegBytes / 16;
   constexpr int kRowsPerRead = 64 / kLanesPerRow;
+  constexpr int kRowBytes = kDv * (int)sizeof(T);
+  // addresses derived from the lane are recomputed per call, not hoisted
+  // out of the piece loop (where they would stay live through the stages)
+  asm volatile("" : "+v"(lane));
   const int l32 = lane & 31, h = lane >> 5;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(rows, (short)0, nrows > 0 ? nrows * kRowBytes : 0, kRawBufferFlags);
+  const int rlane = lane / kLanesPerRow, c = lane % kLanesPerRow;
 #pragma unroll
   for (int pass = 0; pass < kDv / Staging<E>::kPassDims; ++pass) {
 #pragma unroll
@@ -345,11 +358,9 @@ __device__ inline void store_rows(const floatx16 (&acc)[kDv / 32], float sc, uin
     }
 #pragma unroll
     for (int i = 0; i < kWaveRows / kRowsPerRead; ++i) {
-      const int r = i * kRowsPerRead + lane / kLanesPerRow;
-      const int c = lane % kLanesPerRow;
-      const uint4 v = *(const uint4 *)(stg + r * kRow + 16 * c);
-      if (r < nrows)
-        *(uint4 *)((uint8_t *)(rows + (int64_t)r * kDv + pass * Staging<E>::kPassDims) + 16 * c) = v;
+      const int r = i * kRowsPerRead + rlane;
+      const int4v v = *(const int4v *)(stg + r * kRow + 16 * c);
+      __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, r * kRowBytes + pass * kSegBytes + 16 * c, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -485,14 +496,6 @@ attention_kernel(AttnArgs a) {
     page = page_of(nx);
   }
 
-  floatx16 oacc[kDv / 32];
-#pragma unroll
-  for (int d = 0; d < kDv / 32; ++d)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
-  float mrun = kNegInf;
-  float lsum = 0.f;    // sum of the BF16 probabilities fed to the PV MFMAs: normalises O
-  float lsum_f = 0.f;  // fp32 sum of the same probabilities before rounding: gives the LSE
   int cur = 0;
   int64_t u = lo;
 
@@ -501,6 +504,15 @@ attention_kernel(AttnArgs a) {
 
   while (true) {
     load_q(P);
+    // per-piece softmax state; O^T accumulates in AGPRs
+    floatx16 oacc[kDv / 32];
+#pragma unroll
+    for (int d = 0; d < kDv / 32; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
+    float mrun = kNegInf;
+    float lsum = 0.f;    // sum of the BF16 probabilities fed to the PV MFMAs: normalises O
+    float lsum_f = 0.f;  // fp32 sum of the same probabilities before rounding: gives the LSE
     const int b = P.b;
     const int mt = P.mt;
     const bool complete = P.st_begin == 0 && P.st_end == P.stages;
@@ -679,13 +691,6 @@ attention_kernel(AttnArgs a) {
     }
     if (!more) break;
     P = following;
-#pragma unroll
-    for (int d = 0; d < kDv / 32; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
-    mrun = kNegInf;
-    lsum = 0.f;
-    lsum_f = 0.f;
   }
   if (bad) atomicOr(a.err, DCPMLA_ERR_PAGE_RANGE);
 }

@@ -26,6 +26,8 @@ Modules:
   attention  -- global causal attention, per-rank split, LSE merges (float64)
   exchange   -- the a2a message layout (LSE as two 16-bit halves) and the
                 per-head W_V projection of project-before-merge
+  qsplit     -- the exact two-term E4M3 split of BF16 query rows (with a
+                round-to-nearest-even E4M3 encoder over the code table)
 
 Every function is pinned by ``tests/test_oracle_*.py`` against what the pages
 and mathematics fix (printed examples, closed forms, library routines,

@@ -87,6 +87,7 @@ SIGNATURES = {
     "dcpmla_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "dcpmla_get_device_info": (ctypes.c_int, [_I32, ctypes.c_void_p]),
     "dcpmla_a2a_message_elems": (_I64, [_I32]),
+    "dcpmla_split_q": (ctypes.c_int, [_I64, _P, _P, _P, _P]),
     "dcpmla_a2a_pack": (ctypes.c_int, [_I32, _I64, _I32, _I32, _P, _P, _P, _P]),
     "dcpmla_a2a_combine": (ctypes.c_int, [_I32, _I64, _I32, _I32, _P, _P, _P, _P]),
     "dcpmla_project_heads": (ctypes.c_int, [_I64, _I32, _I32, _P, _P, _P, _P]),

@@ -119,7 +119,7 @@ int64_t dcpmla_workspace_bytes(const dcpmla_geom *g) {
   int groups = 0;
   const int r = resolve_groups(g, &groups);
   if (r != DCPMLA_OK) return r;
-  return ws_bytes(groups);
+  return ws_total_bytes(groups, (int64_t)g->batch * g->qlen * g->num_heads);
 }
 
 int dcpmla_write_kv(const dcpmla_geom *g, int32_t rank, int64_t num_tokens, const int32_t *seq_ids,
@@ -165,8 +165,8 @@ static int attention_checks(const dcpmla_geom *g, const void *q, const void *kv_
   if (!meta_ok(g, m) || !workspace || !out_rank || !lse_rank) return DCPMLA_E_INVALID;
   const int r = resolve_groups(g, groups);
   if (r != DCPMLA_OK) return r;
-  if (workspace_bytes < ws_bytes(*groups)) return DCPMLA_E_WORKSPACE;
   const int64_t rows = (int64_t)g->batch * g->qlen * g->num_heads;
+  if (workspace_bytes < ws_total_bytes(*groups, rows)) return DCPMLA_E_WORKSPACE;
   Range mr[5];
   meta_ranges(g, m, mr);
   const Range ins[] = {{q, rows * kDqk * 2},
@@ -251,6 +251,15 @@ int dcpmla_merge_segments_dense(int64_t rows, int32_t nseg, const float *o_seg,
 int64_t dcpmla_a2a_message_elems(int32_t dim) {
   if (dim < 8 || dim > kDv || dim % 8 != 0) return DCPMLA_E_INVALID;
   return (int64_t)dim + 8;
+}
+
+int dcpmla_split_q(int64_t rows, const void *q, void *q_split, float *inv_scale, hipStream_t stream) {
+  if (rows < 0 || rows >= ((int64_t)1 << 40) / kQSplitRow) return DCPMLA_E_INVALID;
+  if (rows > 0 && (!q || !q_split || !inv_scale)) return DCPMLA_E_INVALID;
+  const Range ins[] = {{q, rows * kDqk * 2}};
+  const Range outs[] = {{q_split, rows * kQSplitRow}, {inv_scale, rows * 4}};
+  if (any_alias(outs, 2, ins, 1) || any_alias(outs, 1, outs + 1, 1)) return DCPMLA_E_ALIAS;
+  return hip_status(launch_split_q(rows, q, q_split, inv_scale, stream));
 }
 
 int dcpmla_a2a_pack(int32_t dcp_world, int64_t tokens, int32_t heads, int32_t dim, const void *out_rank,

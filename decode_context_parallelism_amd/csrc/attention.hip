@@ -57,6 +57,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef int int2v __attribute__((ext_vector_type(2)));
 typedef int int4v __attribute__((ext_vector_type(4)));
+typedef int int8v __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_char;
 
@@ -73,6 +74,8 @@ struct AttnArgs {
   const int32_t *row_len;    // [B*qlen]
   const int32_t *page_table; // [B*qlen, max_local_pages]
   const int32_t *work;
+  const uint8_t *qsplit;     // FP8 cache: [B*M][2][576] E4M3 codes hi, lo of the query
+  const float *qscale;       // FP8 cache: [B*M] 2^-k, q = (hi + lo) * 2^-k
   void *ws_o;                // [G][2][128][512] fp16 (FP8 cache) or float (BF16 cache)
   float *ws_lse2;            // [G][2][128]
   float *ws_scale;           // scale of the fp16 partials
@@ -147,18 +150,28 @@ __device__ inline bf16x8 widen_fp8(uint2 raw) {
 
 // ------------------------------------------------------------ QK operands
 //
-// Q is the stationary B operand.  Its k-slot (8h + e) of MFMA step j holds
-// dim qdim(j, h) + e:
-//   FP8 tile:  steps j = 2p + q read one 16-byte tile row per lane (block
-//              2p + h, the same token row for both steps), so
-//              qdim = 32p + 16h + 8q;
-//   BF16 tile: step j reads half h of block j, so qdim = 16j + 8h.
-// K (A operand) follows the same map; any map works as long as both agree.
-template <int E>
-__device__ inline int qdim(int j, int h) {
-  if constexpr (E == 1) return 32 * (j >> 1) + 16 * h + 8 * (j & 1);
-  else return 16 * j + 8 * h;
+// Q is the stationary B operand, K (from the tile) the A operand; both map
+// their k-slots to the same dims (any map works as long as they agree).
+//   FP8 tile: S^T = K hi + K lo on v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3,
+//     fp32 accumulate).  Step t, lane half h, byte e (0..31) is dim
+//     64t + 32h + e: 32 contiguous bytes of the token row, i.e. tile blocks
+//     4t + 2h and 4t + 2h + 1, and the same 32 bytes of the split query's hi
+//     and lo codes.  The cache elements go to the matrix unit as stored.
+//   BF16 tile: v_mfma_f32_32x32x16_bf16 step j reads half h of block j, so
+//     the k-slot 8h + e is dim 16j + 8h + e.
+__device__ inline int qdim_bf16(int j, int h) { return 16 * j + 8 * h; }
+
+__device__ inline int8v cat8(uint4 a, uint4 b) {
+  int8v r;
+  r[0] = (int)a.x; r[1] = (int)a.y; r[2] = (int)a.z; r[3] = (int)a.w;
+  r[4] = (int)b.x; r[5] = (int)b.y; r[6] = (int)b.z; r[7] = (int)b.w;
+  return r;
 }
+
+// per-lane query operand registers
+template <int E> struct QOperand;
+template <> struct QOperand<1> { int8v v[2 * (kDqk / 64)]; };   // hi, lo of each 64-dim step
+template <> struct QOperand<2> { uint4 v[kKBlocks]; };           // bf16 step j
 
 // ------------------------------------------------------------ PV operands
 //
@@ -471,19 +484,37 @@ attention_kernel(AttnArgs a) {
   auto load_stage = [&](const Cursor &c, int32_t page, int buf) {
     issue_stage<E>(lds_base + buf * Tile<E>::kBytes, stage_row<E>(a, page, c.s, lmax_of(c), lane, &bad), wave);
   };
-  bf16x8 qf[kKBlocks];
+  // the query operand, 576 bytes per lane in either format (FP8 cache: step
+  // t's hi codes in q.v[2t], lo codes in q.v[2t+1])
+  QOperand<E> q;
+  float sc2 = a.score_scale2;   // this lane's score scale (times 2^-k with a split query)
   // this lane's head-row of the piece at c, and the query row it loads
   auto load_q = [&](const Cursor &c) {
     const int m = c.mt * kTileRows + wave * kWaveRows + l32;
     const bool mvalid = m < a.M;
     // rows past M read row M-1 (a valid address) and are zeroed
-    const uint16_t *qrow = a.q + ((int64_t)c.b * a.M + (mvalid ? m : a.M - 1)) * kDqk;
+    const int64_t qr = (int64_t)c.b * a.M + (mvalid ? m : a.M - 1);
     const uint32_t keep = mvalid ? 0xFFFFFFFFu : 0u;
+    if constexpr (E == 1) {
+      const uint8_t *qrow = a.qsplit + qr * kQSplitRow + 32 * h;
 #pragma unroll
-    for (int j = 0; j < kKBlocks; ++j) {
-      uint4 v = *(const uint4 *)(qrow + qdim<E>(j, h));
-      v.x &= keep; v.y &= keep; v.z &= keep; v.w &= keep;
-      qf[j] = __builtin_bit_cast(bf16x8, v);
+      for (int t = 0; t < kDqk / 64; ++t) {
+        q.v[2 * t] = cat8(*(const uint4 *)(qrow + 64 * t), *(const uint4 *)(qrow + 64 * t + 16));
+        q.v[2 * t + 1] = cat8(*(const uint4 *)(qrow + kDqk + 64 * t), *(const uint4 *)(qrow + kDqk + 64 * t + 16));
+      }
+#pragma unroll
+      for (int j = 0; j < 2 * (kDqk / 64); ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q.v[j][e] &= (int)keep;
+      sc2 = a.score_scale2 * a.qscale[qr];
+    } else {
+      const uint16_t *qrow = a.q + qr * kDqk;
+#pragma unroll
+      for (int j = 0; j < kKBlocks; ++j) {
+        uint4 v = *(const uint4 *)(qrow + qdim_bf16(j, h));
+        v.x &= keep; v.y &= keep; v.z &= keep; v.w &= keep;
+        q.v[j] = v;
+      }
     }
   };
 
@@ -544,20 +575,66 @@ attention_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
       if constexpr (E == 1) {
-        // one 16-byte tile row per lane feeds two MFMA steps
-        const uint8_t *kb0 = sb + h * Tile<1>::kBlock + kslot * Tile<1>::kRow;
-        uint4 kr[2];
-        kr[0] = *(const uint4 *)(kb0);
-        kr[1] = *(const uint4 *)(kb0 + 2 * Tile<1>::kBlock);
-#pragma unroll
-        for (int p = 0; p < kKBlocks / 2; ++p) {
-          const uint4 cur_row = kr[p & 1];
-          if (p + 2 < kKBlocks / 2) kr[p & 1] = *(const uint4 *)(kb0 + 2 * (p + 2) * Tile<1>::kBlock);
-          const bf16x8 k0 = widen_fp8(make_uint2(cur_row.x, cur_row.y));
-          const bf16x8 k1 = widen_fp8(make_uint2(cur_row.z, cur_row.w));
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[2 * p], sacc, 0, 0, 0);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[2 * p + 1], sacc, 0, 0, 0);
-        }
+        // Per step t two 16-byte tile reads (blocks 4t + 2h, 4t + 2h + 1: 32
+        // dims of this lane's token row) feed the hi and the lo product.  Written
+        // out so the reads run two steps ahead of the MFMAs in three fixed
+        // register tuples and the scores stay in VGPRs; the compiler left alone
+        // waits for each step's reads and moves an output block out of the
+        // AGPRs to hold the scores.  The closing nops are the wait states an
+        // XDL result needs before a VALU reads it.
+        const uint32_t kaddr = lds_base + cur * Tile<1>::kBytes + 2 * h * Tile<1>::kBlock + kslot * Tile<1>::kRow;
+        asm volatile(
+            "s_waitcnt lgkmcnt(0)\n\t"
+            "ds_read_b128 v[240:243], %[addr] offset:0\n\t"
+            "ds_read_b128 v[244:247], %[addr] offset:512\n\t"
+            "ds_read_b128 v[248:251], %[addr] offset:2048\n\t"
+            "ds_read_b128 v[252:255], %[addr] offset:2560\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
+            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q1], %[acc]\n\t"
+            "ds_read_b128 v[232:235], %[addr] offset:4096\n\t"
+            "ds_read_b128 v[236:239], %[addr] offset:4608\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q2], %[acc]\n\t"
+            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q3], %[acc]\n\t"
+            "ds_read_b128 v[240:243], %[addr] offset:6144\n\t"
+            "ds_read_b128 v[244:247], %[addr] offset:6656\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q4], %[acc]\n\t"
+            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
+            "ds_read_b128 v[248:251], %[addr] offset:8192\n\t"
+            "ds_read_b128 v[252:255], %[addr] offset:8704\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
+            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q7], %[acc]\n\t"
+            "ds_read_b128 v[232:235], %[addr] offset:10240\n\t"
+            "ds_read_b128 v[236:239], %[addr] offset:10752\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q8], %[acc]\n\t"
+            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q9], %[acc]\n\t"
+            "ds_read_b128 v[240:243], %[addr] offset:12288\n\t"
+            "ds_read_b128 v[244:247], %[addr] offset:12800\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q10], %[acc]\n\t"
+            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q11], %[acc]\n\t"
+            "ds_read_b128 v[248:251], %[addr] offset:14336\n\t"
+            "ds_read_b128 v[252:255], %[addr] offset:14848\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q12], %[acc]\n\t"
+            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q13], %[acc]\n\t"
+            "ds_read_b128 v[232:235], %[addr] offset:16384\n\t"
+            "ds_read_b128 v[236:239], %[addr] offset:16896\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q14], %[acc]\n\t"
+            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q15], %[acc]\n\t"
+            "s_waitcnt lgkmcnt(0)\n\t"
+            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q16], %[acc]\n\t"
+            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q17], %[acc]\n\t"
+            "s_nop 15\n\t"
+            "s_nop 3\n\t"
+            : [acc] "=&v"(sacc)
+            : [addr] "v"(kaddr), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]), [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]), [q8] "v"(q.v[8]), [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]), [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(q.v[16]), [q17] "v"(q.v[17])
+            : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory");
       } else {
         const uint8_t *kb0 = sb + kslot * Tile<2>::kRow + 16 * h;
         uint4 kr[2];
@@ -567,7 +644,7 @@ attention_kernel(AttnArgs a) {
         for (int j = 0; j < kKBlocks; ++j) {
           const bf16x8 kop = __builtin_bit_cast(bf16x8, kr[j & 1]);
           if (j + 2 < kKBlocks) kr[j & 1] = *(const uint4 *)(kb0 + (j + 2) * Tile<2>::kBlock);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[j], sacc, 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, __builtin_bit_cast(bf16x8, q.v[j]), sacc, 0, 0, 0);
         }
       }
 
@@ -591,7 +668,7 @@ attention_kernel(AttnArgs a) {
       float mx = kNegInf;
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[r]);
-      mx = fmaxf(mx, other_half(mx, h)) * a.score_scale2;
+      mx = fmaxf(mx, other_half(mx, h)) * sc2;
       const float mnew = fmaxf(mrun, mx);
       const bool need = mnew > mrun + kRescaleSlack;
       const float alpha = need ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.0f;
@@ -628,7 +705,7 @@ attention_kernel(AttnArgs a) {
       bf16x8 pb[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], a.score_scale2, -msub));
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], sc2, -msub));
         pb[r >> 3][r & 7] = (__bf16)p;
         lsum_f += p;
       }
@@ -755,7 +832,16 @@ hipError_t launch_partial_attention(const dcpmla_geom &g, int groups, const void
   a.max_local_pages = g.max_local_pages;
   a.score_scale2 = softmax_scale * kv_scale * 1.44269504088896340736f;
   a.out_scale = kv_scale;
-  if (g.kv_dtype == DCPMLA_KV_FP8_E4M3) return launch_tile<1>(a, groups, stream);
+  const int64_t rows = (int64_t)g.batch * a.M;
+  a.qsplit = (const uint8_t *)workspace + ws_qsplit_off(groups);
+  a.qscale = (const float *)((const uint8_t *)workspace + ws_qscale_off(groups, rows));
+  if (g.kv_dtype == DCPMLA_KV_FP8_E4M3) {
+    // the query as two E4M3 terms for the FP8 products, then the attention
+    const hipError_t e = launch_split_q(rows, q, (uint8_t *)workspace + ws_qsplit_off(groups),
+                                        (float *)((uint8_t *)workspace + ws_qscale_off(groups, rows)), stream);
+    if (e != hipSuccess) return e;
+    return launch_tile<1>(a, groups, stream);
+  }
   return launch_tile<2>(a, groups, stream);
 }
 

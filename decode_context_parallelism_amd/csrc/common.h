@@ -57,6 +57,18 @@ __host__ __device__ inline int64_t ws_scale_off(int groups) {
 }
 __host__ __device__ inline int64_t ws_bytes(int groups) { return (ws_scale_off(groups) + 4) * 4; }
 
+// Then (256-byte aligned) the split query of an FP8-cache launch: per
+// head-row 576 E4M3 codes hi, then 576 codes lo, with q = (hi + lo) * 2^-k;
+// then one float 2^-k per head-row.
+constexpr int kQSplitRow = 2 * kDqk;
+__host__ __device__ inline int64_t ws_qsplit_off(int groups) { return ((ws_bytes(groups) + 255) / 256) * 256; }
+__host__ __device__ inline int64_t ws_qscale_off(int groups, int64_t rows) {
+  return ws_qsplit_off(groups) + rows * kQSplitRow;
+}
+__host__ __device__ inline int64_t ws_total_bytes(int groups, int64_t rows) {
+  return ws_qscale_off(groups, rows) + rows * 4;
+}
+
 // Workgroups that actually take work: every one gets at least about
 // kMinUnitsPerGroup stages, because each split costs a 256 KiB fp32 partial
 // (written here, read back by the segment merge).

@@ -21,6 +21,8 @@ hipError_t launch_partial_attention(const dcpmla_geom &g, int groups, const void
                                     const dcpmla_meta &m, void *workspace, void *out_rank,
                                     float *lse_rank, hipStream_t stream);
 
+hipError_t launch_split_q(int64_t rows, const void *q, void *split, float *inv_scale, hipStream_t stream);
+
 hipError_t launch_merge_segments(const dcpmla_geom &g, int groups, const dcpmla_meta &m,
                                  const void *workspace, void *out_rank, float *lse_rank,
                                  hipStream_t stream);

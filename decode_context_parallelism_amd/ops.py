@@ -243,6 +243,15 @@ def a2a_message_elems(dim: int) -> int:
     return n
 
 
+def split_q(q, q_split, inv_scale, stream=None) -> None:
+    """``q [..., 576]`` bf16 -> ``q_split [rows, 1152]`` uint8 (hi codes, lo codes), ``inv_scale [rows]`` f32."""
+    rows = q.numel() // D_QK
+    _need(q, torch.bfloat16, (*q.shape[:-1], D_QK), "q")
+    _need(q_split, torch.uint8, (rows, 2 * D_QK), "q_split")
+    _need(inv_scale, torch.float32, (rows,), "inv_scale")
+    _check(lib.dcpmla_split_q(rows, _ptr(q), _ptr(q_split), _ptr(inv_scale), _stream(stream)), "dcpmla_split_q")
+
+
 def a2a_pack(world: int, out_rank, lse_rank, send, stream=None) -> None:
     """``out_rank [T, H, D]`` bf16, ``lse_rank [T, H]`` f32 -> ``send [W, T, H/W, D + 8]`` bf16."""
     T, H, D = out_rank.shape

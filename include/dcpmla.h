@@ -139,7 +139,8 @@ int32_t dcpmla_subpage_size(int32_t block_size);
 int64_t dcpmla_work_ints(const dcpmla_geom *geom);
 
 /*
- * Bytes of split-KV scratch dcpmla_partial_attention() needs.  Host only when
+ * Bytes of scratch dcpmla_partial_attention() needs (split-KV partials, then
+ * the split query of an FP8-cache launch).  Host only when
  * geom->groups > 0; with groups == 0 it asks the current device for its
  * compute-unit count (DCPMLA_E_HIP without a device).  Negative on error.
  */
@@ -192,7 +193,9 @@ int dcpmla_build_metadata(const dcpmla_geom *geom, int32_t rank, const int32_t *
  * q [B, qlen, H, 576] bf16; kv_pool [num_blocks, block_size, 576] in
  * geom->kv_dtype; out_rank [B, qlen, H, 512] bf16 and lse_rank [B, qlen, H]
  * float (natural log) receive the rows finished here; workspace of
- * dcpmla_workspace_bytes() bytes.  Must be followed by
+ * dcpmla_workspace_bytes() bytes.  With an FP8 cache the call first writes
+ * dcpmla_split_q() of q into the workspace and runs q . k on the FP8 matrix
+ * units as the two exact E4M3 terms.  Must be followed by
  * dcpmla_merge_segments() on the same stream.
  */
 int dcpmla_partial_attention(const dcpmla_geom *geom, const void *q, const void *kv_pool,
@@ -216,6 +219,20 @@ int dcpmla_rank_attention(const dcpmla_geom *geom, const void *q, const void *kv
                           float kv_scale, float softmax_scale, const dcpmla_meta *meta,
                           void *workspace, int64_t workspace_bytes, void *out_rank,
                           float *lse_rank, hipStream_t stream);
+
+/*
+ * Exact two-term E4M3 split of BF16 query rows, the form in which an FP8-cache
+ * dcpmla_partial_attention() multiplies q against the cache (the query is
+ * BF16, PR #51705; the cache FP8 E4M3 with a per-tensor scale, "Context
+ * Parallel Guide", "How it works" item 4).  Per row, k is the largest
+ * integer with max|q| * 2^k <= 448, hi the E4M3 code nearest x = q * 2^k
+ * (ties to even) and lo the code nearest x - hi.  BF16 has 8 significant bits
+ * and E4M3 4, so q = (hi + lo) * 2^-k exactly for |x| >= 2^-2, and within
+ * 2^-10 * 2^-k below.  q [rows, 576] bf16 (device); q_split [rows, 1152]
+ * bytes: 576 hi codes then 576 lo codes per row; inv_scale [rows] float =
+ * 2^-k.  Outputs may not overlap q or each other (DCPMLA_E_ALIAS).
+ */
+int dcpmla_split_q(int64_t rows, const void *q, void *q_split, float *inv_scale, hipStream_t stream);
 
 /*
  * Cross-rank LSE merge ("Context Parallel Guide", enable_project_before_merge:

@@ -91,9 +91,22 @@ def test_sizes():
     # partition (4B + 2 ints), padded to 64 ints, then one zero latent row
     assert ops.work_ints(g) == 64 + 576 * 2 // 4
     ws = ops.workspace_bytes(g)
-    # per group: 2 slots x 128 rows x (512 partial values + 1 lse2) floats; then a 16-byte scale slot
-    assert ws == 4 * 2 * 128 * (512 + 1) * 4 + 16
-    assert (ops.workspace_bytes(_geom(groups=1)) - 16) * 4 == ws - 16
+    # per group: 2 slots x 128 rows x (512 partial values + 1 lse2) floats; then a 16-byte scale
+    # slot; then, 256-byte aligned, per head-row 1152 bytes of split query and a float scale
+    part = 4 * 2 * 128 * (512 + 1) * 4 + 16
+    rows = 5 * 3 * 16
+    assert ws == (part + 255) // 256 * 256 + rows * (1152 + 4)
+    part1 = 1 * 2 * 128 * (512 + 1) * 4 + 16
+    assert ops.workspace_bytes(_geom(groups=1, batch=5)) == (part1 + 255) // 256 * 256 + rows * 1156
+
+
+def test_split_q_checks():
+    L = _lib.lib
+    assert L.dcpmla_split_q(-1, FAKE, FAKE + 10 ** 7, FAKE + 2 * 10 ** 7, None) == _lib.E_INVALID
+    assert L.dcpmla_split_q(4, None, FAKE + 10 ** 7, FAKE + 2 * 10 ** 7, None) == _lib.E_INVALID
+    assert L.dcpmla_split_q(4, FAKE, FAKE + 100, FAKE + 2 * 10 ** 7, None) == _lib.E_ALIAS     # split over q
+    assert L.dcpmla_split_q(4, FAKE, FAKE + 10 ** 7, FAKE + 10 ** 7 + 64, None) == _lib.E_ALIAS  # scale over split
+    assert L.dcpmla_split_q(0, None, None, None, None) == _lib.OK
 
 
 def test_strerror():

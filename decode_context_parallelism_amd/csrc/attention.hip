@@ -446,6 +446,13 @@ attention_kernel(AttnArgs a) {
     int b, mt, s;          // sequence, head-row tile, stage
     int st_begin, st_end;  // this group's stages of the piece
     int stages;            // stages of sequence b
+    int lmax, lrow;        // b's longest rank-local row length and the row that has it
+  };
+  // per-sequence values, read once when a cursor reaches a sequence (not per stage)
+  auto enter_seq = [&](Cursor &c) {
+    c.stages = work_at(work_stages_off(a.B) + c.b);
+    c.lmax = work_at(work_lmax_off(a.B) + c.b);
+    c.lrow = work_at(work_lrow_off(a.B) + c.b);
   };
   auto locate = [&](int64_t u) {
     int blo = 0, bhi = a.B;   // unit_base[blo] <= u < unit_base[bhi]
@@ -455,7 +462,7 @@ attention_kernel(AttnArgs a) {
     }
     Cursor c;
     c.b = blo;
-    c.stages = work_at(work_stages_off(a.B) + blo);
+    enter_seq(c);
     const int64_t rem = u - work_at(work_unit_base_off() + blo);
     c.mt = (int)(rem / c.stages);
     c.s = (int)(rem - (int64_t)c.mt * c.stages);
@@ -469,17 +476,15 @@ attention_kernel(AttnArgs a) {
     if (++c.mt >= a.n_mt) {
       c.mt = 0;
       do { ++c.b; } while (work_at(work_stages_off(a.B) + c.b) == 0);
+      enter_seq(c);
     }
-    c.stages = work_at(work_stages_off(a.B) + c.b);
     c.s = 0;
     c.st_begin = 0;
     c.st_end = (int)min((int64_t)c.stages, hi - u_next);
     return c;
   };
-  auto lmax_of = [&](const Cursor &c) { return work_at(work_lmax_off(a.B) + c.b); };
-  auto pt_of = [&](const Cursor &c) {
-    return a.page_table + (int64_t)work_at(work_lrow_off(a.B) + c.b) * a.max_local_pages;
-  };
+  auto lmax_of = [&](const Cursor &c) { return c.lmax; };
+  auto pt_of = [&](const Cursor &c) { return a.page_table + (int64_t)c.lrow * a.max_local_pages; };
   auto page_of = [&](const Cursor &c) { return fetch_page<E>(a, pt_of(c), c.s, lmax_of(c), lane); };
   auto load_stage = [&](const Cursor &c, int32_t page, int buf) {
     issue_stage<E>(lds_base + buf * Tile<E>::kBytes, stage_row<E>(a, page, c.s, lmax_of(c), lane, &bad), wave);

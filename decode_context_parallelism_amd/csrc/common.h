@@ -70,9 +70,12 @@ __host__ __device__ inline int64_t ws_total_bytes(int groups, int64_t rows) {
 }
 
 // Workgroups that actually take work: every one gets at least about
-// kMinUnitsPerGroup stages, because each split costs a 256 KiB fp32 partial
-// (written here, read back by the segment merge).
-constexpr int64_t kMinUnitsPerGroup = 8;
+// kMinUnitsPerGroup stages, because each split costs a partial of 128 rows
+// x 512 values (written here, read back by the segment merge) and a reload of
+// the tile's query rows.  Four keeps every compute unit busy on the small
+// verify workload (about 1,200 stages per rank) and is measured faster there
+// than eight.
+constexpr int64_t kMinUnitsPerGroup = 4;
 __host__ __device__ inline int64_t effective_groups(int64_t launched, int64_t U) {
   int64_t g = (U + kMinUnitsPerGroup - 1) / kMinUnitsPerGroup;
   if (g < 1) g = 1;

@@ -14,6 +14,8 @@ KV_BF16 = 0
 KV_FP8_E4M3 = 1
 BOUNDARY_CAUSAL = 0
 BOUNDARY_BLOCK = 1
+Q_SPLIT = 0
+Q_FP8 = 1
 
 OK = 0
 E_INVALID = -1
@@ -44,6 +46,7 @@ class Geom(ctypes.Structure):
         ("groups", ctypes.c_int32),
         ("num_blocks", ctypes.c_int64),
         ("row_boundary", ctypes.c_int32),
+        ("q_format", ctypes.c_int32),
     ]
 
 

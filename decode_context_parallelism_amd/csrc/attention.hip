@@ -382,7 +382,7 @@ __device__ inline void store_rows(const floatx16 (&acc)[kDv / 32], float sc, uin
 // LDS: two stage tiles, the four waves' output staging areas, then
 // (PartLds) the work partition and the row lengths, so locating a piece
 // costs no global round trips.
-template <int E, bool PartLds>
+template <int E, bool PartLds, bool QF8>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attention_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
@@ -588,58 +588,105 @@ attention_kernel(AttnArgs a) {
         // AGPRs to hold the scores.  The closing nops are the wait states an
         // XDL result needs before a VALU reads it.
         const uint32_t kaddr = lds_base + cur * Tile<1>::kBytes + 2 * h * Tile<1>::kBlock + kslot * Tile<1>::kRow;
-        asm volatile(
-            "s_waitcnt lgkmcnt(0)\n\t"
-            "ds_read_b128 v[240:243], %[addr] offset:0\n\t"
-            "ds_read_b128 v[244:247], %[addr] offset:512\n\t"
-            "ds_read_b128 v[248:251], %[addr] offset:2048\n\t"
-            "ds_read_b128 v[252:255], %[addr] offset:2560\n\t"
-            "s_waitcnt lgkmcnt(2)\n\t"
-            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
-            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q1], %[acc]\n\t"
-            "ds_read_b128 v[232:235], %[addr] offset:4096\n\t"
-            "ds_read_b128 v[236:239], %[addr] offset:4608\n\t"
-            "s_waitcnt lgkmcnt(2)\n\t"
-            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q2], %[acc]\n\t"
-            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q3], %[acc]\n\t"
-            "ds_read_b128 v[240:243], %[addr] offset:6144\n\t"
-            "ds_read_b128 v[244:247], %[addr] offset:6656\n\t"
-            "s_waitcnt lgkmcnt(2)\n\t"
-            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q4], %[acc]\n\t"
-            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
-            "ds_read_b128 v[248:251], %[addr] offset:8192\n\t"
-            "ds_read_b128 v[252:255], %[addr] offset:8704\n\t"
-            "s_waitcnt lgkmcnt(2)\n\t"
-            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
-            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q7], %[acc]\n\t"
-            "ds_read_b128 v[232:235], %[addr] offset:10240\n\t"
-            "ds_read_b128 v[236:239], %[addr] offset:10752\n\t"
-            "s_waitcnt lgkmcnt(2)\n\t"
-            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q8], %[acc]\n\t"
-            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q9], %[acc]\n\t"
-            "ds_read_b128 v[240:243], %[addr] offset:12288\n\t"
-            "ds_read_b128 v[244:247], %[addr] offset:12800\n\t"
-            "s_waitcnt lgkmcnt(2)\n\t"
-            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q10], %[acc]\n\t"
-            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q11], %[acc]\n\t"
-            "ds_read_b128 v[248:251], %[addr] offset:14336\n\t"
-            "ds_read_b128 v[252:255], %[addr] offset:14848\n\t"
-            "s_waitcnt lgkmcnt(2)\n\t"
-            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q12], %[acc]\n\t"
-            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q13], %[acc]\n\t"
-            "ds_read_b128 v[232:235], %[addr] offset:16384\n\t"
-            "ds_read_b128 v[236:239], %[addr] offset:16896\n\t"
-            "s_waitcnt lgkmcnt(2)\n\t"
-            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q14], %[acc]\n\t"
-            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q15], %[acc]\n\t"
-            "s_waitcnt lgkmcnt(0)\n\t"
-            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q16], %[acc]\n\t"
-            "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q17], %[acc]\n\t"
-            "s_nop 15\n\t"
-            "s_nop 3\n\t"
-            : [acc] "=&v"(sacc)
-            : [addr] "v"(kaddr), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]), [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]), [q8] "v"(q.v[8]), [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]), [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(q.v[16]), [q17] "v"(q.v[17])
-            : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory");
+        if constexpr (!QF8) {
+          asm volatile(
+              "s_waitcnt lgkmcnt(0)\n\t"
+              "ds_read_b128 v[240:243], %[addr] offset:0\n\t"
+              "ds_read_b128 v[244:247], %[addr] offset:512\n\t"
+              "ds_read_b128 v[248:251], %[addr] offset:2048\n\t"
+              "ds_read_b128 v[252:255], %[addr] offset:2560\n\t"
+              "s_waitcnt lgkmcnt(2)\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q1], %[acc]\n\t"
+              "ds_read_b128 v[232:235], %[addr] offset:4096\n\t"
+              "ds_read_b128 v[236:239], %[addr] offset:4608\n\t"
+              "s_waitcnt lgkmcnt(2)\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q2], %[acc]\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q3], %[acc]\n\t"
+              "ds_read_b128 v[240:243], %[addr] offset:6144\n\t"
+              "ds_read_b128 v[244:247], %[addr] offset:6656\n\t"
+              "s_waitcnt lgkmcnt(2)\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q4], %[acc]\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
+              "ds_read_b128 v[248:251], %[addr] offset:8192\n\t"
+              "ds_read_b128 v[252:255], %[addr] offset:8704\n\t"
+              "s_waitcnt lgkmcnt(2)\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q7], %[acc]\n\t"
+              "ds_read_b128 v[232:235], %[addr] offset:10240\n\t"
+              "ds_read_b128 v[236:239], %[addr] offset:10752\n\t"
+              "s_waitcnt lgkmcnt(2)\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q8], %[acc]\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q9], %[acc]\n\t"
+              "ds_read_b128 v[240:243], %[addr] offset:12288\n\t"
+              "ds_read_b128 v[244:247], %[addr] offset:12800\n\t"
+              "s_waitcnt lgkmcnt(2)\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q10], %[acc]\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q11], %[acc]\n\t"
+              "ds_read_b128 v[248:251], %[addr] offset:14336\n\t"
+              "ds_read_b128 v[252:255], %[addr] offset:14848\n\t"
+              "s_waitcnt lgkmcnt(2)\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q12], %[acc]\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q13], %[acc]\n\t"
+              "ds_read_b128 v[232:235], %[addr] offset:16384\n\t"
+              "ds_read_b128 v[236:239], %[addr] offset:16896\n\t"
+              "s_waitcnt lgkmcnt(2)\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q14], %[acc]\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q15], %[acc]\n\t"
+              "s_waitcnt lgkmcnt(0)\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q16], %[acc]\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q17], %[acc]\n\t"
+              "s_nop 15\n\t"
+              "s_nop 3\n\t"
+              : [acc] "=&v"(sacc)
+              : [addr] "v"(kaddr), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]), [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]), [q8] "v"(q.v[8]), [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]), [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(q.v[16]), [q17] "v"(q.v[17])
+              : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory");
+        } else {
+          // the quantised query: the hi terms alone
+          asm volatile(
+              "s_waitcnt lgkmcnt(0)\n\t"
+              "ds_read_b128 v[240:243], %[addr] offset:0\n\t"
+              "ds_read_b128 v[244:247], %[addr] offset:512\n\t"
+              "ds_read_b128 v[248:251], %[addr] offset:2048\n\t"
+              "ds_read_b128 v[252:255], %[addr] offset:2560\n\t"
+              "s_waitcnt lgkmcnt(2)\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
+              "ds_read_b128 v[232:235], %[addr] offset:4096\n\t"
+              "ds_read_b128 v[236:239], %[addr] offset:4608\n\t"
+              "s_waitcnt lgkmcnt(2)\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q2], %[acc]\n\t"
+              "ds_read_b128 v[240:243], %[addr] offset:6144\n\t"
+              "ds_read_b128 v[244:247], %[addr] offset:6656\n\t"
+              "s_waitcnt lgkmcnt(2)\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q4], %[acc]\n\t"
+              "ds_read_b128 v[248:251], %[addr] offset:8192\n\t"
+              "ds_read_b128 v[252:255], %[addr] offset:8704\n\t"
+              "s_waitcnt lgkmcnt(2)\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
+              "ds_read_b128 v[232:235], %[addr] offset:10240\n\t"
+              "ds_read_b128 v[236:239], %[addr] offset:10752\n\t"
+              "s_waitcnt lgkmcnt(2)\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q8], %[acc]\n\t"
+              "ds_read_b128 v[240:243], %[addr] offset:12288\n\t"
+              "ds_read_b128 v[244:247], %[addr] offset:12800\n\t"
+              "s_waitcnt lgkmcnt(2)\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q10], %[acc]\n\t"
+              "ds_read_b128 v[248:251], %[addr] offset:14336\n\t"
+              "ds_read_b128 v[252:255], %[addr] offset:14848\n\t"
+              "s_waitcnt lgkmcnt(2)\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q12], %[acc]\n\t"
+              "ds_read_b128 v[232:235], %[addr] offset:16384\n\t"
+              "ds_read_b128 v[236:239], %[addr] offset:16896\n\t"
+              "s_waitcnt lgkmcnt(2)\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q14], %[acc]\n\t"
+              "s_waitcnt lgkmcnt(0)\n\t"
+              "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q16], %[acc]\n\t"
+              "s_nop 15\n\t"
+              "s_nop 3\n\t"
+              : [acc] "=&v"(sacc)
+              : [addr] "v"(kaddr), [q0] "v"(q.v[0]), [q2] "v"(q.v[2]), [q4] "v"(q.v[4]), [q6] "v"(q.v[6]), [q8] "v"(q.v[8]), [q10] "v"(q.v[10]), [q12] "v"(q.v[12]), [q14] "v"(q.v[14]), [q16] "v"(q.v[16])
+              : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory");
+        }
       } else {
         const uint8_t *kb0 = sb + kslot * Tile<2>::kRow + 16 * h;
         uint4 kr[2];
@@ -779,30 +826,30 @@ attention_kernel(AttnArgs a) {
 
 constexpr size_t kLdsLimit = 160 * 1024;   // gfx950 LDS per workgroup
 
-template <int E, bool PartLds>
+template <int E, bool PartLds, bool QF8>
 hipError_t launch_variant(const AttnArgs &a, int groups, size_t shmem, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
     const size_t cap = PartLds ? kLdsLimit : 2 * Tile<E>::kBytes + Staging<E>::kBytes;
-    const hipError_t e = hipFuncSetAttribute((const void *)attention_kernel<E, PartLds>,
+    const hipError_t e = hipFuncSetAttribute((const void *)attention_kernel<E, PartLds, QF8>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)cap);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((attention_kernel<E, PartLds>), dim3(groups), dim3(kThreads), shmem, stream, a);
+  hipLaunchKernelGGL((attention_kernel<E, PartLds, QF8>), dim3(groups), dim3(kThreads), shmem, stream, a);
   return hipGetLastError();
 }
 
-template <int E>
+template <int E, bool QF8>
 hipError_t launch_tile(AttnArgs a, int groups, hipStream_t stream) {
   const size_t tiles = 2 * Tile<E>::kBytes + Staging<E>::kBytes;
   const size_t part = (size_t)(4 * (int64_t)a.B + 2 + (int64_t)a.B * a.qlen) * 4;
   if (tiles + part <= kLdsLimit) {
     a.part_ints = (int)(part / 4);
-    return launch_variant<E, true>(a, groups, tiles + part, stream);
+    return launch_variant<E, true, QF8>(a, groups, tiles + part, stream);
   }
   a.part_ints = 0;
-  return launch_variant<E, false>(a, groups, tiles, stream);
+  return launch_variant<E, false, QF8>(a, groups, tiles, stream);
 }
 
 }  // namespace
@@ -845,9 +892,10 @@ hipError_t launch_partial_attention(const dcpmla_geom &g, int groups, const void
     const hipError_t e = launch_split_q(rows, q, (uint8_t *)workspace + ws_qsplit_off(groups),
                                         (float *)((uint8_t *)workspace + ws_qscale_off(groups, rows)), stream);
     if (e != hipSuccess) return e;
-    return launch_tile<1>(a, groups, stream);
+    if (g.q_format == DCPMLA_Q_FP8) return launch_tile<1, true>(a, groups, stream);
+    return launch_tile<1, false>(a, groups, stream);
   }
-  return launch_tile<2>(a, groups, stream);
+  return launch_tile<2, false>(a, groups, stream);
 }
 
 }  // namespace dcpmla

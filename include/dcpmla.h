@@ -77,6 +77,21 @@ enum {
   DCPMLA_BOUNDARY_BLOCK = 1
 };
 
+/*
+ * How an FP8-cache attention multiplies the BF16 query against the cache.
+ * SPLIT (default): as two E4M3 terms that sum to the query exactly (see
+ * dcpmla_split_q()), so the result is the BF16-query attention.  FP8: as one
+ * E4M3 term per element with a per-head-row power-of-two scale -- the
+ * quantised FP8 query of "Context Parallel Guide (PCP & DCP)", "How it
+ * works" item 4 (decode gathers an FP8 query for an FP8 cache); the result
+ * is attention with that quantised query, and the query products take half
+ * the matrix work.  FP8 requires an FP8 cache.
+ */
+enum {
+  DCPMLA_Q_SPLIT = 0,
+  DCPMLA_Q_FP8 = 1
+};
+
 /* Bits of the device error word. */
 enum {
   DCPMLA_ERR_CTX_LT_QLEN = 1,    /* ctx < qlen: rows whose boundary would be < 1 get no tokens */
@@ -107,6 +122,7 @@ typedef struct dcpmla_geom {
                                  compute unit of the current device */
   int64_t num_blocks;         /* physical blocks in each rank's pool */
   int32_t row_boundary;       /* DCPMLA_BOUNDARY_CAUSAL (default) or DCPMLA_BOUNDARY_BLOCK */
+  int32_t q_format;           /* DCPMLA_Q_SPLIT (default) or DCPMLA_Q_FP8 (FP8 cache only) */
 } dcpmla_geom;
 
 /*

@@ -88,3 +88,14 @@ def split_rows(q: np.ndarray):
 def join_rows(hi, lo, inv) -> np.ndarray:
     """Inverse of ``split_rows`` (exact for elements the split keeps exactly)."""
     return (E4M3_TABLE[np.asarray(hi)] + E4M3_TABLE[np.asarray(lo)]) * np.asarray(inv)[:, None]
+
+
+def quantize_rows(q: np.ndarray) -> np.ndarray:
+    """The FP8 query: each element as its one nearest E4M3 value at the row's
+    scale 2^-k (the hi term of ``split_rows`` alone), as float64.  This is the
+    quantised query of "Context Parallel Guide (PCP & DCP)", "How it works"
+    item 4 (decode gathers an FP8 query for an FP8 cache), with a power-of-two
+    scale per head-row."""
+    q = np.asarray(q, dtype=np.float64)
+    hi, _, inv = split_rows(q.reshape(-1, q.shape[-1]))
+    return (E4M3_TABLE[hi] * inv[:, None]).reshape(q.shape)

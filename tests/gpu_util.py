@@ -11,14 +11,14 @@ from oracle import formats
 HAS_GPU = torch.cuda.is_available()
 
 
-def geometry(w, groups=0, max_local_pages=None, num_blocks=None, row_boundary="causal"):
+def geometry(w, groups=0, max_local_pages=None, num_blocks=None, row_boundary="causal", q_format="split"):
     from decode_context_parallelism_amd import ops
     return ops.Geometry(dcp_world=w.world, interleave=w.interleave, block_size=w.block_size,
                         qlen=w.qlen, num_heads=w.heads, batch=w.batch,
                         max_blocks_per_seq=w.block_table.shape[1],
                         max_local_pages=max_local_pages or w.max_local_pages,
                         kv_dtype=w.kv_format, num_blocks=num_blocks or w.num_blocks,
-                        groups=groups, row_boundary=row_boundary)
+                        groups=groups, row_boundary=row_boundary, q_format=q_format)
 
 
 def device_inputs(w, device="cuda"):
@@ -35,10 +35,10 @@ def device_inputs(w, device="cuda"):
                 ctx_lens=torch.from_numpy(w.ctx_lens).to(device))
 
 
-def run_group(w, groups=0, device="cuda", row_boundary="causal"):
+def run_group(w, groups=0, device="cuda", row_boundary="causal", q_format="split"):
     """Write the KV, build every rank's metadata, run every rank and the merge."""
     from decode_context_parallelism_amd.group import DcpGroup
-    g = geometry(w, groups=groups, row_boundary=row_boundary)
+    g = geometry(w, groups=groups, row_boundary=row_boundary, q_format=q_format)
     d = device_inputs(w, device)
     grp = DcpGroup(g, device)
     grp.write_kv(d["seq_ids"], d["positions"], d["latents"], d["block_table"])
@@ -54,8 +54,14 @@ def oracle_latents(w):
     return get
 
 
-def oracle_q(w):
-    return formats.decode_bf16(w.q_bits)
+def oracle_q(w, q_format="split"):
+    """The query the method multiplies: the BF16 query, or with q_format "fp8"
+    its per-row E4M3 quantisation (oracle.qsplit.quantize_rows)."""
+    q = formats.decode_bf16(w.q_bits)
+    if q_format == "fp8":
+        from oracle import qsplit
+        q = qsplit.quantize_rows(q)
+    return q
 
 
 def bf16_to_f64(t):

@@ -22,8 +22,8 @@ from gpu_util import (LSE_TOL, bf16_to_f64, oracle_latents, oracle_q, output_bou
 pytestmark = pytest.mark.gpu
 
 
-def _compare_rank(w, grp, r, rows, boundary=layout.verify_row_boundary):
-    o, l = A.verify_attention(oracle_q(w), oracle_latents(w), w.ctx_lens, w.softmax_scale,
+def _compare_rank(w, grp, r, rows, boundary=layout.verify_row_boundary, q_format="split"):
+    o, l = A.verify_attention(oracle_q(w, q_format), oracle_latents(w), w.ctx_lens, w.softmax_scale,
                               world=w.world, interleave=w.interleave, rank=r, rows=rows,
                               boundary=boundary)
     go = bf16_to_f64(grp.out_ranks[r])
@@ -43,8 +43,8 @@ def _compare_rank(w, grp, r, rows, boundary=layout.verify_row_boundary):
             assert err_l <= LSE_TOL, (r, b, i, err_l)
 
 
-def _compare_merged(w, grp, rows, boundary=layout.verify_row_boundary):
-    q, lat = oracle_q(w), oracle_latents(w)
+def _compare_merged(w, grp, rows, boundary=layout.verify_row_boundary, q_format="split"):
+    q, lat = oracle_q(w, q_format), oracle_latents(w)
     o, l = A.verify_attention(q, lat, w.ctx_lens, w.softmax_scale, rows=rows, boundary=boundary)
     ro, rl = [], []
     for r in range(w.world):
@@ -176,3 +176,28 @@ def test_block_rows_full(k, groups):
     for r in range(w.world):
         _compare_rank(w, grp, r, rows, boundary=layout.block_row_boundary)
     _compare_merged(w, grp, rows, boundary=layout.block_row_boundary)
+
+
+@pytest.mark.parametrize("k,groups", [(2, 0), (2, 5)])
+def test_fp8_query_full(k, groups):
+    # the quantised-query variant against attention with the same E4M3 query
+    w = make_config(k)
+    print(f"config {k} groups {groups} q_format fp8", flush=True)
+    grp, _ = run_group(w, groups=groups, q_format="fp8")
+    assert grp.errors() == 0
+    rows = [(b, i) for b in range(w.batch) for i in range(w.qlen)]
+    for r in range(w.world):
+        _compare_rank(w, grp, r, rows, q_format="fp8")
+    _compare_merged(w, grp, rows, q_format="fp8")
+
+
+@pytest.mark.parametrize("k", [3, 4])
+def test_fp8_query_sampled(k):
+    w = make_config(k)
+    print(f"config {k}: {w.name} q_format fp8", flush=True)
+    grp, _ = run_group(w, q_format="fp8")
+    assert grp.errors() == 0
+    rows = _sample_rows(w, 3, 60 + k)
+    for r in (0, w.world - 1):
+        _compare_rank(w, grp, r, rows, q_format="fp8")
+    _compare_merged(w, grp, rows, q_format="fp8")

@@ -73,6 +73,14 @@ def test_validate_rejects_bad_dtype():
     assert _lib.lib.dcpmla_validate(ctypes.byref(g)) == _lib.E_INVALID
 
 
+def test_validate_q_format():
+    assert ops.validate(_geom(kv_dtype="fp8_e4m3", q_format="fp8")) == _lib.OK
+    assert ops.validate(_geom(kv_dtype="bf16", q_format="fp8")) == _lib.E_INVALID   # FP8 cache only
+    g = _geom().c()
+    g.q_format = 2
+    assert _lib.lib.dcpmla_validate(ctypes.byref(g)) == _lib.E_INVALID
+
+
 def test_validate_row_boundary():
     assert ops.validate(_geom(row_boundary="block")) == _lib.OK
     g = _geom().c()

@@ -83,3 +83,25 @@ def test_split_rows_reconstruct(wide):
     amax = np.abs(q).max(axis=1)
     nz = amax > 0
     assert np.all(amax[nz] / inv[nz] <= 448.0) and np.all(amax[nz] / inv[nz] > 224.0)
+
+
+def test_quantize_rows_error_bound_and_idempotence():
+    rng = np.random.default_rng(21)
+    q = _bf16_rows(rng, 32, 576, wide=True)
+    qq = qsplit.quantize_rows(q)
+    inv = np.array([2.0 ** -qsplit.row_exponent(float(np.abs(r).max())) for r in q])
+    x = np.abs(q) / inv[:, None]
+    normal = x >= 2.0 ** -6
+    # nearest E4M3: half an ulp, 2^-4 of the value in the normal range, 2^-10 (x units) below
+    assert np.all(np.abs(qq - q)[normal] <= 2.0 ** -4 * np.abs(q)[normal])
+    assert np.all((np.abs(qq - q) / inv[:, None])[~normal] <= 2.0 ** -10)
+    assert np.array_equal(qsplit.quantize_rows(qq), qq)
+
+
+def test_quantize_rows_matches_library_conversion():
+    rng = np.random.default_rng(22)
+    q = _bf16_rows(rng, 16, 576)
+    k = np.array([qsplit.row_exponent(float(np.abs(r).max())) for r in q])
+    x = q * np.exp2(k)[:, None]
+    lib = torch.tensor(x, dtype=torch.float64).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(qsplit.quantize_rows(q), lib * np.exp2(-k)[:, None])

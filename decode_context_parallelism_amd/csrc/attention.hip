@@ -292,14 +292,40 @@ __device__ inline void dma16(const uint8_t *src, uint32_t lds_addr) {
 
 // This wave's share of a stage: loads i = wave + 4 j.  Load i reads row bytes
 // 32 i + (lane part, already in row) and fills tile bytes [1024 i, +1024).
+// The loads of one call share one M0 save/restore (the instruction offset
+// stays 0, as it would move the LDS side too).
 template <int E>
 __device__ inline void issue_stage(uint32_t tile_lds, const uint8_t *row, int wave_s) {
   constexpr int kFull = Tile<E>::kLoads / kWaves;
   constexpr int kRest = Tile<E>::kLoads % kWaves;
   const uint8_t *src = row + 32 * wave_s;
   const uint32_t dst = tile_lds + 1024 * wave_s;
+  if constexpr (kFull == 4) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %5\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %6\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, off\n\t"
+        "s_mov_b32 m0, %7\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, off\n\t"
+        "s_mov_b32 m0, %8\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, off\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "v"(src + 128), "v"(src + 256), "v"(src + 384),
+          "s"(dst), "s"(dst + 4096), "s"(dst + 8192), "s"(dst + 12288)
+        : "memory");
+  } else {
 #pragma unroll
-  for (int j = 0; j < kFull; ++j) dma16(src + 128 * j, dst + 4096 * j);
+    for (int j = 0; j < kFull; ++j) dma16(src + 128 * j, dst + 4096 * j);
+  }
   if constexpr (kRest != 0) {
     if (wave_s < kRest) dma16(src + 128 * kFull, dst + 4096 * kFull);
   }

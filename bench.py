@@ -69,6 +69,8 @@ def parse():
                     help="cross-rank combine: direct LSE merge of all partials (default); a2a pack, "
                          "exchange and local combine; or pbm (project each partial through a "
                          "synthetic W_V [H, 512 -> 128] before the a2a)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of replaying the step as a captured HIP graph")
     ap.add_argument("--no-rotate", action="store_true",
                     help="reuse one input set every step (cache-warm KV)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -223,6 +225,7 @@ def main():
             proj = torch.empty(W, T, H, D, dtype=torch.bfloat16, device=dev)
 
     def combine():
+        stream = torch.cuda.current_stream()
         if args.merge == "direct":
             ops.merge_ranks(grp.out_ranks, grp.lse_ranks, grp.out, grp.lse, stream)
             return
@@ -237,6 +240,8 @@ def main():
             ops.a2a_combine(recv[p], comb_o[p], comb_l[p], stream)
 
     def step(k, events=None):
+        # launches go to the current stream (a capture stream while a graph is recorded)
+        stream = torch.cuda.current_stream()
         pools, q = sets[k % n_sets]
         for r in range(W):
             ops.build_metadata(g, r, ctx, bt, grp.meta[r], stream)
@@ -281,7 +286,32 @@ def main():
     if grp.errors() != 0:
         raise RuntimeError(f"device error word {grp.errors():#x}")
 
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_per_step_eager = (t1 - t0) * 1e3 / args.steps
+    ms_per_step = ms_per_step_eager
+    step_mode = "eager launches"
+    if not args.no_graph:
+        # The same steps replayed as captured HIP graphs (one per input set):
+        # the work is identical, the host launch overhead between the short
+        # kernels is gone.  The per-launch kernel durations above come from
+        # the eager pass.
+        graphs = []
+        for i in range(n_sets):
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gph):
+                step(i)
+            graphs.append(gph)
+        for k in range(args.warmup):
+            graphs[k % n_sets].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            graphs[(args.warmup + k) % n_sets].replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        if grp.errors() != 0:
+            raise RuntimeError(f"device error word {grp.errors():#x}")
+        ms_per_step = (t1 - t0) * 1e3 / args.steps
+        step_mode = "HIP graph replay (one captured graph per input set)"
     attn_ms = np.array([[events[k][r][0].elapsed_time(events[k][r][1]) for r in range(W)]
                         for k in range(args.steps)])
     attn_merge_ms = np.array([[events[k][r][0].elapsed_time(events[k][r][2]) for r in range(W)]
@@ -354,6 +384,8 @@ def main():
                    "kv_tokens_per_step": kv_tokens, "ranks_per_step": W, "input_sets": n_sets,
                    "row_boundary": args.row_boundary, "merge": args.merge, "q_format": args.q_format},
         "verify_rows_per_s": w.batch * w.qlen / (ms_per_step * 1e-3),
+        "step_mode": step_mode,
+        "ms_per_step_eager": ms_per_step_eager,
         "per_rank": {
             "attention_us_mean": float(per_rank_ms.mean() * 1e3),
             "attention_us_max": float(per_rank_ms.max() * 1e3),

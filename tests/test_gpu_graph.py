@@ -1,0 +1,41 @@
+"""The verification step captured as a HIP graph and replayed.
+
+The bench times the step as graph replays, so the captured step must give
+exactly the eager result on every replay: the kernels are deterministic (no
+atomics on the data path, fixed merge orders), so each replay is compared bit
+for bit with an eager forward, with eager work and synchronisations between
+the replays.
+"""
+import pytest
+import torch
+
+from synth import make_config
+from gpu_util import run_group
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("k", [1, 2])
+def test_step_graph_replays_match_eager(k):
+    w = make_config(k)
+    print(f"config {k}: {w.name} graph replay", flush=True)
+    grp, d = run_group(w)
+    ref = [t.clone() for t in (grp.out, grp.lse, grp.out_ranks, grp.lse_ranks)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        grp.forward(d["q"], d["ctx_lens"], d["block_table"], w.kv_scale, w.softmax_scale)
+    for i in range(3):
+        for t in (grp.out, grp.out_ranks):
+            t.fill_(float("nan"))
+        grp.lse.zero_()
+        grp.lse_ranks.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((grp.out, grp.lse, grp.out_ranks, grp.lse_ranks), ref):
+            assert torch.equal(got, want), (k, i)
+        # an eager step between replays, then the same check on its output
+        grp.forward(d["q"], d["ctx_lens"], d["block_table"], w.kv_scale, w.softmax_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(grp.out, ref[0]) and torch.equal(grp.lse, ref[1])
+    assert grp.errors() == 0

@@ -245,11 +245,19 @@ def main():
         pools, q = sets[k % n_sets]
         for r in range(W):
             ops.build_metadata(g, r, ctx, bt, grp.meta[r], stream)
+        if grp.q_split is not None:
+            # once per forward: each rank splits its own head slice before the query gather
+            ops.split_q(q, grp.q_split, grp.q_scale, stream)
         for r in range(W):
             if events is not None:
                 events[r][0].record(stream)
-            ops.partial_attention(g, q, pools[r], w.kv_scale, w.softmax_scale, grp.meta[r],
-                                  grp.workspace, grp.out_ranks[r], grp.lse_ranks[r], stream)
+            if grp.q_split is not None:
+                ops.partial_attention_split(g, grp.q_split, grp.q_scale, pools[r], w.kv_scale,
+                                            w.softmax_scale, grp.meta[r], grp.workspace,
+                                            grp.out_ranks[r], grp.lse_ranks[r], stream)
+            else:
+                ops.partial_attention(g, q, pools[r], w.kv_scale, w.softmax_scale, grp.meta[r],
+                                      grp.workspace, grp.out_ranks[r], grp.lse_ranks[r], stream)
             if events is not None:
                 events[r][1].record(stream)
             ops.merge_segments(g, grp.meta[r], grp.workspace, grp.out_ranks[r], grp.lse_ranks[r],

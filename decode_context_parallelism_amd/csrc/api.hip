@@ -159,7 +159,9 @@ int dcpmla_build_metadata(const dcpmla_geom *g, int32_t rank, const int32_t *ctx
   return hip_status(launch_build_metadata(*g, rank, ctx_lens, block_table, *m, stream));
 }
 
-static int attention_checks(const dcpmla_geom *g, const void *q, const void *kv_pool,
+// q_in: the query operand's buffers (the BF16 query, or the split query and
+// its scales)
+static int attention_checks(const dcpmla_geom *g, const Range *q_in, int n_q, const void *kv_pool,
                             const dcpmla_meta *m, const void *workspace, int64_t workspace_bytes,
                             const void *out_rank, const float *lse_rank, int *groups) {
   const int v = dcpmla_validate(g);
@@ -171,31 +173,53 @@ static int attention_checks(const dcpmla_geom *g, const void *q, const void *kv_
   if (workspace_bytes < ws_total_bytes(*groups, rows)) return DCPMLA_E_WORKSPACE;
   Range mr[5];
   meta_ranges(g, m, mr);
-  const Range ins[] = {{q, rows * kDqk * 2},
-                       {kv_pool, g->num_blocks * g->block_size * (int64_t)kDqk * elem_bytes(g)},
-                       mr[0], mr[1], mr[2], mr[4]};
+  Range ins[7] = {{kv_pool, g->num_blocks * g->block_size * (int64_t)kDqk * elem_bytes(g)},
+                 mr[0], mr[1], mr[2], mr[4]};
+  int n_in = 5;
+  for (int i = 0; i < n_q; ++i) ins[n_in++] = q_in[i];
   const Range outs[] = {{workspace, workspace_bytes}, {out_rank, rows * kDv * 2}, {lse_rank, rows * 4}};
-  if (any_alias(outs, 3, ins, 6)) return DCPMLA_E_ALIAS;
+  if (any_alias(outs, 3, ins, n_in)) return DCPMLA_E_ALIAS;
   // the error word is written too; it may not share memory with anything else
   const Range err_out[] = {mr[3]};
-  if (any_alias(err_out, 1, outs, 3) || any_alias(err_out, 1, ins, 6)) return DCPMLA_E_ALIAS;
+  if (any_alias(err_out, 1, outs, 3) || any_alias(err_out, 1, ins, n_in)) return DCPMLA_E_ALIAS;
   return DCPMLA_OK;
+}
+
+static bool scales_ok(float kv_scale, float softmax_scale) {
+  return kv_scale > 0.f && softmax_scale > 0.f && kv_scale != __builtin_huge_valf() &&
+         softmax_scale != __builtin_huge_valf();
 }
 
 int dcpmla_partial_attention(const dcpmla_geom *g, const void *q, const void *kv_pool,
                              float kv_scale, float softmax_scale, const dcpmla_meta *m,
                              void *workspace, int64_t workspace_bytes, void *out_rank,
                              float *lse_rank, hipStream_t stream) {
-  if (!q || !kv_pool) return DCPMLA_E_INVALID;
-  if (!(kv_scale > 0.f) || !(softmax_scale > 0.f) || kv_scale == __builtin_huge_valf() ||
-      softmax_scale == __builtin_huge_valf())
-    return DCPMLA_E_INVALID;
+  if (!q || !kv_pool || !g) return DCPMLA_E_INVALID;
+  if (!scales_ok(kv_scale, softmax_scale)) return DCPMLA_E_INVALID;
   int groups = 0;
-  const int c = attention_checks(g, q, kv_pool, m, workspace, workspace_bytes, out_rank, lse_rank,
+  const Range qr[] = {{q, (int64_t)g->batch * g->qlen * g->num_heads * kDqk * 2}};
+  const int c = attention_checks(g, qr, 1, kv_pool, m, workspace, workspace_bytes, out_rank, lse_rank,
                                  &groups);
   if (c != DCPMLA_OK) return c;
-  return hip_status(launch_partial_attention(*g, groups, q, kv_pool, kv_scale, softmax_scale, *m,
-                                             workspace, out_rank, lse_rank, stream));
+  return hip_status(launch_partial_attention(*g, groups, q, nullptr, nullptr, kv_pool, kv_scale,
+                                             softmax_scale, *m, workspace, out_rank, lse_rank, stream));
+}
+
+int dcpmla_partial_attention_split(const dcpmla_geom *g, const void *q_split, const float *q_inv_scale,
+                                   const void *kv_pool, float kv_scale, float softmax_scale,
+                                   const dcpmla_meta *m, void *workspace, int64_t workspace_bytes,
+                                   void *out_rank, float *lse_rank, hipStream_t stream) {
+  if (!q_split || !q_inv_scale || !kv_pool || !g) return DCPMLA_E_INVALID;
+  if (g->kv_dtype != DCPMLA_KV_FP8_E4M3) return DCPMLA_E_INVALID;
+  if (!scales_ok(kv_scale, softmax_scale)) return DCPMLA_E_INVALID;
+  int groups = 0;
+  const int64_t rows = (int64_t)g->batch * g->qlen * g->num_heads;
+  const Range qr[] = {{q_split, rows * kQSplitRow}, {q_inv_scale, rows * 4}};
+  const int c = attention_checks(g, qr, 2, kv_pool, m, workspace, workspace_bytes, out_rank, lse_rank,
+                                 &groups);
+  if (c != DCPMLA_OK) return c;
+  return hip_status(launch_partial_attention(*g, groups, nullptr, q_split, q_inv_scale, kv_pool, kv_scale,
+                                             softmax_scale, *m, workspace, out_rank, lse_rank, stream));
 }
 
 int dcpmla_merge_segments(const dcpmla_geom *g, const dcpmla_meta *m, const void *workspace,

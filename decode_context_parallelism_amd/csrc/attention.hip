@@ -881,6 +881,7 @@ hipError_t launch_tile(AttnArgs a, int groups, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_partial_attention(const dcpmla_geom &g, int groups, const void *q,
+                                    const void *q_split, const float *q_inv_scale,
                                     const void *kv_pool, float kv_scale, float softmax_scale,
                                     const dcpmla_meta &m, void *workspace, void *out_rank,
                                     float *lse_rank, hipStream_t stream) {
@@ -911,13 +912,19 @@ hipError_t launch_partial_attention(const dcpmla_geom &g, int groups, const void
   a.score_scale2 = softmax_scale * kv_scale * 1.44269504088896340736f;
   a.out_scale = kv_scale;
   const int64_t rows = (int64_t)g.batch * a.M;
-  a.qsplit = (const uint8_t *)workspace + ws_qsplit_off(groups);
-  a.qscale = (const float *)((const uint8_t *)workspace + ws_qscale_off(groups, rows));
   if (g.kv_dtype == DCPMLA_KV_FP8_E4M3) {
-    // the query as two E4M3 terms for the FP8 products, then the attention
-    const hipError_t e = launch_split_q(rows, q, (uint8_t *)workspace + ws_qsplit_off(groups),
-                                        (float *)((uint8_t *)workspace + ws_qscale_off(groups, rows)), stream);
-    if (e != hipSuccess) return e;
+    if (q_split) {
+      // the caller's split query
+      a.qsplit = (const uint8_t *)q_split;
+      a.qscale = q_inv_scale;
+    } else {
+      // the query as two E4M3 terms for the FP8 products, then the attention
+      a.qsplit = (const uint8_t *)workspace + ws_qsplit_off(groups);
+      a.qscale = (const float *)((const uint8_t *)workspace + ws_qscale_off(groups, rows));
+      const hipError_t e = launch_split_q(rows, q, (uint8_t *)workspace + ws_qsplit_off(groups),
+                                          (float *)((uint8_t *)workspace + ws_qscale_off(groups, rows)), stream);
+      if (e != hipSuccess) return e;
+    }
     if (g.q_format == DCPMLA_Q_FP8) return launch_tile<1, true>(a, groups, stream);
     return launch_tile<1, false>(a, groups, stream);
   }

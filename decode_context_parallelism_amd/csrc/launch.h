@@ -17,6 +17,7 @@ hipError_t launch_write_kv(const dcpmla_geom &g, int rank, int64_t num_tokens,
                            int32_t *err, hipStream_t stream);
 
 hipError_t launch_partial_attention(const dcpmla_geom &g, int groups, const void *q,
+                                    const void *q_split, const float *q_inv_scale,
                                     const void *kv_pool, float kv_scale, float softmax_scale,
                                     const dcpmla_meta &m, void *workspace, void *out_rank,
                                     float *lse_rank, hipStream_t stream);

@@ -12,6 +12,8 @@ Buffer layout (all contiguous, allocated once):
                read of an unwritten slot cannot go unnoticed
   meta[r]      verify view of rank r (see ``ops.RankMetadata``)
   workspace    split-KV partials, shared by the ranks in turn
+  q_split      FP8 cache: the query split once per forward into two E4M3
+  q_scale      terms and its per-row scale, read by every rank
   out_ranks    [W, B, qlen, H, 512] bfloat16, lse_ranks [W, B, qlen, H] float
   out, lse     merged result
 """
@@ -42,6 +44,11 @@ class DcpGroup:
         self.out = torch.empty(B, q, H, ops.D_V, dtype=torch.bfloat16, device=device)
         self.lse = torch.empty(B, q, H, dtype=torch.float32, device=device)
         self.kv_err = torch.zeros(1, dtype=torch.int32, device=device)
+        self.q_split = self.q_scale = None
+        if geom.kv_dtype == "fp8_e4m3":
+            rows = B * q * H
+            self.q_split = torch.empty(rows, 2 * ops.D_QK, dtype=torch.uint8, device=device)
+            self.q_scale = torch.empty(rows, dtype=torch.float32, device=device)
 
     def write_kv(self, seq_ids, positions, latents, block_table, stream=None):
         """Scatter global latent rows into every rank's pool; returns slot mappings [W, T]."""
@@ -63,11 +70,28 @@ class DcpGroup:
     def merge(self, stream=None):
         ops.merge_ranks(self.out_ranks, self.lse_ranks, self.out, self.lse, stream)
 
+    def rank_attention_split(self, r, kv_scale, softmax_scale, stream=None):
+        """Rank r's attention and segment merge on the query split by ``split_query``."""
+        ops.partial_attention_split(self.geom, self.q_split, self.q_scale, self.pools[r], kv_scale,
+                                    softmax_scale, self.meta[r], self.workspace, self.out_ranks[r],
+                                    self.lse_ranks[r], stream)
+        ops.merge_segments(self.geom, self.meta[r], self.workspace, self.out_ranks[r],
+                           self.lse_ranks[r], stream)
+
+    def split_query(self, q, stream=None):
+        ops.split_q(q, self.q_split, self.q_scale, stream)
+
     def forward(self, q, ctx_lens, block_table, kv_scale, softmax_scale, stream=None):
-        """One verification step: metadata, every rank's attention, cross-rank merge."""
+        """One verification step: metadata, every rank's attention, cross-rank merge.  With an
+        FP8 cache the query is split once and every rank reads the split."""
         self.build_metadata(ctx_lens, block_table, stream)
+        if self.q_split is not None:
+            self.split_query(q, stream)
         for r in range(self.geom.dcp_world):
-            self.rank_attention(r, q, kv_scale, softmax_scale, stream)
+            if self.q_split is not None:
+                self.rank_attention_split(r, kv_scale, softmax_scale, stream)
+            else:
+                self.rank_attention(r, q, kv_scale, softmax_scale, stream)
         self.merge(stream)
         return self.out, self.lse
 

@@ -182,6 +182,25 @@ def partial_attention(geom: Geometry, q, kv_pool, kv_scale: float, softmax_scale
            "dcpmla_partial_attention")
 
 
+def partial_attention_split(geom: Geometry, q_split, q_inv_scale, kv_pool, kv_scale: float,
+                            softmax_scale: float, meta: RankMetadata, workspace, out, lse,
+                            stream=None) -> None:
+    """``partial_attention`` with the query already split (``split_q`` output); FP8 cache only."""
+    rows = geom.batch * geom.qlen * geom.num_heads
+    _need(kv_pool, geom.kv_torch_dtype, (geom.num_blocks, geom.block_size, D_QK), "kv_pool")
+    _need(q_split, torch.uint8, (rows, 2 * D_QK), "q_split")
+    _need(q_inv_scale, torch.float32, (rows,), "q_inv_scale")
+    _need(out, torch.bfloat16, (geom.batch, geom.qlen, geom.num_heads, D_V), "out")
+    _need(lse, torch.float32, (geom.batch, geom.qlen, geom.num_heads), "lse")
+    g = geom.c()
+    m = meta.c()
+    _check(lib.dcpmla_partial_attention_split(ctypes.byref(g), _ptr(q_split), _ptr(q_inv_scale),
+                                              _ptr(kv_pool), kv_scale, softmax_scale, ctypes.byref(m),
+                                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                              _ptr(out), _ptr(lse), _stream(stream)),
+           "dcpmla_partial_attention_split")
+
+
 def merge_segments(geom: Geometry, meta: RankMetadata, workspace, out, lse, stream=None) -> None:
     _need(out, torch.bfloat16, (geom.batch, geom.qlen, geom.num_heads, D_V), "out")
     _need(lse, torch.float32, (geom.batch, geom.qlen, geom.num_heads), "lse")

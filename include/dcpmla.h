@@ -220,6 +220,23 @@ int dcpmla_partial_attention(const dcpmla_geom *geom, const void *q, const void 
                              float *lse_rank, hipStream_t stream);
 
 /*
+ * dcpmla_partial_attention() for an FP8 cache with the query given already
+ * split (dcpmla_split_q() output): q_split [B*qlen*H, 1152] bytes and
+ * q_inv_scale [B*qlen*H] float, device memory.  For a DCP group the split is
+ * done once per forward ("Context Parallel Guide", "How it works" item 4: the
+ * query is gathered once per decode step; each rank may split its own head
+ * slice before the gather, the split form having the size of the BF16
+ * query), and every rank's call reads it.  DCPMLA_E_INVALID with a BF16
+ * cache; other arguments, the workspace and the errors as in
+ * dcpmla_partial_attention().
+ */
+int dcpmla_partial_attention_split(const dcpmla_geom *geom, const void *q_split,
+                                   const float *q_inv_scale, const void *kv_pool, float kv_scale,
+                                   float softmax_scale, const dcpmla_meta *meta, void *workspace,
+                                   int64_t workspace_bytes, void *out_rank, float *lse_rank,
+                                   hipStream_t stream);
+
+/*
  * Segment merge (PR #51705, "Implementation" item 3 and commit message: the
  * base-2 statistics become a BF16 output plus a natural-log LSE):
  *   L2 = log2 sum_s 2^lse2_s,  O = sum_s 2^(lse2_s - L2) o_s,  LSE = L2 * ln 2

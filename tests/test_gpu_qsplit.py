@@ -70,3 +70,21 @@ def test_split_q_zero_rows_is_a_no_op():
     inv = torch.zeros((0,), dtype=torch.float32, device="cuda")
     ops.split_q(q, split, inv)
     torch.cuda.synchronize()
+
+
+def test_presplit_attention_equals_internal_split():
+    # dcpmla_partial_attention (splits the query itself) and
+    # dcpmla_partial_attention_split (reads the group's split) run the same
+    # arithmetic: their outputs must be identical
+    from synth import make_config
+    from gpu_util import run_group
+    ops = _ops()
+    w = make_config(2)
+    grp, d = run_group(w)
+    for r in range(w.world):
+        out = torch.empty_like(grp.out_ranks[r])
+        lse = torch.empty_like(grp.lse_ranks[r])
+        ops.rank_attention(grp.geom, d["q"], grp.pools[r], w.kv_scale, w.softmax_scale, grp.meta[r],
+                           grp.workspace, out, lse)
+        torch.cuda.synchronize()
+        assert torch.equal(out, grp.out_ranks[r]) and torch.equal(lse, grp.lse_ranks[r]), r

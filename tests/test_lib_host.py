@@ -126,6 +126,19 @@ def test_strerror():
 FAKE = 1 << 40   # host-only checks run before any device access
 
 
+def test_partial_attention_split_checks():
+    L = _lib.lib
+    m = _meta(FAKE + 10 ** 9)
+    wsb = ops.workspace_bytes(_geom(kv_dtype="fp8_e4m3"))
+    args = lambda g, **o: [ctypes.byref(g), o.get("qs", FAKE), o.get("qsc", FAKE + 10 ** 6), FAKE + 10 ** 7,
+                           1.0, 0.07, ctypes.byref(m), FAKE + 2 * 10 ** 7, wsb, FAKE + 4 * 10 ** 7,
+                           FAKE + 5 * 10 ** 7, None]
+    g8 = _geom(kv_dtype="fp8_e4m3").c()
+    assert L.dcpmla_partial_attention_split(*args(_geom(kv_dtype="bf16").c())) == _lib.E_INVALID  # FP8 only
+    assert L.dcpmla_partial_attention_split(*args(g8, qs=None)) == _lib.E_INVALID
+    assert L.dcpmla_partial_attention_split(*args(g8, qsc=FAKE + 4 * 10 ** 7 + 8)) == _lib.E_ALIAS  # scale in out
+
+
 def test_merge_ranks_alias_and_args():
     L = _lib.lib
     rows = 100

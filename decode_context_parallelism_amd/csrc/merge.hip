@@ -118,8 +118,9 @@ __global__ void __launch_bounds__(256) merge_segments_dense_kernel(
 // split over several workgroups, and give sequences with no rank-local token
 // their empty result.  Tiles finished inside one workgroup are left alone.
 // One workgroup per (sequence, tile, group of kMergeRows rows), one row per
-// wave; the partials of a row are requested kMergeBatch at a time so a row
-// costs few dependent memory round trips.
+// wave; the partials of a row are requested kMergeBatch at a time, their
+// base-2 LSEs with them, and merged against a running maximum, so a row costs
+// one dependent memory round trip per batch (no separate pass for the maximum).
 constexpr int kMergeRows = 4;
 constexpr int kMergeBatch = 8;
 
@@ -176,33 +177,47 @@ __global__ void __launch_bounds__(256) merge_segments_kernel(
   const int n = (int)(w1 - w0 + 1);
   auto src_of = [&](int k) { return (w0 + k) * kSlots + (k == 0 ? piece_slot(0) : piece_slot(1)); };
   const int pr0 = chunk * kMergeRows + wave;   // row index inside the tile (partial rows)
-  float mx = kNegInf;
-  for (int k = lane; k < n; k += 64) mx = fmaxf(mx, ws_lse2[src_of(k) * kTileRows + pr0]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  // One pass with a running maximum: each batch's base-2 LSEs and partial
+  // rows are requested together, the sums are rescaled when the maximum
+  // moves, so an item split into at most kMergeBatch parts costs one memory
+  // round trip.
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  float L = kNegInf;
-  if (mx > kNegInf) {
-    float z = 0.f;
-    for (int k = 0; k < n; k += kMergeBatch) {
-      float wgt[kMergeBatch];
-      float v[kMergeBatch][8];
+  float mx = kNegInf;
+  float z = 0.f;
+  for (int k = 0; k < n; k += kMergeBatch) {
+    float l[kMergeBatch];
+    float v[kMergeBatch][8];
+#pragma unroll
+    for (int q = 0; q < kMergeBatch; ++q) {
+      // entries past n repeat the last partial and are dropped below (a valid address)
+      const int kk = k + q < n ? k + q : n - 1;
+      const int64_t pr = src_of(kk) * kTileRows + pr0;
+      l[q] = k + q < n ? ws_lse2[pr] : kNegInf;
+      load_partial8(ws_o + pr * kDv, lane, v[q]);
+    }
+    float bm = kNegInf;
+#pragma unroll
+    for (int q = 0; q < kMergeBatch; ++q) bm = fmaxf(bm, l[q]);
+    if (bm > mx) {
+      // rescale what was summed against the old maximum (nothing when it was -inf)
+      const float c = mx > kNegInf ? fast_exp2(mx - bm) : 0.f;
+      z *= c;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] *= c;
+      mx = bm;
+    }
+    if (mx > kNegInf) {
 #pragma unroll
       for (int q = 0; q < kMergeBatch; ++q) {
-        // entries past n repeat the last partial with weight 0 (a valid address)
-        const int kk = k + q < n ? k + q : n - 1;
-        const int64_t pr = src_of(kk) * kTileRows + pr0;
-        const float l = ws_lse2[pr];
-        wgt[q] = (k + q < n && l > kNegInf) ? fast_exp2(l - mx) : 0.f;
-        load_partial8(ws_o + pr * kDv, lane, v[q]);
-      }
+        const float wgt = l[q] > kNegInf ? fast_exp2(l[q] - mx) : 0.f;
+        z += wgt;
 #pragma unroll
-      for (int q = 0; q < kMergeBatch; ++q) {
-        z += wgt[q];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += wgt[q] * v[q][e];
+        for (int e = 0; e < 8; ++e) acc[e] += wgt * v[q][e];
       }
     }
+  }
+  float L = kNegInf;
+  if (mx > kNegInf) {
     // fp16 partials carry o / kv_scale
     const float inv = (sizeof(PT) == 2 ? *ws_scale : 1.f) / z;
 #pragma unroll

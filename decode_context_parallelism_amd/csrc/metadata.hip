@@ -13,6 +13,37 @@
 
 namespace dcpmla {
 
+namespace {
+
+// Row i of sequence b: its global boundary, rank-local length and subpage
+// count, with the capacity clamps (before any block-id check).
+struct RowGeom {
+  int64_t len;
+  int np;
+  int err;
+};
+__device__ inline RowGeom row_geometry(int64_t ctx, int i, int W, int S, int qlen, int P, int ppb,
+                                       int max_blocks, int max_local_pages, int rank, int block_rows) {
+  int e = 0;
+  // global boundary of row i: causal verify, or the whole cache for a
+  // bidirectional draft block
+  int64_t g = block_rows ? ctx : ctx - qlen + 1 + i;
+  if (ctx < qlen) e |= DCPMLA_ERR_CTX_LT_QLEN;
+  if (g < 0) g = 0;
+  const int64_t span = (int64_t)W * S;
+  int64_t rem = g % span - (int64_t)rank * S;
+  rem = rem < 0 ? 0 : (rem > S ? S : rem);
+  int64_t len = (g / span) * S + rem;    // rank-local tokens visible to the row
+  int64_t np = (len + P - 1) / P;
+  const int64_t cap = (int64_t)max_blocks * ppb;
+  if (np > cap) { np = cap; e |= DCPMLA_ERR_TABLE_CAPACITY; }
+  if (np > max_local_pages) { np = max_local_pages; e |= DCPMLA_ERR_LOCAL_PAGES; }
+  if (len > np * P) len = np * P;
+  return RowGeom{len, (int)np, e};
+}
+
+}  // namespace
+
 __global__ void __launch_bounds__(256) meta_rows_kernel(
     int W, int S, int block_size, int qlen, int max_blocks, int max_local_pages,
     int64_t num_blocks, int rank, int block_rows, const int32_t *__restrict__ ctx_lens,
@@ -26,26 +57,12 @@ __global__ void __launch_bounds__(256) meta_rows_kernel(
   __shared__ int s_np, s_err, s_first_bad;
   __shared__ int64_t s_len;
   if (threadIdx.x == 0) {
-    const int64_t ctx = ctx_lens[b];
-    int e = 0;
-    // global boundary of row i: causal verify, or the whole cache for a
-    // bidirectional draft block
-    int64_t g = block_rows ? ctx : ctx - qlen + 1 + i;
-    if (ctx < qlen) e |= DCPMLA_ERR_CTX_LT_QLEN;
-    if (g < 0) g = 0;
-    const int64_t span = (int64_t)W * S;
-    int64_t rem = g % span - (int64_t)rank * S;
-    rem = rem < 0 ? 0 : (rem > S ? S : rem);
-    int64_t len = (g / span) * S + rem;    // rank-local tokens visible to the row
-    int64_t np = (len + P - 1) / P;
-    const int64_t cap = (int64_t)max_blocks * ppb;
-    if (np > cap) { np = cap; e |= DCPMLA_ERR_TABLE_CAPACITY; }
-    if (np > max_local_pages) { np = max_local_pages; e |= DCPMLA_ERR_LOCAL_PAGES; }
-    if (len > np * P) len = np * P;
-    s_np = (int)np;
-    s_len = len;
-    s_err = e;
-    s_first_bad = (int)np;
+    const RowGeom r = row_geometry(ctx_lens[b], i, W, S, qlen, P, ppb, max_blocks, max_local_pages,
+                                   rank, block_rows);
+    s_np = r.np;
+    s_len = r.len;
+    s_err = r.err;
+    s_first_bad = r.np;
   }
   __syncthreads();
   int np = s_np;
@@ -120,10 +137,109 @@ __global__ void __launch_bounds__(256) meta_work_kernel(int B, int qlen, int n_m
   for (int i = tid; i < kZeroInts; i += 256) work[work_zero_off(B) + i] = 0;
 }
 
+// Small verify views (rows * max_local_pages <= kSmallEntries, rows and
+// sequences <= kSmallThreads): the same per-row steps and the partition in
+// one workgroup, so the view costs one launch instead of two.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallEntries = 8192;
+
+__global__ void __launch_bounds__(kSmallThreads) meta_small_kernel(
+    int W, int S, int block_size, int qlen, int max_blocks, int max_local_pages, int64_t num_blocks,
+    int rank, int block_rows, int B, int n_mt, const int32_t *__restrict__ ctx_lens,
+    const int32_t *__restrict__ block_table, int32_t *__restrict__ row_len,
+    int32_t *__restrict__ page_table, int32_t *__restrict__ last_len, int32_t *__restrict__ err,
+    int32_t *__restrict__ work) {
+  __shared__ int s_np[kSmallThreads], s_len[kSmallThreads], s_first_bad[kSmallThreads];
+  __shared__ int s_scan[kSmallThreads];
+  __shared__ int s_err;
+  const int tid = threadIdx.x;
+  const int rows = B * qlen;
+  const int P = subpage_size(block_size);
+  const int ppb = block_size / P;
+  if (tid == 0) s_err = 0;
+  __syncthreads();
+  // per-row boundary, length and page count (one thread per row)
+  if (tid < rows) {
+    const int b = tid / qlen;
+    const RowGeom r = row_geometry(ctx_lens[b], tid - b * qlen, W, S, qlen, P, ppb, max_blocks,
+                                   max_local_pages, rank, block_rows);
+    s_np[tid] = r.np;
+    s_len[tid] = (int)r.len;   // <= max_local_pages * 128
+    s_first_bad[tid] = r.np;
+    if (r.err) atomicOr(&s_err, r.err);
+  }
+  __syncthreads();
+  // block ids each row uses, bounded by its page count
+  for (int idx = tid; idx < rows * max_local_pages; idx += kSmallThreads) {
+    const int row = idx / max_local_pages, j = idx - row * max_local_pages;
+    if (j < s_np[row]) {
+      const int32_t blk = block_table[(int64_t)(row / qlen) * max_blocks + j / ppb];
+      if (blk < 0 || (int64_t)blk >= num_blocks) atomicMin(&s_first_bad[row], j);
+    }
+  }
+  __syncthreads();
+  if (tid < rows) {
+    int np = s_np[tid];
+    if (s_first_bad[tid] < np) {
+      np = s_first_bad[tid];
+      atomicOr(&s_err, DCPMLA_ERR_BLOCK_ID);
+    }
+    const int len = min(s_len[tid], np * P);
+    s_np[tid] = np;
+    s_len[tid] = len;
+    row_len[tid] = len;
+    last_len[tid] = np ? len - (np - 1) * P : 0;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < rows * max_local_pages; idx += kSmallThreads) {
+    const int row = idx / max_local_pages, j = idx - row * max_local_pages;
+    int32_t v = -1;
+    if (j < s_np[row]) v = block_table[(int64_t)(row / qlen) * max_blocks + j / ppb] * ppb + (j % ppb);
+    page_table[idx] = v;
+  }
+  // the work partition (as meta_work_kernel), one thread per sequence
+  int units = 0;
+  if (tid < B) {
+    int lm = 0, lrow = tid * qlen + qlen - 1;
+    for (int i = 0; i < qlen; ++i) {
+      const int v = s_len[tid * qlen + i];
+      if (v > lm) { lm = v; lrow = tid * qlen + i; }
+    }
+    const int st = (lm + kStageTokens - 1) / kStageTokens;
+    work[work_lmax_off(B) + tid] = lm;
+    work[work_lrow_off(B) + tid] = lrow;
+    work[work_stages_off(B) + tid] = st;
+    units = st * n_mt;
+  }
+  s_scan[tid] = units;
+  __syncthreads();
+  for (int off = 1; off < kSmallThreads; off <<= 1) {
+    const int v = tid >= off ? s_scan[tid - off] : 0;
+    __syncthreads();
+    s_scan[tid] += v;
+    __syncthreads();
+  }
+  if (tid < B) work[work_unit_base_off() + tid] = s_scan[tid] - units;
+  if (tid == 0) {
+    work[work_unit_base_off() + B] = s_scan[kSmallThreads - 1];
+    work[0] = s_scan[kSmallThreads - 1];
+    if (s_err) atomicOr(err, s_err);
+  }
+  for (int i = tid; i < kZeroInts; i += kSmallThreads) work[work_zero_off(B) + i] = 0;
+}
+
 hipError_t launch_build_metadata(const dcpmla_geom &g, int rank, const int32_t *ctx_lens,
                                  const int32_t *block_table, const dcpmla_meta &m,
                                  hipStream_t stream) {
   const int rows = g.batch * g.qlen;
+  if (rows <= kSmallThreads && (int64_t)rows * g.max_local_pages <= kSmallEntries) {
+    hipLaunchKernelGGL(meta_small_kernel, dim3(1), dim3(kSmallThreads), 0, stream, g.dcp_world,
+                       g.interleave, g.block_size, g.qlen, g.max_blocks_per_seq, g.max_local_pages,
+                       g.num_blocks, rank, g.row_boundary == DCPMLA_BOUNDARY_BLOCK ? 1 : 0, g.batch,
+                       n_mtiles(g.qlen, g.num_heads), ctx_lens, block_table, m.row_local_len,
+                       m.page_table, m.last_page_len, m.err, m.work);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(meta_rows_kernel, dim3(rows), dim3(256), 0, stream, g.dcp_world,
                      g.interleave, g.block_size, g.qlen, g.max_blocks_per_seq, g.max_local_pages,
                      g.num_blocks, rank, g.row_boundary == DCPMLA_BOUNDARY_BLOCK ? 1 : 0, ctx_lens,

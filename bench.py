@@ -159,7 +159,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: every DCP rank is played in turn on a single MI355X; "
-              "runs on more than one GPU are not part of this build", file=sys.stderr)
+              "--gpus above 1 is not supported", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)

@@ -54,7 +54,7 @@ typedef enum {
   DCPMLA_E_INVALID = -1,     /* bad geometry, null pointer or out-of-range scalar */
   DCPMLA_E_ALIAS = -2,       /* an output buffer overlaps an input buffer */
   DCPMLA_E_WORKSPACE = -3,   /* workspace smaller than dcpmla_workspace_bytes() */
-  DCPMLA_E_UNSUPPORTED = -4, /* valid request this build does not implement */
+  DCPMLA_E_UNSUPPORTED = -4, /* valid request the library does not implement */
   DCPMLA_E_HIP = -5          /* a HIP runtime call failed (launch, attribute query) */
 } dcpmla_status;
 
@@ -340,7 +340,7 @@ const char *dcpmla_strerror(int status);
 
 /*
  * Device description used to state roofline peaks next to measurements (the
- * measurement of the segmented kernel is judged against the binding HBM or
+ * measurement of the segmented kernel is set against the binding HBM or
  * MFMA roofline; the peaks are the chip's, not the pages').  Fills *out for
  * HIP device `device`; DCPMLA_E_INVALID for a null pointer, DCPMLA_E_HIP if
  * the runtime cannot describe the device.  Host call, no kernel launch.

@@ -239,6 +239,18 @@ def main():
         for p in range(W):
             ops.a2a_combine(recv[p], comb_o[p], comb_l[p], stream)
 
+    def attention_launches(k):
+        stream = torch.cuda.current_stream()
+        pools, q = sets[k % n_sets]
+        for r in range(W):
+            if grp.q_split is not None:
+                ops.partial_attention_split(g, grp.q_split, grp.q_scale, pools[r], w.kv_scale,
+                                            w.softmax_scale, grp.meta[r], grp.workspace,
+                                            grp.out_ranks[r], grp.lse_ranks[r], stream)
+            else:
+                ops.partial_attention(g, q, pools[r], w.kv_scale, w.softmax_scale, grp.meta[r],
+                                      grp.workspace, grp.out_ranks[r], grp.lse_ranks[r], stream)
+
     def step(k, events=None):
         # launches go to the current stream (a capture stream while a graph is recorded)
         stream = torch.cuda.current_stream()
@@ -326,6 +338,33 @@ def main():
                               for k in range(args.steps)])
     avg_launch_ms = float(attn_ms.mean())
     per_rank_ms = attn_ms.mean(axis=0)
+    attn_timing = "HIP events around each eager launch"
+    if not args.no_graph:
+        # The roofline's launch duration: every rank's attention launch of a
+        # step captured back to back in one graph per input set, K replays
+        # bracketed by HIP events on the stream -- no host launch gap can
+        # stretch it (as the eager events can under a slow host).
+        attn_graphs = []
+        for i in range(n_sets):
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gph):
+                attention_launches(i)
+            attn_graphs.append(gph)
+        for k in range(args.warmup):
+            attn_graphs[k % n_sets].replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for k in range(args.steps):
+            attn_graphs[(args.warmup + k) % n_sets].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        avg_launch_ms = e0.elapsed_time(e1) / (args.steps * W)
+        # per-rank shares as measured by the eager events, scaled to this total
+        per_rank_ms = per_rank_ms * (avg_launch_ms * W / float(per_rank_ms.sum()))
+        attn_timing = ("HIP events around K replays of a graph of every rank's attention launch, "
+                       "back to back; per-rank split from the eager pass")
 
     # roofline of the attention kernel against the published peaks.  The
     # default path runs q.k as two E4M3 products on the FP8 units (twice the
@@ -353,7 +392,7 @@ def main():
     roof["traffic"] = traffic
     roof.update({
         "kernel": "attention_kernel (segmented split-KV MLA, one rank per launch)",
-        "avg_launch_ms": avg_launch_ms, "launches": int(attn_ms.size),
+        "avg_launch_ms": avg_launch_ms, "launches": int(attn_ms.size), "launch_timing": attn_timing,
         "algorithmic_flops_per_launch": sum(flops) / W,
         "algorithmic_bytes_per_launch": sum(alg_bytes) / W,
         "algorithmic_hbm_GBs": gbs,

@@ -89,6 +89,26 @@ struct AttnArgs {
   float out_scale;           // kv_scale
 };
 
+// This lane's index in the wave, read from the hardware at each call (a
+// volatile asm the compiler can neither hoist nor keep live across loops:
+// recomputing it is cheaper than a register held through the stage loop).
+__device__ inline int fresh_lane_id() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// The kernel's argument block as it sits in the kernel-argument segment.
+// Reading a field through this pointer is a scalar load; the empty asm makes
+// each call a fresh pointer, so the compiler re-reads the field where it is
+// used instead of holding it in registers across the kernel.
+typedef const __attribute__((address_space(4))) AttnArgs *KernargArgs;
+__device__ inline KernargArgs kernarg_args() {
+  KernargArgs p = (KernargArgs)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return p;
+}
+
 // LDS tile of one stage with E-byte elements: 36 blocks of [32 token slots]
 // [16 elements], 18 KiB (FP8) or 36 KiB (BF16); no padding (every access
 // pattern below covers whole 128-byte bank windows).
@@ -360,7 +380,7 @@ struct Staging {
 // reload's wait would then also wait for every store issued before it.
 template <int E, typename T>
 __device__ inline void store_rows(const floatx16 (&acc)[kDv / 32], float sc, uint8_t *stg, T *rows,
-                                  int nrows, int lane) {
+                                  int nrows) {
   constexpr int kRow = Staging<E>::kRowBytes;
   constexpr int kSegBytes = Staging<E>::kPassDims * (int)sizeof(T);
   constexpr int kLanesPerRow = kSegBytes / 16;
@@ -368,7 +388,7 @@ __device__ inline void store_rows(const floatx16 (&acc)[kDv / 32], float sc, uin
   constexpr int kRowBytes = kDv * (int)sizeof(T);
   // addresses derived from the lane are recomputed per call, not hoisted
   // out of the piece loop (where they would stay live through the stages)
-  asm volatile("" : "+v"(lane));
+  const int lane = fresh_lane_id();
   const int l32 = lane & 31, h = lane >> 5;
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(rows, (short)0, nrows > 0 ? nrows * kRowBytes : 0, kRawBufferFlags);
@@ -521,13 +541,21 @@ attention_kernel(AttnArgs a) {
   float sc2 = a.score_scale2;   // this lane's score scale (times 2^-k with a split query)
   // this lane's head-row of the piece at c, and the query row it loads
   auto load_q = [&](const Cursor &c) {
-    const int m = c.mt * kTileRows + wave * kWaveRows + l32;
-    const bool mvalid = m < a.M;
+    // lane-derived addresses are recomputed per piece: kept live across the
+    // piece loop they end up in scratch, and the reload's wait at the top of
+    // a piece would also wait for every load and store still in flight
+    const int ln = fresh_lane_id();
+    // the arguments it needs are read again from the kernel-argument segment
+    // (scalar loads), not kept in registers from the kernel's start
+    const KernargArgs ka = kernarg_args();
+    const int M = ka->M;
+    const int m = c.mt * kTileRows + wave * kWaveRows + (ln & 31);
+    const bool mvalid = m < M;
     // rows past M read row M-1 (a valid address) and are zeroed
-    const int64_t qr = (int64_t)c.b * a.M + (mvalid ? m : a.M - 1);
+    const int64_t qr = (int64_t)c.b * M + (mvalid ? m : M - 1);
     const uint32_t keep = mvalid ? 0xFFFFFFFFu : 0u;
     if constexpr (E == 1) {
-      const uint8_t *qrow = a.qsplit + qr * kQSplitRow + 32 * h;
+      const uint8_t *qrow = ka->qsplit + qr * kQSplitRow + 32 * (ln >> 5);
 #pragma unroll
       for (int t = 0; t < kDqk / 64; ++t) {
         q.v[2 * t] = cat8(*(const uint4 *)(qrow + 64 * t), *(const uint4 *)(qrow + 64 * t + 16));
@@ -537,12 +565,12 @@ attention_kernel(AttnArgs a) {
       for (int j = 0; j < 2 * (kDqk / 64); ++j)
 #pragma unroll
         for (int e = 0; e < 8; ++e) q.v[j][e] &= (int)keep;
-      sc2 = a.score_scale2 * a.qscale[qr];
+      sc2 = ka->score_scale2 * ka->qscale[qr];
     } else {
-      const uint16_t *qrow = a.q + qr * kDqk;
+      const uint16_t *qrow = ka->q + qr * kDqk;
 #pragma unroll
       for (int j = 0; j < kKBlocks; ++j) {
-        uint4 v = *(const uint4 *)(qrow + qdim_bf16(j, h));
+        uint4 v = *(const uint4 *)(qrow + qdim_bf16(j, ln >> 5));
         v.x &= keep; v.y &= keep; v.z &= keep; v.w &= keep;
         q.v[j] = v;
       }
@@ -560,12 +588,17 @@ attention_kernel(AttnArgs a) {
 
   int cur = 0;
   int64_t u = lo;
-
-  wait_direct_loads();
-  __syncthreads();
+  bool first_piece = true;
 
   while (true) {
     load_q(P);
+    if (first_piece) {
+      // the first tile and the first query rows are in flight together: one
+      // wait covers both, then the barrier hands the tile to every wave
+      wait_direct_loads();
+      __syncthreads();
+      first_piece = false;
+    }
     // per-piece softmax state; O^T accumulates in AGPRs
     floatx16 oacc[kDv / 32];
 #pragma unroll
@@ -578,10 +611,11 @@ attention_kernel(AttnArgs a) {
     const int b = P.b;
     const int mt = P.mt;
     const bool complete = P.st_begin == 0 && P.st_end == P.stages;
-    // this lane's head-row and its verify-row window
-    const int m = mt * kTileRows + wave * kWaveRows + l32;
+    // this lane's head-row and its verify-row window (lane and head count
+    // re-read here, for the reason given at kernarg_args)
+    const int m = mt * kTileRows + wave * kWaveRows + (fresh_lane_id() & 31);
     const bool mvalid = m < a.M;
-    const int vrow = mvalid ? m / a.H : 0;
+    const int vrow = mvalid ? m / kernarg_args()->H : 0;
     // rows past M (zero queries) see every token: their results are never
     // stored, and they keep the wave on the unmasked path
     const int rlen = mvalid ? row_len_at(b * a.qlen + vrow) : 0x3FFFFFFF;
@@ -827,10 +861,16 @@ attention_kernel(AttnArgs a) {
     // rows of this wave that exist (m < M)
     const int nrows = min(kWaveRows, a.M - (mt * kTileRows + wave * kWaveRows));
     uint8_t *stg = lds + 2 * Tile<E>::kBytes + wave * Staging<E>::kWaveBytes;
+    // output pointers are read where they are used (see kernarg_args): a
+    // copy kept from the kernel's start would be reloaded from scratch after
+    // the row stores, and that reload's wait would drain every store first
+    const KernargArgs ka = kernarg_args();
     if (complete) {
-      __bf16 *orow0 = (__bf16 *)a.out + ((int64_t)b * a.M + mt * kTileRows + wave * kWaveRows) * kDv;
-      store_rows<E>(oacc, inv, stg, orow0, nrows, lane);
-      if (mvalid && h == 0) a.lse[(int64_t)b * a.M + m] = has ? lse2 * kLn2 : kNegInf;
+      __bf16 *orow0 = (__bf16 *)ka->out + ((int64_t)b * a.M + mt * kTileRows + wave * kWaveRows) * kDv;
+      store_rows<E>(oacc, inv, stg, orow0, nrows);
+      if (mvalid && h == 0)
+        ka->lse[(int64_t)b * a.M + mt * kTileRows + wave * kWaveRows + (fresh_lane_id() & 31)] =
+            has ? lse2 * kLn2 : kNegInf;
     } else {
       // rows past M are never merged: no partial for them
       const int64_t prow0 = (w * kSlots + piece_slot(P.st_begin)) * kTileRows + wave * kWaveRows;
@@ -838,11 +878,11 @@ attention_kernel(AttnArgs a) {
         // fp16 partial of o / kv_scale: a weighted mean of E4M3 values, so
         // |value| <= 448 and fp16 keeps 11 significant bits of it
         const float invr = has ? 1.0f / ltot : 0.f;
-        store_rows<E>(oacc, invr, stg, (_Float16 *)a.ws_o + prow0 * kDv, nrows, lane);
+        store_rows<E>(oacc, invr, stg, (_Float16 *)ka->ws_o + prow0 * kDv, nrows);
       } else {
-        store_rows<E>(oacc, inv, stg, (float *)a.ws_o + prow0 * kDv, nrows, lane);
+        store_rows<E>(oacc, inv, stg, (float *)ka->ws_o + prow0 * kDv, nrows);
       }
-      if (mvalid && h == 0) a.ws_lse2[prow0 + l32] = lse2;
+      if (mvalid && h == 0) ka->ws_lse2[prow0 + (fresh_lane_id() & 31)] = lse2;
     }
     if (!more) break;
     P = following;

@@ -49,6 +49,11 @@ __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 }  // namespace
 
+// Ranks are taken kRankBatch at a time: the batch's LSEs and rows are
+// requested together and merged against a running maximum, so up to
+// kRankBatch ranks cost one memory round trip.
+constexpr int kRankBatch = 8;
+
 __global__ void __launch_bounds__(256) merge_ranks_kernel(int W, int64_t rows,
                                                           const uint4 *__restrict__ out_ranks,
                                                           const float *__restrict__ lse_ranks,
@@ -57,22 +62,43 @@ __global__ void __launch_bounds__(256) merge_ranks_kernel(int W, int64_t rows,
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
-  float mx = kNegInf;
-  for (int r = 0; r < W; ++r) mx = fmaxf(mx, lse_ranks[(int64_t)r * rows + row]);
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float mx = kNegInf;
+  float z = 0.f;
+  for (int r0 = 0; r0 < W; r0 += kRankBatch) {
+    float l[kRankBatch];
+    float v[kRankBatch][8];
+#pragma unroll
+    for (int q = 0; q < kRankBatch; ++q) {
+      // entries past W repeat the last rank (a valid address) and are dropped below
+      const int r = r0 + q < W ? r0 + q : W - 1;
+      l[q] = r0 + q < W ? lse_ranks[(int64_t)r * rows + row] : kNegInf;
+      unpack_bf16x8(out_ranks[((int64_t)r * rows + row) * 64 + lane], v[q]);
+    }
+    float bm = kNegInf;
+#pragma unroll
+    for (int q = 0; q < kRankBatch; ++q) bm = fmaxf(bm, l[q]);
+    if (bm > mx) {
+      // rescale what was summed against the old maximum (nothing when it was -inf)
+      const float c = mx > kNegInf ? fast_exp2((mx - bm) * kLog2e) : 0.f;
+      z *= c;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] *= c;
+      mx = bm;
+    }
+    if (mx > kNegInf) {
+#pragma unroll
+      for (int q = 0; q < kRankBatch; ++q) {
+        // an empty rank (LSE = -inf) adds nothing
+        const float w = l[q] > kNegInf ? fast_exp2((l[q] - mx) * kLog2e) : 0.f;
+        z += w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += w * v[q][e];
+      }
+    }
+  }
   float L = kNegInf;
   if (mx > kNegInf) {
-    float z = 0.f;
-    for (int r = 0; r < W; ++r) {
-      const float l = lse_ranks[(int64_t)r * rows + row];
-      if (!(l > kNegInf)) continue;
-      const float w = fast_exp2((l - mx) * kLog2e);
-      z += w;
-      float v[8];
-      unpack_bf16x8(out_ranks[((int64_t)r * rows + row) * 64 + lane], v);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] += w * v[k];
-    }
     const float inv = 1.f / z;
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[k] *= inv;

@@ -149,15 +149,18 @@ __global__ void __launch_bounds__(kSmallThreads) meta_small_kernel(
     const int32_t *__restrict__ block_table, int32_t *__restrict__ row_len,
     int32_t *__restrict__ page_table, int32_t *__restrict__ last_len, int32_t *__restrict__ err,
     int32_t *__restrict__ work) {
+  constexpr int kWaves = kSmallThreads / 64;
+  constexpr int kPerThread = kSmallEntries / kSmallThreads;
   __shared__ int s_np[kSmallThreads], s_len[kSmallThreads], s_first_bad[kSmallThreads];
-  __shared__ int s_scan[kSmallThreads];
+  __shared__ int s_row_err[kSmallThreads];
+  __shared__ int s_wave_sum[kWaves];
   __shared__ int s_err;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const int rows = B * qlen;
+  const int n_entries = rows * max_local_pages;
   const int P = subpage_size(block_size);
   const int ppb = block_size / P;
-  if (tid == 0) s_err = 0;
-  __syncthreads();
   // per-row boundary, length and page count (one thread per row)
   if (tid < rows) {
     const int b = tid / qlen;
@@ -166,24 +169,34 @@ __global__ void __launch_bounds__(kSmallThreads) meta_small_kernel(
     s_np[tid] = r.np;
     s_len[tid] = (int)r.len;   // <= max_local_pages * 128
     s_first_bad[tid] = r.np;
-    if (r.err) atomicOr(&s_err, r.err);
+    s_row_err[tid] = r.err;
   }
+  if (tid == 0) s_err = 0;
   __syncthreads();
-  // block ids each row uses, bounded by its page count
-  for (int idx = tid; idx < rows * max_local_pages; idx += kSmallThreads) {
-    const int row = idx / max_local_pages, j = idx - row * max_local_pages;
-    if (j < s_np[row]) {
-      const int32_t blk = block_table[(int64_t)(row / qlen) * max_blocks + j / ppb];
-      if (blk < 0 || (int64_t)blk >= num_blocks) atomicMin(&s_first_bad[row], j);
+  // block ids each row uses, bounded by its page count; each thread keeps
+  // the ids of its entries for the page table below (one read of the table)
+  int32_t blk[kPerThread];
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int idx = tid + k * kSmallThreads;
+    blk[k] = -1;
+    if (idx < n_entries) {
+      const int row = idx / max_local_pages, j = idx - row * max_local_pages;
+      if (j < s_np[row]) {
+        blk[k] = block_table[(int64_t)(row / qlen) * max_blocks + j / ppb];
+        if (blk[k] < 0 || (int64_t)blk[k] >= num_blocks) atomicMin(&s_first_bad[row], j);
+      }
     }
   }
   __syncthreads();
   if (tid < rows) {
     int np = s_np[tid];
+    int e = s_row_err[tid];
     if (s_first_bad[tid] < np) {
       np = s_first_bad[tid];
-      atomicOr(&s_err, DCPMLA_ERR_BLOCK_ID);
+      e |= DCPMLA_ERR_BLOCK_ID;
     }
+    if (e) atomicOr(&s_err, e);
     const int len = min(s_len[tid], np * P);
     s_np[tid] = np;
     s_len[tid] = len;
@@ -191,11 +204,13 @@ __global__ void __launch_bounds__(kSmallThreads) meta_small_kernel(
     last_len[tid] = np ? len - (np - 1) * P : 0;
   }
   __syncthreads();
-  for (int idx = tid; idx < rows * max_local_pages; idx += kSmallThreads) {
-    const int row = idx / max_local_pages, j = idx - row * max_local_pages;
-    int32_t v = -1;
-    if (j < s_np[row]) v = block_table[(int64_t)(row / qlen) * max_blocks + j / ppb] * ppb + (j % ppb);
-    page_table[idx] = v;
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int idx = tid + k * kSmallThreads;
+    if (idx < n_entries) {
+      const int row = idx / max_local_pages, j = idx - row * max_local_pages;
+      page_table[idx] = j < s_np[row] ? blk[k] * ppb + (j % ppb) : -1;
+    }
   }
   // the work partition (as meta_work_kernel), one thread per sequence
   int units = 0;
@@ -211,18 +226,27 @@ __global__ void __launch_bounds__(kSmallThreads) meta_small_kernel(
     work[work_stages_off(B) + tid] = st;
     units = st * n_mt;
   }
-  s_scan[tid] = units;
-  __syncthreads();
-  for (int off = 1; off < kSmallThreads; off <<= 1) {
-    const int v = tid >= off ? s_scan[tid - off] : 0;
-    __syncthreads();
-    s_scan[tid] += v;
-    __syncthreads();
+  // prefix sum of the units: inclusive within each wave by shuffles, then
+  // the waves' totals in order
+  int incl = units;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
   }
-  if (tid < B) work[work_unit_base_off() + tid] = s_scan[tid] - units;
+  if (lane == 63) s_wave_sum[wv] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    const int v = s_wave_sum[i];
+    before += i < wv ? v : 0;
+    total += v;
+  }
+  if (tid < B) work[work_unit_base_off() + tid] = before + incl - units;
   if (tid == 0) {
-    work[work_unit_base_off() + B] = s_scan[kSmallThreads - 1];
-    work[0] = s_scan[kSmallThreads - 1];
+    work[work_unit_base_off() + B] = total;
+    work[0] = total;
     if (s_err) atomicOr(err, s_err);
   }
   for (int i = tid; i < kZeroInts; i += kSmallThreads) work[work_zero_off(B) + i] = 0;

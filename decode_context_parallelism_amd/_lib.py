@@ -91,6 +91,7 @@ SIGNATURES = {
     "dcpmla_get_device_info": (ctypes.c_int, [_I32, ctypes.c_void_p]),
     "dcpmla_a2a_message_elems": (_I64, [_I32]),
     "dcpmla_split_q": (ctypes.c_int, [_I64, _P, _P, _P, _P]),
+    "dcpmla_split_q_bytes": (ctypes.c_int64, [_I64]),
     "dcpmla_partial_attention_split": (ctypes.c_int, [_G, _P, _P, _P, _F, _F, _M, _P, _I64, _P, _P, _P]),
     "dcpmla_a2a_pack": (ctypes.c_int, [_I32, _I64, _I32, _I32, _P, _P, _P, _P]),
     "dcpmla_a2a_combine": (ctypes.c_int, [_I32, _I64, _I32, _I32, _P, _P, _P, _P]),

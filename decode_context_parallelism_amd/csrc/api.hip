@@ -214,7 +214,7 @@ int dcpmla_partial_attention_split(const dcpmla_geom *g, const void *q_split, co
   if (!scales_ok(kv_scale, softmax_scale)) return DCPMLA_E_INVALID;
   int groups = 0;
   const int64_t rows = (int64_t)g->batch * g->qlen * g->num_heads;
-  const Range qr[] = {{q_split, rows * kQSplitRow}, {q_inv_scale, rows * 4}};
+  const Range qr[] = {{q_split, qsplit_bytes(rows)}, {q_inv_scale, rows * 4}};
   const int c = attention_checks(g, qr, 2, kv_pool, m, workspace, workspace_bytes, out_rank, lse_rank,
                                  &groups);
   if (c != DCPMLA_OK) return c;
@@ -279,11 +279,16 @@ int64_t dcpmla_a2a_message_elems(int32_t dim) {
   return (int64_t)dim + 8;
 }
 
+int64_t dcpmla_split_q_bytes(int64_t rows) {
+  if (rows < 0 || rows >= ((int64_t)1 << 40) / kQSplitRow) return DCPMLA_E_INVALID;
+  return qsplit_bytes(rows);
+}
+
 int dcpmla_split_q(int64_t rows, const void *q, void *q_split, float *inv_scale, hipStream_t stream) {
   if (rows < 0 || rows >= ((int64_t)1 << 40) / kQSplitRow) return DCPMLA_E_INVALID;
   if (rows > 0 && (!q || !q_split || !inv_scale)) return DCPMLA_E_INVALID;
   const Range ins[] = {{q, rows * kDqk * 2}};
-  const Range outs[] = {{q_split, rows * kQSplitRow}, {inv_scale, rows * 4}};
+  const Range outs[] = {{q_split, qsplit_bytes(rows)}, {inv_scale, rows * 4}};
   if (any_alias(outs, 2, ins, 1) || any_alias(outs, 1, outs + 1, 1)) return DCPMLA_E_ALIAS;
   return hip_status(launch_split_q(rows, q, q_split, inv_scale, stream));
 }

@@ -555,11 +555,16 @@ attention_kernel(AttnArgs a) {
     const int64_t qr = (int64_t)c.b * M + (mvalid ? m : M - 1);
     const uint32_t keep = mvalid ? 0xFFFFFFFFu : 0u;
     if constexpr (E == 1) {
-      const uint8_t *qrow = ka->qsplit + qr * kQSplitRow + 32 * (ln >> 5);
+      // tiled split: chunk 4t + 2 term + half holds this lane's 16 bytes at
+      // 16 (32 h + row % 32), so each load below reads one contiguous KiB
+      // across the wave (two runs when a wave's rows straddle a 32-row block)
+      const uint8_t *qrow = ka->qsplit + qsplit_off(qr, 0, ln >> 5);
 #pragma unroll
       for (int t = 0; t < kDqk / 64; ++t) {
-        q.v[2 * t] = cat8(*(const uint4 *)(qrow + 64 * t), *(const uint4 *)(qrow + 64 * t + 16));
-        q.v[2 * t + 1] = cat8(*(const uint4 *)(qrow + kDqk + 64 * t), *(const uint4 *)(qrow + kDqk + 64 * t + 16));
+        q.v[2 * t] = cat8(*(const uint4 *)(qrow + (4 * t) * kQSplitChunk),
+                          *(const uint4 *)(qrow + (4 * t + 1) * kQSplitChunk));
+        q.v[2 * t + 1] = cat8(*(const uint4 *)(qrow + (4 * t + 2) * kQSplitChunk),
+                              *(const uint4 *)(qrow + (4 * t + 3) * kQSplitChunk));
       }
 #pragma unroll
       for (int j = 0; j < 2 * (kDqk / 64); ++j)

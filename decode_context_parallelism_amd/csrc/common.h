@@ -57,13 +57,33 @@ __host__ __device__ inline int64_t ws_scale_off(int groups) {
 }
 __host__ __device__ inline int64_t ws_bytes(int groups) { return (ws_scale_off(groups) + 4) * 4; }
 
-// Then (256-byte aligned) the split query of an FP8-cache launch: per
-// head-row 576 E4M3 codes hi, then 576 codes lo, with q = (hi + lo) * 2^-k;
+// Then (256-byte aligned) the split query of an FP8-cache launch, q =
+// (hi + lo) * 2^-k with 576 E4M3 codes hi and 576 codes lo per head-row,
 // then one float 2^-k per head-row.
-constexpr int kQSplitRow = 2 * kDqk;
+//
+// The codes are tiled for the attention kernel's operand loads: rows go in
+// blocks of 32 (block n holds rows 32n .. 32n + 31), and a block is 36
+// chunks of 1 KiB.  Chunk c = 4t + 2 term + half (t < 9 the 64-dim step,
+// term 0 = hi, 1 = lo) holds, at bytes 16 (32 g + i) .. +15, the 16 codes of
+// row 32n + i, that term, dims 64t + 32g + 16 half .. +15 (g = 0, 1): the
+// bytes lane 32g + i of a wave needs for that step, so each of the wave's
+// query loads reads one contiguous KiB.  The last block is padded to 32
+// rows.
+constexpr int kQSplitRow = 2 * kDqk;                             // bytes per head-row
+constexpr int kQSplitBlockRows = 32;
+constexpr int kQSplitChunk = 1024;
+constexpr int kQSplitBlock = kQSplitBlockRows * kQSplitRow;      // 36 chunks
+__host__ __device__ inline int64_t qsplit_bytes(int64_t rows) {
+  return (rows + kQSplitBlockRows - 1) / kQSplitBlockRows * kQSplitBlock;
+}
+// byte offset of chunk c's 16 bytes for row `row`, lane half g
+__host__ __device__ inline int64_t qsplit_off(int64_t row, int c, int g) {
+  return (row / kQSplitBlockRows) * kQSplitBlock + (int64_t)c * kQSplitChunk +
+         (kQSplitBlockRows * g + row % kQSplitBlockRows) * 16;
+}
 __host__ __device__ inline int64_t ws_qsplit_off(int groups) { return ((ws_bytes(groups) + 255) / 256) * 256; }
 __host__ __device__ inline int64_t ws_qscale_off(int groups, int64_t rows) {
-  return ws_qsplit_off(groups) + rows * kQSplitRow;
+  return ws_qsplit_off(groups) + qsplit_bytes(rows);
 }
 __host__ __device__ inline int64_t ws_total_bytes(int groups, int64_t rows) {
   return ws_qscale_off(groups, rows) + rows * 4;

@@ -77,7 +77,9 @@ __device__ inline void split8(uint4 q, int k, uint2 &hi, uint2 &lo) {
 }  // namespace
 
 // One wave per head-row: lanes 0..63 hold dims 8*lane .. +7, lanes 0..7 also
-// dims 512 + 8*lane .. +7.
+// dims 512 + 8*lane .. +7.  Eight dims d = 8j .. 8j + 7 lie in one 16-byte
+// piece of the tiled layout: step t = j / 8, lane half g = j / 4 % 2, half
+// j / 2 % 2, byte 8 (j % 2) of the piece.
 __global__ void __launch_bounds__(256) split_q_kernel(int64_t rows, const uint4 *__restrict__ q,
                                                       uint8_t *__restrict__ split,
                                                       float *__restrict__ inv_scale) {
@@ -95,15 +97,19 @@ __global__ void __launch_bounds__(256) split_q_kernel(int64_t rows, const uint4 
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   const int k = row_exponent(amax);
-  uint8_t *dst = split + row * kQSplitRow;
+  // the hi and lo pieces of dims 8j .. 8j + 7
+  auto put = [&](int j, uint2 hi, uint2 lo) {
+    const int t = j >> 3, g = (j >> 2) & 1, half = (j >> 1) & 1;
+    const int64_t off = qsplit_off(row, 4 * t + half, g) + 8 * (j & 1);
+    *(uint2 *)(split + off) = hi;
+    *(uint2 *)(split + off + 2 * kQSplitChunk) = lo;
+  };
   uint2 hi, lo;
   split8(v0, k, hi, lo);
-  *(uint2 *)(dst + 8 * lane) = hi;
-  *(uint2 *)(dst + kDqk + 8 * lane) = lo;
+  put(lane, hi, lo);
   if (tail) {
     split8(v1, k, hi, lo);
-    *(uint2 *)(dst + 512 + 8 * lane) = hi;
-    *(uint2 *)(dst + kDqk + 512 + 8 * lane) = lo;
+    put(64 + lane, hi, lo);
   }
   if (lane == 0) inv_scale[row] = __builtin_ldexpf(1.0f, -k);
 }

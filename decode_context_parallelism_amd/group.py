@@ -47,7 +47,7 @@ class DcpGroup:
         self.q_split = self.q_scale = None
         if geom.kv_dtype == "fp8_e4m3":
             rows = B * q * H
-            self.q_split = torch.empty(rows, 2 * ops.D_QK, dtype=torch.uint8, device=device)
+            self.q_split = torch.empty(ops.split_q_bytes(rows), dtype=torch.uint8, device=device)
             self.q_scale = torch.empty(rows, dtype=torch.float32, device=device)
 
     def write_kv(self, seq_ids, positions, latents, block_table, stream=None):

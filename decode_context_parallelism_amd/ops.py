@@ -188,7 +188,7 @@ def partial_attention_split(geom: Geometry, q_split, q_inv_scale, kv_pool, kv_sc
     """``partial_attention`` with the query already split (``split_q`` output); FP8 cache only."""
     rows = geom.batch * geom.qlen * geom.num_heads
     _need(kv_pool, geom.kv_torch_dtype, (geom.num_blocks, geom.block_size, D_QK), "kv_pool")
-    _need(q_split, torch.uint8, (rows, 2 * D_QK), "q_split")
+    _need(q_split, torch.uint8, (split_q_bytes(rows),), "q_split")
     _need(q_inv_scale, torch.float32, (rows,), "q_inv_scale")
     _need(out, torch.bfloat16, (geom.batch, geom.qlen, geom.num_heads, D_V), "out")
     _need(lse, torch.float32, (geom.batch, geom.qlen, geom.num_heads), "lse")
@@ -264,11 +264,19 @@ def a2a_message_elems(dim: int) -> int:
     return n
 
 
+def split_q_bytes(rows: int) -> int:
+    """Bytes of the tiled split of ``rows`` head-rows (``dcpmla_split_q_bytes``)."""
+    n = int(lib.dcpmla_split_q_bytes(int(rows)))
+    _check(min(n, 0), "dcpmla_split_q_bytes")
+    return n
+
+
 def split_q(q, q_split, inv_scale, stream=None) -> None:
-    """``q [..., 576]`` bf16 -> ``q_split [rows, 1152]`` uint8 (hi codes, lo codes), ``inv_scale [rows]`` f32."""
+    """``q [..., 576]`` bf16 -> ``q_split [split_q_bytes(rows)]`` uint8 (hi and lo codes, tiled as
+    ``include/dcpmla.h`` describes), ``inv_scale [rows]`` f32."""
     rows = q.numel() // D_QK
     _need(q, torch.bfloat16, (*q.shape[:-1], D_QK), "q")
-    _need(q_split, torch.uint8, (rows, 2 * D_QK), "q_split")
+    _need(q_split, torch.uint8, (split_q_bytes(rows),), "q_split")
     _need(inv_scale, torch.float32, (rows,), "inv_scale")
     _check(lib.dcpmla_split_q(rows, _ptr(q), _ptr(q_split), _ptr(inv_scale), _stream(stream)), "dcpmla_split_q")
 

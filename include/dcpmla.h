@@ -221,8 +221,8 @@ int dcpmla_partial_attention(const dcpmla_geom *geom, const void *q, const void 
 
 /*
  * dcpmla_partial_attention() for an FP8 cache with the query given already
- * split (dcpmla_split_q() output): q_split [B*qlen*H, 1152] bytes and
- * q_inv_scale [B*qlen*H] float, device memory.  For a DCP group the split is
+ * split (dcpmla_split_q() output): q_split of dcpmla_split_q_bytes(B*qlen*H)
+ * bytes and q_inv_scale [B*qlen*H] float, device memory.  For a DCP group the split is
  * done once per forward ("Context Parallel Guide", "How it works" item 4: the
  * query is gathered once per decode step; each rank may split its own head
  * slice before the gather, the split form having the size of the BF16
@@ -261,11 +261,19 @@ int dcpmla_rank_attention(const dcpmla_geom *geom, const void *q, const void *kv
  * integer with max|q| * 2^k <= 448, hi the E4M3 code nearest x = q * 2^k
  * (ties to even) and lo the code nearest x - hi.  BF16 has 8 significant bits
  * and E4M3 4, so q = (hi + lo) * 2^-k exactly for |x| >= 2^-2, and within
- * 2^-10 * 2^-k below.  q [rows, 576] bf16 (device); q_split [rows, 1152]
- * bytes: 576 hi codes then 576 lo codes per row; inv_scale [rows] float =
- * 2^-k.  Outputs may not overlap q or each other (DCPMLA_E_ALIAS).
+ * 2^-10 * 2^-k below.  q [rows, 576] bf16 (device); inv_scale [rows] float =
+ * 2^-k; q_split dcpmla_split_q_bytes(rows) bytes holding the codes tiled for
+ * the attention kernel's loads: rows in blocks of 32 (the last block padded),
+ * each block 36 chunks of 1 KiB; chunk c = 4t + 2 term + half (t < 9, term 0
+ * = hi, 1 = lo, half < 2) holds at bytes 16 (32 g + i) .. +15 the codes of
+ * row 32 n + i of block n for dims 64t + 32g + 16 half .. +15 (g < 2).  The
+ * padding rows of the last block are not written.  Outputs may not overlap
+ * q or each other (DCPMLA_E_ALIAS).
  */
 int dcpmla_split_q(int64_t rows, const void *q, void *q_split, float *inv_scale, hipStream_t stream);
+
+/* Host only.  Bytes of q_split for `rows` head-rows (DCPMLA_E_INVALID if out of range). */
+int64_t dcpmla_split_q_bytes(int64_t rows);
 
 /*
  * Cross-rank LSE merge ("Context Parallel Guide", enable_project_before_merge:

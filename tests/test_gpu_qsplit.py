@@ -3,8 +3,10 @@
 The codes are integer output of the split: hi, lo and the per-row 2^-k must
 equal the float64 oracle's bit for bit (oracle/qsplit.py: round to nearest
 E4M3, ties to even, residual of the same, k the largest exponent that fits
-448).  The attention parity tests cover the split's use inside the FP8-cache
-attention on every workload.
+448).  The library stores the codes tiled for its attention kernel
+(include/dcpmla.h, dcpmla_split_q); the test undoes the tiling on the host
+before comparing.  The attention parity tests cover the split's use inside
+the FP8-cache attention on every workload.
 """
 import numpy as np
 import pytest
@@ -47,26 +49,50 @@ def _rows(seed):
     return np.concatenate(rows)
 
 
-def test_split_q_matches_oracle_bit_exact():
+def _untile(flat, R):
+    """Tiled split bytes -> (hi [R, 576], lo [R, 576]).  Block n, chunk c = 4t + 2 term + half,
+    bytes 16 (32 g + i) + e hold row 32 n + i, dim 64t + 32g + 16 half + e of that term."""
+    nb = (R + 31) // 32
+    a = flat.reshape(nb, 9, 2, 2, 2, 32, 16)          # n, t, term, half, g, i, e
+    a = a.transpose(0, 5, 2, 1, 4, 3, 6)              # n, i, term, t, g, half, e
+    a = a.reshape(nb * 32, 2, 576)[:R]
+    return a[:, 0], a[:, 1]
+
+
+def _padding_rows(flat, R):
+    """Bytes of the last block that belong to rows R .. (padding)."""
+    nb = (R + 31) // 32
+    a = flat.reshape(nb, 9, 2, 2, 2, 32, 16)
+    return a[nb - 1, :, :, :, :, R - 32 * (nb - 1):, :]
+
+
+@pytest.mark.parametrize("take", [None, 45])
+def test_split_q_matches_oracle_bit_exact(take):
+    # all 512 rows (whole blocks), and the first 45 (a ragged last block)
     ops = _ops()
     bits = _bf16_bits(_rows(3))
+    if take is not None:
+        bits = bits[np.r_[0:33, 500:512]]
     R = bits.shape[0]
     q = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
-    split = torch.full((R, 1152), 0x5A, dtype=torch.uint8, device="cuda")
+    split = torch.full((ops.split_q_bytes(R),), 0x5A, dtype=torch.uint8, device="cuda")
     inv = torch.full((R,), -1.0, dtype=torch.float32, device="cuda")
     ops.split_q(q, split, inv)
     torch.cuda.synchronize()
     hi_r, lo_r, inv_r = qsplit.split_rows(formats.decode_bf16(bits))
-    got = split.cpu().numpy()
-    assert np.array_equal(got[:, :576], hi_r), np.argwhere(got[:, :576] != hi_r)[:5]
-    assert np.array_equal(got[:, 576:], lo_r), np.argwhere(got[:, 576:] != lo_r)[:5]
+    flat = split.cpu().numpy()
+    hi, lo = _untile(flat, R)
+    assert np.array_equal(hi, hi_r), np.argwhere(hi != hi_r)[:5]
+    assert np.array_equal(lo, lo_r), np.argwhere(lo != lo_r)[:5]
     assert np.array_equal(inv.cpu().numpy().view(np.uint32), inv_r.astype(np.float32).view(np.uint32))
+    if R % 32:
+        assert (_padding_rows(flat, R) == 0x5A).all()   # padding rows are not written
 
 
 def test_split_q_zero_rows_is_a_no_op():
     ops = _ops()
     q = torch.zeros((0, 576), dtype=torch.bfloat16, device="cuda")
-    split = torch.zeros((0, 1152), dtype=torch.uint8, device="cuda")
+    split = torch.zeros((0,), dtype=torch.uint8, device="cuda")
     inv = torch.zeros((0,), dtype=torch.float32, device="cuda")
     ops.split_q(q, split, inv)
     torch.cuda.synchronize()

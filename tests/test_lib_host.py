@@ -100,12 +100,22 @@ def test_sizes():
     assert ops.work_ints(g) == 64 + 576 * 2 // 4
     ws = ops.workspace_bytes(g)
     # per group: 2 slots x 128 rows x (512 partial values + 1 lse2) floats; then a 16-byte scale
-    # slot; then, 256-byte aligned, per head-row 1152 bytes of split query and a float scale
+    # slot; then, 256-byte aligned, the split query (1152 bytes per head-row in blocks of 32
+    # rows, the last block padded) and a float scale per head-row
     part = 4 * 2 * 128 * (512 + 1) * 4 + 16
     rows = 5 * 3 * 16
-    assert ws == (part + 255) // 256 * 256 + rows * (1152 + 4)
+    split = (rows + 31) // 32 * 32 * 1152
+    assert ws == (part + 255) // 256 * 256 + split + rows * 4
     part1 = 1 * 2 * 128 * (512 + 1) * 4 + 16
-    assert ops.workspace_bytes(_geom(groups=1, batch=5)) == (part1 + 255) // 256 * 256 + rows * 1156
+    assert ops.workspace_bytes(_geom(groups=1, batch=5)) == (part1 + 255) // 256 * 256 + split + rows * 4
+
+
+def test_split_q_bytes():
+    # whole 32-row blocks of 36 KiB
+    assert [ops.split_q_bytes(r) for r in (0, 1, 31, 32, 33, 96, 97)] == \
+        [0, 36864, 36864, 36864, 73728, 110592, 147456]
+    assert _lib.lib.dcpmla_split_q_bytes(-1) == _lib.E_INVALID
+    assert _lib.lib.dcpmla_split_q_bytes(1 << 40) == _lib.E_INVALID
 
 
 def test_split_q_checks():

@@ -111,20 +111,25 @@ def test_large_configs_sampled(k):
     _compare_merged(w, grp, rows)
 
 
-def test_ragged_tiles_and_tiny_contexts():
+@pytest.mark.parametrize("kv_format,q_format", [("bf16", "split"), ("fp8_e4m3", "split"),
+                                                 ("fp8_e4m3", "fp8")])
+def test_ragged_tiles_and_tiny_contexts(kv_format, q_format):
     # M = 3 * 40 = 120 (one ragged tile); contexts down to qlen (first row sees one token);
-    # interleave 4 over 8 ranks leaves most ranks empty for short rows
+    # interleave 4 over 8 ranks leaves most ranks empty for short rows.  With an FP8 cache
+    # the sequences' head-rows start inside the split query's 32-row blocks (120 b), so
+    # a wave's query rows straddle two blocks
     ctx = np.array([3, 4, 5, 9, 33, 64, 65, 200, 1000])
     w = make_workload(name="ragged", world=8, interleave=4, batch=len(ctx), qlen=3, heads=40,
-                      block_size=16, kv_format="bf16", ctx=ctx, table="random",
+                      block_size=16, kv_format=kv_format, ctx=ctx, table="random",
                       max_local_pages=16, seed=77)
+    print(f"ragged tiles {kv_format} q_format {q_format}", flush=True)
     for groups in (0, 5):
-        grp, _ = run_group(w, groups=groups)
+        grp, _ = run_group(w, groups=groups, q_format=q_format)
         assert grp.errors() == 0
         rows = [(b, i) for b in range(w.batch) for i in range(w.qlen)]
         for r in range(w.world):
-            _compare_rank(w, grp, r, rows)
-        _compare_merged(w, grp, rows)
+            _compare_rank(w, grp, r, rows, q_format=q_format)
+        _compare_merged(w, grp, rows, q_format=q_format)
 
 
 def test_all_ranks_but_one_empty():

@@ -44,7 +44,10 @@ PEAK_MFMA_FP8_TFLOPS = 5000.0
 # flops per clock per CU of dense BF16 MFMA on gfx950 (4 SIMDs x 1024)
 BF16_FLOPS_PER_CLK_CU = 4096
 INFINITY_CACHE_BYTES = 256 << 20
-ATTN_SOURCE = os.path.join(ROOT, "decode_context_parallelism_amd", "csrc", "attention.hip")
+# sources that fix the attention kernel's code and work partition: the counter
+# summaries under profiles/ record their digest
+KERNEL_SOURCES = [os.path.join(ROOT, "decode_context_parallelism_amd", "csrc", f)
+                  for f in ("attention.hip", "common.h")]
 
 
 def parse():
@@ -92,8 +95,11 @@ def copy_calibration(mib):
 
 
 def source_digest():
-    with open(ATTN_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()
 
 
 def read_traffic(workload, digest):

@@ -98,10 +98,12 @@ __device__ inline int fresh_lane_id() {
   return l;
 }
 
-// The kernel's argument block as it sits in the kernel-argument segment.
-// Reading a field through this pointer is a scalar load; the empty asm makes
-// each call a fresh pointer, so the compiler re-reads the field where it is
-// used instead of holding it in registers across the kernel.
+// The kernel's argument block as it sits in the kernel-argument segment
+// (attention_kernel takes its AttnArgs by value as its only argument, so the
+// block starts at offset 0).  Reading a field through this pointer is a
+// scalar load; the empty asm makes each call a fresh pointer, so the compiler
+// re-reads the field where it is used instead of holding it in registers
+// across the kernel.
 typedef const __attribute__((address_space(4))) AttnArgs *KernargArgs;
 __device__ inline KernargArgs kernarg_args() {
   KernargArgs p = (KernargArgs)__builtin_amdgcn_kernarg_segment_ptr();

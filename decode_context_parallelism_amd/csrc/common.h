@@ -104,7 +104,10 @@ __host__ __device__ inline int64_t effective_groups(int64_t launched, int64_t U)
 
 // Scheduling cost.  Besides its stages, every (sequence, head-row tile) item
 // costs kPieceCost stage-equivalents for its query load and output stores,
-// which dominate when sequences are short.  Items are laid out on a cost
+// which dominate when sequences are short.  Measured, a piece's query load
+// and output stores take about 16-18k cycles against about 4k per stage;
+// every split piece pays them while the axis below charges them once per
+// item, and 5 measured best over the five workloads (6 and 4 were close).  Items are laid out on a cost
 // axis in (sequence, tile) order, each as kPieceCost of overhead followed by
 // its stages: item (b, mt) starts at
 //   item_cost(b, mt) = unit_base[b] + kPieceCost * n_mt * b + mt * (stages[b] + kPieceCost)
@@ -112,7 +115,7 @@ __host__ __device__ inline int64_t effective_groups(int64_t launched, int64_t U)
 // the units whose cost position lies in [w C / G, (w + 1) C / G) with
 // C = U + kPieceCost * n_mt * B.  Every group's cost range is non-empty
 // (G <= U <= C), but it may hold only overhead and so no unit.
-constexpr int64_t kPieceCost = 6;
+constexpr int64_t kPieceCost = 5;
 __host__ __device__ inline int64_t total_cost(int64_t U, int n_mt, int batch) {
   return U + kPieceCost * n_mt * (int64_t)batch;
 }

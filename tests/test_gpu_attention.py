@@ -132,6 +132,24 @@ def test_ragged_tiles_and_tiny_contexts(kv_format, q_format):
         _compare_merged(w, grp, rows, q_format=q_format)
 
 
+@pytest.mark.parametrize("B,qlen,kv_format", [(1024, 3, "bf16"), (5000, 1, "fp8_e4m3")])
+def test_partition_outside_lds(B, qlen, kv_format):
+    # batches whose work partition and row lengths do not fit in LDS next to the stage tiles and
+    # staging areas: the kernel reads them from global memory.  With more than 1024 verify rows
+    # the metadata also takes its two-kernel path.  Short contexts keep the oracle cheap
+    ctx = np.random.default_rng(5).integers(qlen, 120, B)
+    w = make_workload(name="bigbatch", world=2, interleave=1, batch=B, qlen=qlen, heads=8,
+                      block_size=16, kv_format=kv_format, ctx=ctx, table="shuffled",
+                      max_local_pages=8, seed=91)
+    print(f"partition outside LDS: B={B} qlen={qlen} {kv_format}", flush=True)
+    grp, _ = run_group(w)
+    assert grp.errors() == 0
+    rows = _sample_rows(w, 48, 93)
+    for r in range(w.world):
+        _compare_rank(w, grp, r, rows)
+    _compare_merged(w, grp, rows)
+
+
 def test_all_ranks_but_one_empty():
     # every context shorter than the interleave: only rank 0 owns tokens
     ctx = np.array([5, 8, 12, 16])

@@ -150,6 +150,24 @@ def test_partition_outside_lds(B, qlen, kv_format):
     _compare_merged(w, grp, rows)
 
 
+@pytest.mark.parametrize("block_size", [1, 48, 512])
+@pytest.mark.parametrize("kv_format", ["bf16", "fp8_e4m3"])
+def test_block_sizes(block_size, kv_format):
+    # subpage P = min(128, lowbit(block size)): P = 1 (a page per token, 32 page lookups per
+    # stage), P = 16 with three subpages per block, and P = 128
+    ctx = np.array([5, 300, 1100])
+    w = make_workload(name=f"bs{block_size}", world=2, interleave=1, batch=3, qlen=3, heads=16,
+                      block_size=block_size, kv_format=kv_format, ctx=ctx, table="random",
+                      max_local_pages=600, seed=95)
+    print(f"block size {block_size} {kv_format}", flush=True)
+    grp, _ = run_group(w)
+    assert grp.errors() == 0
+    rows = [(b, i) for b in range(w.batch) for i in range(w.qlen)]
+    for r in range(w.world):
+        _compare_rank(w, grp, r, rows)
+    _compare_merged(w, grp, rows)
+
+
 def test_all_ranks_but_one_empty():
     # every context shorter than the interleave: only rank 0 owns tokens
     ctx = np.array([5, 8, 12, 16])

@@ -168,6 +168,29 @@ def test_block_sizes(block_size, kv_format):
     _compare_merged(w, grp, rows)
 
 
+@pytest.mark.parametrize("world,interleave,heads,qlen,kv_format", [
+    (1, 1, 16, 3, "bf16"),       # no context parallelism: one rank owns every token
+    (3, 2, 1, 1, "fp8_e4m3"),    # M = 1: one valid head-row in the whole tile
+    (3, 1, 3, 7, "fp8_e4m3"),    # M = 21: odd world, rows straddle the split's 32-row blocks
+    (2, 1, 7, 2, "bf16"),
+])
+def test_degenerate_shapes(world, interleave, heads, qlen, kv_format):
+    ctx = np.array([qlen, qlen + 1, 40, 257, 700])
+    w = make_workload(name="degenerate", world=world, interleave=interleave, batch=len(ctx),
+                      qlen=qlen, heads=heads, block_size=16, kv_format=kv_format, ctx=ctx,
+                      table="random", max_local_pages=64, seed=97)
+    print(f"W={world} S={interleave} H={heads} q={qlen} {kv_format}", flush=True)
+    grp, _ = run_group(w)
+    assert grp.errors() == 0
+    rows = [(b, i) for b in range(w.batch) for i in range(w.qlen)]
+    for r in range(w.world):
+        _compare_rank(w, grp, r, rows)
+    _compare_merged(w, grp, rows)
+    if world == 1:
+        # the merge of a single rank returns that rank's result
+        assert torch.equal(grp.out, grp.out_ranks[0]) and torch.equal(grp.lse, grp.lse_ranks[0])
+
+
 def test_all_ranks_but_one_empty():
     # every context shorter than the interleave: only rank 0 owns tokens
     ctx = np.array([5, 8, 12, 16])

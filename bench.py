@@ -94,11 +94,37 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}))
 
 
+def code_only(text):
+    """C/C++ source without its comments, whitespace runs collapsed: edits to comments or layout
+    leave it unchanged, edits to code do not."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest():
+    """sha256 over the code (not the comments) of the attention kernel's sources."""
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
-            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + code_only(f.read()).encode())
     return h.hexdigest()
 
 

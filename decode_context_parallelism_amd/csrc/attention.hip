@@ -122,11 +122,10 @@ struct Tile {
   static constexpr int kLoads = kBytes / 1024;   // 1 KiB direct loads per stage
 };
 
-// token (within a 32-token stage) held by register r of a 32x32 accumulator
-// in lane half h: rows 8*(r/4) + 4*h + r%4 of the MFMA output tile.  The
-// same map assigns PV k-slot 8*h + e (e < 8) of token half kb to token
-// 16*kb + tau(h, e).
-__device__ inline int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+// Accumulator layout: register r of a 32x32 accumulator in lane half h holds
+// row 8*(r/4) + 4*h + r%4 of the MFMA output tile, so in the score tile it
+// holds that token of the stage.  The same map assigns PV k-slot 8*h + e
+// (e < 8) of token half kb to token 16*kb + tau(h, e).
 
 // LDS row slot of stage-token t (and, being an involution -- it swaps bits 2
 // and 3 -- the token of slot t).  The PV operand of lane half h gathers the

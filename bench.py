@@ -130,7 +130,19 @@ def source_digest():
 
 def read_traffic(workload, digest):
     """HBM bytes per attention launch from the committed counter summary, or None."""
-    path = os.path.join(ROOT, "profiles", f"attention_kernel_{workload}_hbm.md")
+    kv, src = read_summary(os.path.join(ROOT, "profiles", f"attention_kernel_{workload}_hbm.md"), digest)
+    if kv is None:
+        return None, src
+    try:
+        fetch = float(kv["fetch_kib_per_launch"]) * 1024 * float(kv["fetch_scale"])
+        write = float(kv["write_kib_per_launch"]) * 1024 * float(kv["write_scale"])
+    except KeyError:
+        return None, "counter summary incomplete"
+    return fetch + write, src
+
+
+def read_summary(path, digest):
+    """key: value lines of a committed counter summary, or (None, reason)."""
     if not os.path.exists(path):
         return None, "no counter summary"
     kv = {}
@@ -140,12 +152,24 @@ def read_traffic(workload, digest):
             kv[m.group(1)] = m.group(2)
     if kv.get("kernel_source_sha256") != digest:
         return None, "kernel changed since the counters were taken"
+    return kv, os.path.relpath(path, ROOT)
+
+
+def read_mfma_busy(workload, digest):
+    """Matrix-unit busy share and clock of the attention launch from the
+    committed counter summary (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE),
+    or None."""
+    kv, src = read_summary(os.path.join(ROOT, "profiles", f"attention_kernel_{workload}_mfma.md"), digest)
+    if kv is None:
+        return None, src
     try:
-        fetch = float(kv["fetch_kib_per_launch"]) * 1024 * float(kv["fetch_scale"])
-        write = float(kv["write_kib_per_launch"]) * 1024 * float(kv["write_scale"])
+        busy = {"mfma_busy_frac": float(kv["mfma_busy_frac"]), "clock_ghz": float(kv["clock_ghz"])}
     except KeyError:
         return None, "counter summary incomplete"
-    return fetch + write, os.path.relpath(path, ROOT)
+    if "mfma_busy_frac_at_2_4_ghz" in kv:
+        busy["mfma_busy_frac_at_2_4_ghz"] = float(kv["mfma_busy_frac_at_2_4_ghz"])
+    busy["source"] = src
+    return busy, src
 
 
 def cpu_baseline(w, seconds):
@@ -431,6 +455,9 @@ def main():
         "traffic_source": traffic_src,
         "kernel_source_sha256": digest,
     })
+    # the matrix units' measured busy share of the launch, at the clock they ran
+    busy, busy_src = read_mfma_busy(w.name, digest)
+    roof["mfma_busy_counters"] = busy if busy is not None else busy_src
 
     clk_ghz = dev_info["clock_khz"] / 1e6
     device = dict(dev_info)

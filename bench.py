@@ -72,6 +72,10 @@ def parse():
                     help="cross-rank combine: direct LSE merge of all partials (default); a2a pack, "
                          "exchange and local combine; or pbm (project each partial through a "
                          "synthetic W_V [H, 512 -> 128] before the a2a)")
+    ap.add_argument("--streams", type=int, choices=(1, 2), default=2,
+                    help="streams of the replayed step: 2 issues the query split and the odd ranks on a "
+                         "second stream, each stream with its own split-KV workspace, so independent "
+                         "launches overlap (default); 1 issues everything in order on one stream")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of replaying the step as a captured HIP graph")
     ap.add_argument("--no-rotate", action="store_true",
@@ -370,11 +374,21 @@ def main():
         # the work is identical, the host launch overhead between the short
         # kernels is gone.  The per-launch kernel durations above come from
         # the eager pass.
+        side = torch.cuda.Stream()
+
+        def step_replayed(k):
+            if args.streams == 1:
+                step(k)
+                return
+            pools, q = sets[k % n_sets]
+            grp.ranks_two_streams(q, ctx, bt, w.kv_scale, w.softmax_scale, side, pools=pools)
+            combine()
+
         graphs = []
         for i in range(n_sets):
             gph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gph):
-                step(i)
+                step_replayed(i)
             graphs.append(gph)
         for k in range(args.warmup):
             graphs[k % n_sets].replay()
@@ -387,7 +401,9 @@ def main():
         if grp.errors() != 0:
             raise RuntimeError(f"device error word {grp.errors():#x}")
         ms_per_step = (t1 - t0) * 1e3 / args.steps
-        step_mode = "HIP graph replay (one captured graph per input set)"
+        step_mode = ("HIP graph replay (one captured graph per input set); " +
+                     ("two streams: the query split and the odd ranks on the second, each stream "
+                      "with its own split-KV workspace" if args.streams == 2 else "one stream"))
     attn_ms = np.array([[events[k][r][0].elapsed_time(events[k][r][1]) for r in range(W)]
                         for k in range(args.steps)])
     attn_merge_ms = np.array([[events[k][r][0].elapsed_time(events[k][r][2]) for r in range(W)]
@@ -488,7 +504,8 @@ def main():
                    "batch": w.batch, "qlen": w.qlen, "heads": w.heads,
                    "block_size": w.block_size, "kv_cache": w.kv_format,
                    "kv_tokens_per_step": kv_tokens, "ranks_per_step": W, "input_sets": n_sets,
-                   "row_boundary": args.row_boundary, "merge": args.merge, "q_format": args.q_format},
+                   "row_boundary": args.row_boundary, "merge": args.merge, "q_format": args.q_format,
+                   "streams": 1 if args.no_graph else args.streams},
         "verify_rows_per_s": w.batch * w.qlen / (ms_per_step * 1e-3),
         "step_mode": step_mode,
         "ms_per_step_eager": ms_per_step_eager,

@@ -1,9 +1,10 @@
 """One GPU playing every rank of a DCP group.
 
-Each rank keeps its own KV pool and verify-view buffers in HBM; the ranks run
-one after another on one stream (KV write, metadata, segmented attention and
-segment merge per rank), and the cross-rank LSE merge then reads all W
-partials from HBM.  In a real deployment each rank is a different GPU and the
+Each rank keeps its own KV pool and verify-view buffers in HBM; ``forward``
+runs the ranks one after another on one stream (KV write, metadata, segmented
+attention and segment merge per rank), and the cross-rank LSE merge then reads
+all W partials from HBM.  ``ranks_two_streams`` issues the same launches over
+two streams, so independent work overlaps.  In a real deployment each rank is a different GPU and the
 merge input arrives through an all-to-all; the per-rank work is identical.
 
 Buffer layout (all contiguous, allocated once):
@@ -11,7 +12,8 @@ Buffer layout (all contiguous, allocated once):
                or bfloat16), filled with a NaN pattern until written, so a
                read of an unwritten slot cannot go unnoticed
   meta[r]      verify view of rank r (see ``ops.RankMetadata``)
-  workspace    split-KV partials, shared by the ranks in turn
+  workspace    split-KV partials, shared by the ranks in turn (workspace2: the
+               second stream's, for ``ranks_two_streams``)
   q_split      FP8 cache: the query split once per forward into two E4M3
   q_scale      terms and its per-row scale, read by every rank
   out_ranks    [W, B, qlen, H, 512] bfloat16, lse_ranks [W, B, qlen, H] float
@@ -39,6 +41,7 @@ class DcpGroup:
             self.pools.append(pool)
         self.meta = [ops.RankMetadata(geom, device) for _ in range(W)]
         self.workspace = ops.alloc_workspace(geom, device)
+        self.workspace2 = ops.alloc_workspace(geom, device)
         self.out_ranks = torch.empty(W, B, q, H, ops.D_V, dtype=torch.bfloat16, device=device)
         self.lse_ranks = torch.empty(W, B, q, H, dtype=torch.float32, device=device)
         self.out = torch.empty(B, q, H, ops.D_V, dtype=torch.bfloat16, device=device)
@@ -93,6 +96,50 @@ class DcpGroup:
             else:
                 self.rank_attention(r, q, kv_scale, softmax_scale, stream)
         self.merge(stream)
+        return self.out, self.lse
+
+    def ranks_two_streams(self, q, ctx_lens, block_table, kv_scale, softmax_scale, side,
+                          pools=None):
+        """Metadata, query split, attention and segment merge of every rank, issued over two
+        streams: the current stream takes the even ranks, ``side`` the query split and the odd
+        ranks, each stream with its own split-KV workspace.  The launches and their inputs are
+        those of ``forward``; only independent work overlaps (the query split beside rank 0's
+        metadata, one stream's attention beside the other's, a segment merge beside the other
+        stream's attention).  On return the current stream waits for ``side``, so what is
+        issued next on it (the cross-rank merge) sees every rank's result.  Capturable into a
+        HIP graph (the fork and the join become graph edges).  ``pools`` replaces the KV pools
+        (the bench rotates input copies)."""
+        main = torch.cuda.current_stream()
+        pools = self.pools if pools is None else pools
+        streams = (main, side)
+        work = (self.workspace, self.workspace2)
+        W = self.geom.dcp_world
+        side.wait_stream(main)
+        split_done = None
+        if self.q_split is not None:
+            ops.split_q(q, self.q_split, self.q_scale, side)
+            split_done = torch.cuda.Event()
+            split_done.record(side)
+        for r in range(W):
+            ops.build_metadata(self.geom, r, ctx_lens, block_table, self.meta[r], streams[r % 2])
+        if split_done is not None:
+            main.wait_event(split_done)
+        for r in range(W):
+            s, ws = streams[r % 2], work[r % 2]
+            if self.q_split is not None:
+                ops.partial_attention_split(self.geom, self.q_split, self.q_scale, pools[r],
+                                            kv_scale, softmax_scale, self.meta[r], ws,
+                                            self.out_ranks[r], self.lse_ranks[r], s)
+            else:
+                ops.partial_attention(self.geom, q, pools[r], kv_scale, softmax_scale,
+                                      self.meta[r], ws, self.out_ranks[r], self.lse_ranks[r], s)
+            ops.merge_segments(self.geom, self.meta[r], ws, self.out_ranks[r], self.lse_ranks[r], s)
+        main.wait_stream(side)
+
+    def forward_two_streams(self, q, ctx_lens, block_table, kv_scale, softmax_scale, side):
+        """``forward`` with the ranks issued by ``ranks_two_streams``."""
+        self.ranks_two_streams(q, ctx_lens, block_table, kv_scale, softmax_scale, side)
+        self.merge()
         return self.out, self.lse
 
     def errors(self):

@@ -39,3 +39,46 @@ def test_step_graph_replays_match_eager(k):
         torch.cuda.synchronize()
         assert torch.equal(grp.out, ref[0]) and torch.equal(grp.lse, ref[1])
     assert grp.errors() == 0
+
+
+@pytest.mark.parametrize("k", [1, 2, 4])
+def test_two_stream_step_matches_one_stream(k):
+    """The ranks issued over two streams (the query split and the odd ranks on a second
+    stream with its own split-KV workspace), eagerly and as replays of a captured graph,
+    give the one-stream forward's result bit for bit: the launches and their inputs are the
+    same, only their order across streams differs."""
+    w = make_config(k)
+    print(f"config {k}: {w.name} two-stream step", flush=True)
+    grp, d = run_group(w)
+    ref = [t.clone() for t in (grp.out, grp.lse, grp.out_ranks, grp.lse_ranks)]
+    side = torch.cuda.Stream()
+    args = (d["q"], d["ctx_lens"], d["block_table"], w.kv_scale, w.softmax_scale)
+
+    def clear():
+        for t in (grp.out, grp.out_ranks):
+            t.fill_(float("nan"))
+        grp.lse.zero_()
+        grp.lse_ranks.zero_()
+        torch.cuda.synchronize()
+
+    def check(tag):
+        for got, want in zip((grp.out, grp.lse, grp.out_ranks, grp.lse_ranks), ref):
+            assert torch.equal(got, want), (k, tag)
+
+    clear()
+    grp.forward_two_streams(*args, side)
+    torch.cuda.synchronize()
+    check("eager")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        grp.forward_two_streams(*args, side)
+    for i in range(3):
+        clear()
+        graph.replay()
+        torch.cuda.synchronize()
+        check(f"replay {i}")
+        # a one-stream eager step between replays
+        grp.forward(*args)
+        torch.cuda.synchronize()
+        check(f"eager after replay {i}")
+    assert grp.errors() == 0

@@ -55,8 +55,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2,
-                    help="workload 1..5 (default 2: dcp=2, qlen=3, 96 heads, batch 8, FP8 KV)")
+    ap.add_argument("--config", type=int, default=5,
+                    help="workload 1..5 (default 5, the largest: dcp=8, 1,048,576-token contexts, "
+                         "batch 4, qlen 3, 128 heads, FP8 KV)")
     ap.add_argument("--groups", type=int, default=0,
                     help="persistent workgroups of the attention kernel (0: one per compute unit)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -176,42 +177,74 @@ def read_mfma_busy(workload, digest):
     return busy, src
 
 
+def host_cpu():
+    """Host cores this process may run on, the machine's count, and the CPU model."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return usable, os.cpu_count() or usable, model
+
+
 def cpu_baseline(w, seconds):
-    """Time the float64 oracle on this host: each rank's partial attention over
-    whole sequences, ranks and sequences in order, repeated until the budget is
-    spent (at least one (rank, sequence) pair)."""
+    """Time the float64 oracle on this host, as it stands: verify rows taken in
+    order (sequence-major), each computed twice -- global causal attention over
+    the whole visible prefix, and the per-rank split (every rank's partial
+    over the positions it owns) plus the LSE merge -- until the time budget is
+    spent (at least one row).  A row is credited ctx/qlen of its sequence's KV
+    tokens, so the rates are in the metric's unit: global KV tokens of a full
+    step per second."""
+    import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import attention as A
-    from oracle import formats, layout
+    from oracle import formats
 
     q = formats.decode_bf16(w.q_bits)
     lat = lambda b, pos: formats.decode_cache(w.kv[w.seq_start[b] + pos], w.kv_format, w.kv_scale)
-    tokens = 0
-    pairs = 0
-    t0 = time.perf_counter()
-    done = False
-    while not done:
-        for r in range(w.world):
-            for b in range(w.batch):
-                rows = [(b, i) for i in range(w.qlen)]
-                A.verify_attention(q, lat, w.ctx_lens, w.softmax_scale, world=w.world,
-                                   interleave=w.interleave, rank=r, rows=rows)
-                g_last = layout.verify_row_boundary(int(w.ctx_lens[b]), w.qlen, w.qlen - 1)
-                tokens += layout.rank_local_positions(g_last, w.world, w.interleave, r).shape[0]
-                pairs += 1
-                if time.perf_counter() - t0 > seconds:
-                    done = True
-                    break
-            if done:
+    t_glob = t_split = 0.0
+    credited = 0.0
+    done = []
+    for b in range(w.batch):
+        for i in range(w.qlen):
+            rows = [(b, i)]
+            t0 = time.perf_counter()
+            A.verify_attention(q, lat, w.ctx_lens, w.softmax_scale, rows=rows)
+            t1 = time.perf_counter()
+            parts = [A.verify_attention(q, lat, w.ctx_lens, w.softmax_scale, world=w.world,
+                                        interleave=w.interleave, rank=r, rows=rows)
+                     for r in range(w.world)]
+            A.merge_ranks(np.stack([p[0][b, i] for p in parts]), np.stack([p[1][b, i] for p in parts]))
+            t2 = time.perf_counter()
+            t_glob += t1 - t0
+            t_split += t2 - t1
+            credited += float(w.ctx_lens[b]) / w.qlen
+            done.append((b, i))
+            if t_glob + t_split > seconds:
                 break
-    dt = time.perf_counter() - t0
+        if t_glob + t_split > seconds:
+            break
     threads = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-    return {"value": tokens / dt, "unit": "KV tokens/s", "cores": int(max(threads) if threads else 1),
-            "kind": "oracle",
-            "sample": f"float64 oracle (numpy BLAS), per-rank partial attention of {pairs} (rank, sequence) "
-                      f"pairs taken in order over {w.world} ranks x {w.batch} sequences, all {w.qlen} verify "
-                      f"rows x {w.heads} heads each: {tokens} rank-local KV tokens in {dt:.1f} s"}
+    usable, machine, model = host_cpu()
+    return {"value": credited / t_split, "unit": "KV tokens/s",
+            "cores": int(max(threads) if threads else 1), "kind": "oracle",
+            "host_cores_usable": usable, "host_cores_machine": machine, "cpu_model": model,
+            "global_attention": {"value": credited / t_glob, "unit": "KV tokens/s", "seconds": t_glob},
+            "split_and_merge": {"value": credited / t_split, "unit": "KV tokens/s", "seconds": t_split},
+            "sample": f"float64 oracle (numpy, BLAS threads = cores), {len(done)} verify row(s) of "
+                      f"{w.name} taken in order from (sequence {done[0][0]}, row {done[0][1]}), all "
+                      f"{w.heads} heads each: global causal attention {t_glob:.1f} s, the {w.world} ranks' "
+                      f"partials plus the LSE merge {t_split:.1f} s; each row credited ctx/qlen KV tokens; "
+                      f"value = the split-and-merge rate"}
 
 
 def main():

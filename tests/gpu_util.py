@@ -6,7 +6,8 @@ computes any part of the method.
 import numpy as np
 import torch
 
-from oracle import formats
+from oracle import attention as A
+from oracle import formats, layout, parity
 
 HAS_GPU = torch.cuda.is_available()
 
@@ -69,33 +70,139 @@ def bf16_to_f64(t):
 
 
 def tolerance(w):
-    """Arithmetic max-abs tolerance: 1.5e-2 with an FP8 cache, 5e-3 with BF16."""
+    """Arithmetic max-abs bar on outputs: 1.5e-2 with an FP8 cache, 5e-3 with BF16."""
     return 1.5e-2 if w.kv_format == "fp8_e4m3" else 5e-3
 
 
-def bf16_half_ulp(x):
-    """Half a BF16 ulp at |x|: the error of a correctly rounded BF16 value.
-
-    BF16 keeps 8 significant bits, so a value in [2^e, 2^(e+1)) is stored to
-    within 2^(e-8).  For |x| >= 2 that is 7.8e-3 or more, above the 5e-3 bar
-    itself; the output tolerance is therefore the arithmetic bar plus the
-    output format's own rounding.
-    """
-    ax = np.abs(np.asarray(x, dtype=np.float64))
-    e = np.floor(np.log2(np.maximum(ax, 2.0 ** -126)))
-    return np.ldexp(1.0, (e - 8).astype(np.int64))
-
-
-def output_bound(w, exact, rank_exact=None, rank_weights=None):
-    """Per-element bound for a BF16 output against the exact float64 value.
-
-    ``rank_exact``/``rank_weights`` ([W, ...]): for a merged output, each rank's
-    BF16-rounded partial adds its half-ulp times its merge weight.
-    """
-    bound = tolerance(w) + bf16_half_ulp(exact)
-    if rank_exact is not None:
-        bound = bound + (np.asarray(rank_weights)[..., None] * bf16_half_ulp(rank_exact)).sum(axis=0)
-    return bound
-
-
 LSE_TOL = 1e-3
+
+
+def bf16_half_ulp(x):
+    """Half a BF16 ulp at |x| (the projection bound of the exchange tests)."""
+    return formats.bf16_quantum(x) / 2
+
+
+def rank_expectations(w, rows, q_format="split", boundary=layout.verify_row_boundary, ranks=None):
+    """Exact float64 per-rank partials ``(o[W, B, qlen, H, 512], l[W, B, qlen, H])``
+    of the selected rows from the oracle (rows not selected, and ranks not in
+    ``ranks``, are NaN).
+
+    The oracle attends row by row; the windows of one sequence's rows on one
+    rank are prefixes of one another, so each (sequence, rank) is decoded once,
+    for its longest window, and shorter windows read a prefix of it.
+    """
+    q = oracle_q(w, q_format)
+    ranks = range(w.world) if ranks is None else ranks
+    B, ql, H = w.batch, w.qlen, w.heads
+    o = np.full((w.world, B, ql, H, 512), np.nan)
+    l = np.full((w.world, B, ql, H), np.nan)
+    by_seq = {}
+    for b, i in rows:
+        by_seq.setdefault(int(b), []).append(int(i))
+    for b, ilist in sorted(by_seq.items()):
+        gmax = max(boundary(int(w.ctx_lens[b]), ql, i) for i in ilist)
+        for r in ranks:
+            pos_all = layout.rank_local_positions(max(gmax, 0), w.world, w.interleave, r)
+            keys = formats.decode_cache(w.kv[w.seq_start[b] + pos_all], w.kv_format, w.kv_scale)
+
+            def lat(bb, pos, keys=keys, pos_all=pos_all, b=b):
+                n = len(pos)
+                assert bb == b and np.array_equal(pos, pos_all[:n])
+                return keys[:n]
+
+            ro, rl = A.verify_attention(q, lat, w.ctx_lens, w.softmax_scale, world=w.world,
+                                        interleave=w.interleave, rank=r,
+                                        rows=[(b, i) for i in ilist], boundary=boundary)
+            for i in ilist:
+                o[r, b, i], l[r, b, i] = ro[b, i], rl[b, i]
+    return o, l
+
+
+def _new_stats():
+    return dict(elements=0, differ=0, one_step=0, beyond_bar=0, max_abs=0.0, max_abs_no_flip=0.0,
+                max_implied=0.0)
+
+
+def _add_stats(st, v, e, implied, bar):
+    """Error of BF16 outputs ``v`` against their rounded expectation ``e``:
+    elements that differ, those one BF16 step away (rounding-boundary flips),
+    the largest |v - e| overall and over the elements that are not one-step
+    flips, and the largest arithmetic error the outputs imply (the distance from
+    the expected real to the reals that round to v)."""
+    d = np.abs(v - e)
+    one = (d > 0) & ((formats.bf16_step(e, 1) == v) | (formats.bf16_step(e, -1) == v))
+    st["elements"] += v.size
+    st["differ"] += int((d > 0).sum())
+    st["one_step"] += int(one.sum())
+    st["beyond_bar"] += int((d > bar).sum())
+    st["max_abs"] = max(st["max_abs"], float(d.max(initial=0.0)))
+    st["max_abs_no_flip"] = max(st["max_abs_no_flip"], float(d[~one].max(initial=0.0)))
+    st["max_implied"] = max(st["max_implied"], float(implied.max(initial=0.0)))
+
+
+def check_rank(w, gpu_o, gpu_l, o, l, rows, tag=""):
+    """One rank's BF16 output and LSE against its exact partial (``o``, ``l`` for
+    that rank).  Empty (row, rank): exactly 0 and -inf.  Otherwise each output
+    element must be the BF16 rounding of a real within the bar of the exact value,
+    and the LSE within 1e-3.  Returns statistics of the error against the
+    rounded exact value."""
+    bar = tolerance(w)
+    st = _new_stats()
+    for b, i in rows:
+        emp = np.isneginf(l[b, i])
+        assert np.all(np.isneginf(gpu_l[b, i][emp])), (tag, b, i)
+        assert np.all(gpu_o[b, i][emp] == 0.0), (tag, b, i)
+        assert np.all(np.isfinite(gpu_l[b, i][~emp])), (tag, b, i)
+        if not (~emp).any():
+            continue
+        x, v = o[b, i][~emp], gpu_o[b, i][~emp]
+        implied = parity.distance_to_rounding(v, x)
+        assert (implied <= bar).all(), (tag, b, i, float(implied.max()))
+        err_l = float(np.abs(gpu_l[b, i][~emp] - l[b, i][~emp]).max())
+        assert err_l <= LSE_TOL, (tag, b, i, err_l)
+        _add_stats(st, v, formats.round_bf16(x), implied, bar)
+    return st
+
+
+def check_merged(w, gpu_o, gpu_l, o, l, rows, tag=""):
+    """The merged BF16 output against the two-rounding expectation of the exact
+    per-rank partials ``o[W, ...]``, ``l[W, ...]``: each element must be the
+    rounding of a real within the bar of a merge of admissible per-rank BF16
+    values (the rounded exact value, or one step from it where the exact value
+    lies within the bar of that rounding boundary); LSE within 1e-3 of the
+    exact merged LSE.  Returns error statistics against the expectation."""
+    bar = tolerance(w)
+    st = _new_stats()
+    for b, i in rows:
+        _, _, e, lse = parity.merged_expectation(o[:, b, i], l[:, b, i])
+        v = gpu_o[b, i]
+        emp = np.isneginf(lse)
+        assert np.all(np.isneginf(gpu_l[b, i][emp])) and np.all(v[emp] == 0.0), (tag, b, i)
+        implied = parity.merged_gap(v, o[:, b, i], l[:, b, i], bar)
+        ok = implied <= bar
+        assert ok.all(), (tag, b, i, int((~ok).sum()), float(np.abs(v - e)[~ok].max()))
+        assert np.abs(gpu_l[b, i][~emp] - lse[~emp]).max(initial=0.0) <= LSE_TOL, (tag, b, i)
+        _add_stats(st, v, e, implied, bar)
+    return st
+
+
+def count_rejected(w, gpu_o, o, l, rows):
+    """Merged output elements the acceptance rule rejects (the negative control),
+    and the largest |GPU - expectation| among the selected rows."""
+    bar = tolerance(w)
+    bad, total, worst = 0, 0, 0.0
+    for b, i in rows:
+        _, _, e, _ = parity.merged_expectation(o[:, b, i], l[:, b, i])
+        v = gpu_o[b, i]
+        ok = parity.accept_merged(v, o[:, b, i], l[:, b, i], bar)
+        bad += int((~ok).sum())
+        total += v.size
+        worst = max(worst, float(np.abs(v - e).max()))
+    return bad, total, worst
+
+
+def fmt_stats(st):
+    return (f"{st['elements']} elements: {st['differ']} differ from the rounded expectation "
+            f"({st['one_step']} by one BF16 step), {st['beyond_bar']} by more than the bar; "
+            f"max |d| {st['max_abs']:.3e}, {st['max_abs_no_flip']:.3e} without one-step flips; "
+            f"largest implied arithmetic error {st['max_implied']:.3e}")

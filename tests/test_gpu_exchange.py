@@ -6,8 +6,9 @@
   kernel (same arithmetic and order) and within the merge tolerance of the
   float64 oracle;
 * project-before-merge: the per-head W_V projection against float64, and the
-  whole PBM route (project each rank's real partial, pack, exchange, combine)
-  against projecting the oracle's merge of the same partials.
+  whole PBM route (project each rank's partial, pack, exchange, combine) on
+  seeded partials shaped like a verify step, against projecting the oracle's
+  merge of the same partials.
 
 The all-to-all itself is a collective: here one GPU plays every rank and the
 exchange is a copy between the ranks' buffers.
@@ -19,8 +20,7 @@ import torch
 from oracle import attention as A
 from oracle import exchange as X
 from oracle import formats
-from synth import make_config
-from gpu_util import bf16_half_ulp, run_group
+from gpu_util import bf16_half_ulp
 
 pytestmark = pytest.mark.gpu
 
@@ -127,25 +127,24 @@ def test_project_heads(T, H, DV):
     assert np.all(np.abs(got - exact) <= _projection_bound(o, w, exact))
 
 
-@pytest.mark.parametrize("k", [1, 2])
-def test_project_before_merge_route(k):
-    # real per-rank partials of a DCP verify step; PBM route on the GPU against
+@pytest.mark.parametrize("W,B,q,H", [(2, 1, 3, 16), (2, 8, 3, 96), (8, 4, 3, 128)])
+def test_project_before_merge_route(W, B, q, H):
+    # seeded BF16 partials and LSEs with the shapes of a DCP verify step (the
+    # workloads' world, rows and heads); PBM route on the GPU against
     # projecting the float64 merge of the same partials
     ops = _ops()
-    w = make_config(k)
-    grp, _ = run_group(w)
-    W, B, q, H = w.world, w.batch, w.qlen, w.heads
     T = B * q
     DV = 128
-    wbits, wv = _w_v(H, DV, 11 * k)
+    bits, lse_np = _partials(1000 * W + H, W, T, H, 512)
+    wbits, wv = _w_v(H, DV, 11 * W + H)
     wdev = _dev_bf16(wbits)
     Hl = H // W
     sends, proj_bits = [], []
     for r in range(W):
         pr = torch.empty(T, H, DV, dtype=torch.bfloat16, device="cuda")
-        ops.project_heads(grp.out_ranks[r].view(T, H, 512), wdev, pr)
+        ops.project_heads(_dev_bf16(bits[r]), wdev, pr)
         send = torch.empty(W, T, Hl, DV + 8, dtype=torch.bfloat16, device="cuda")
-        ops.a2a_pack(W, pr, grp.lse_ranks[r].view(T, H), send)
+        ops.a2a_pack(W, pr, torch.from_numpy(lse_np[r]).cuda(), send)
         sends.append(send)
         proj_bits.append(pr)
     recvs = _exchange(sends)
@@ -159,8 +158,8 @@ def test_project_before_merge_route(k):
     torch.cuda.synchronize()
     got = torch.cat(outs, dim=1).float().cpu().numpy().astype(np.float64)
     got_l = torch.cat(lses, dim=1).cpu().numpy().astype(np.float64)
-    o_r = np.stack([grp.out_ranks[r].view(T, H, 512).float().cpu().numpy() for r in range(W)]).astype(np.float64)
-    l_r = np.stack([grp.lse_ranks[r].view(T, H).cpu().numpy() for r in range(W)]).astype(np.float64)
+    o_r = formats.decode_bf16(bits)
+    l_r = lse_np.astype(np.float64)
     mo, ml = A.merge_ranks(o_r, l_r)
     exact = X.project_heads(mo, wv)
     # bound: the final BF16 rounding, plus each rank's projected partial --
@@ -168,7 +167,8 @@ def test_project_before_merge_route(k):
     # (the weights sum to 1); 1e-6 covers the fp32 combine itself
     # The final rounding acts on the fp32 value, which may sit just past a
     # power of two from the exact one: charge half an ulp of the larger binade
-    wts = np.where(np.isneginf(l_r), 0.0, np.exp(l_r - ml[None]))
+    with np.errstate(invalid="ignore"):
+        wts = np.where(np.isneginf(l_r), 0.0, np.exp(l_r - ml[None]))
     bound = np.maximum(bf16_half_ulp(exact), bf16_half_ulp(got)) + 1e-6
     for r in range(W):
         proj_exact = X.project_heads(o_r[r], wv)

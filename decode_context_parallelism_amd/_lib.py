@@ -85,6 +85,8 @@ SIGNATURES = {
     "dcpmla_partial_attention": (ctypes.c_int, [_G, _P, _P, _F, _F, _M, _P, _I64, _P, _P, _P]),
     "dcpmla_merge_segments": (ctypes.c_int, [_G, _M, _P, _I64, _P, _P, _P]),
     "dcpmla_rank_attention": (ctypes.c_int, [_G, _P, _P, _F, _F, _M, _P, _I64, _P, _P, _P]),
+    "dcpmla_rank_attention_static": (ctypes.c_int, [_G, _P, _P, _F, _F, _M, _P, _P, _P]),
+    "dcpmla_static_scratch_bytes": (_I64, []),
     "dcpmla_merge_ranks": (ctypes.c_int, [_I32, _I64, _P, _P, _P, _P, _P]),
     "dcpmla_merge_segments_dense": (ctypes.c_int, [_I64, _I32, _P, _P, _P, _P, _P]),
     "dcpmla_strerror": (ctypes.c_char_p, [ctypes.c_int]),

@@ -340,6 +340,7 @@ const char *dcpmla_strerror(int status) {
     case DCPMLA_E_WORKSPACE: return "workspace too small";
     case DCPMLA_E_UNSUPPORTED: return "unsupported request";
     case DCPMLA_E_HIP: return "HIP runtime error";
+    case DCPMLA_E_SCRATCH: return "request needs more than the library's static scratch array";
     default: return "unknown status";
   }
 }

@@ -224,6 +224,23 @@ def rank_attention(geom: Geometry, q, kv_pool, kv_scale: float, softmax_scale: f
            "dcpmla_rank_attention")
 
 
+def rank_attention_static(geom: Geometry, q, kv_pool, kv_scale: float, softmax_scale: float,
+                          meta: RankMetadata, out, lse, stream=None) -> None:
+    """``rank_attention`` with the library's static scratch array as its
+    workspace: allocates nothing.  Calls that overlap on one GPU race."""
+    _attn_shapes(geom, q, kv_pool, out, lse)
+    g = geom.c()
+    m = meta.c()
+    _check(lib.dcpmla_rank_attention_static(ctypes.byref(g), _ptr(q), _ptr(kv_pool), kv_scale,
+                                            softmax_scale, ctypes.byref(m), _ptr(out), _ptr(lse),
+                                            _stream(stream)),
+           "dcpmla_rank_attention_static")
+
+
+def static_scratch_bytes() -> int:
+    return int(lib.dcpmla_static_scratch_bytes())
+
+
 def merge_ranks(out_ranks, lse_ranks, out, lse, stream=None) -> None:
     """``out_ranks [W, ..., 512]`` bf16, ``lse_ranks [W, ...]`` f32 -> ``out``, ``lse``."""
     W = out_ranks.shape[0]

@@ -55,7 +55,8 @@ typedef enum {
   DCPMLA_E_ALIAS = -2,       /* an output buffer overlaps an input buffer */
   DCPMLA_E_WORKSPACE = -3,   /* workspace smaller than dcpmla_workspace_bytes() */
   DCPMLA_E_UNSUPPORTED = -4, /* valid request the library does not implement */
-  DCPMLA_E_HIP = -5          /* a HIP runtime call failed (launch, attribute query) */
+  DCPMLA_E_HIP = -5,         /* a HIP runtime call failed (launch, attribute query) */
+  DCPMLA_E_SCRATCH = -6      /* request larger than the library's static scratch array */
 } dcpmla_status;
 
 /* Latent-cache element formats. */
@@ -252,6 +253,34 @@ int dcpmla_rank_attention(const dcpmla_geom *geom, const void *q, const void *kv
                           float kv_scale, float softmax_scale, const dcpmla_meta *meta,
                           void *workspace, int64_t workspace_bytes, void *out_rank,
                           float *lse_rank, hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * dcpmla_rank_attention() without the workspace argument.  The split-KV
+ * partials and the split query go to a device array inside the library,
+ * DCPMLA_STATIC_SCRATCH_BYTES (160 MiB) on every GPU it runs on, held until
+ * the process ends; the call itself allocates nothing (no hipMalloc, hipFree
+ * or allocating library routine).  The request needs
+ * dcpmla_workspace_bytes(geom) bytes of it (with geom->groups = 0 that is
+ * about 134 MB for the 256-CU grid plus 1,156 bytes per head-row, so up to
+ * about 28,000 head-rows); a larger request returns DCPMLA_E_SCRATCH before
+ * any launch (a smaller geom->groups needs less).  The array keeps the last
+ * call's contents; nothing in it has to start at zero.  All calls on one GPU
+ * share its array, so calls that overlap in time on one GPU (on different
+ * streams, or from different threads) race and must be ordered by the
+ * caller.  Other arguments, results and errors as in dcpmla_rank_attention();
+ * the results are those of dcpmla_rank_attention() with the same geometry,
+ * bit for bit.
+ */
+#define DCPMLA_STATIC_SCRATCH_BYTES (160LL << 20)
+int dcpmla_rank_attention_static(const dcpmla_geom *geom, const void *q, const void *kv_pool,
+                                 float kv_scale, float softmax_scale, const dcpmla_meta *meta,
+                                 void *out_rank, float *lse_rank, hipStream_t stream);
+
+/* Host only.  DCPMLA_STATIC_SCRATCH_BYTES. */
+int64_t dcpmla_static_scratch_bytes(void);
 
 /*
  * Exact two-term E4M3 split of BF16 query rows, the form in which an FP8-cache

@@ -47,7 +47,7 @@ INFINITY_CACHE_BYTES = 256 << 20
 # sources that fix the attention kernel's code and work partition: the counter
 # summaries under profiles/ record their digest
 KERNEL_SOURCES = [os.path.join(ROOT, "decode_context_parallelism_amd", "csrc", f)
-                  for f in ("attention.hip", "common.h")]
+                  for f in ("attention.hip", "attention_fp8.hip", "attention_common.h", "common.h")]
 
 
 def parse():

@@ -16,6 +16,8 @@ BOUNDARY_CAUSAL = 0
 BOUNDARY_BLOCK = 1
 Q_SPLIT = 0
 Q_FP8 = 1
+P_SPLIT = 0
+P_FP8 = 1
 
 OK = 0
 E_INVALID = -1
@@ -23,6 +25,7 @@ E_ALIAS = -2
 E_WORKSPACE = -3
 E_UNSUPPORTED = -4
 E_HIP = -5
+E_SCRATCH = -6
 
 ERR_CTX_LT_QLEN = 1
 ERR_TABLE_CAPACITY = 2
@@ -47,6 +50,7 @@ class Geom(ctypes.Structure):
         ("num_blocks", ctypes.c_int64),
         ("row_boundary", ctypes.c_int32),
         ("q_format", ctypes.c_int32),
+        ("p_format", ctypes.c_int32),
     ]
 
 

@@ -87,6 +87,8 @@ int dcpmla_validate(const dcpmla_geom *g) {
   if (g->groups < 0 || g->groups > kMaxGroups) return DCPMLA_E_INVALID;
   if (g->q_format != DCPMLA_Q_SPLIT && g->q_format != DCPMLA_Q_FP8) return DCPMLA_E_INVALID;
   if (g->q_format == DCPMLA_Q_FP8 && g->kv_dtype != DCPMLA_KV_FP8_E4M3) return DCPMLA_E_INVALID;
+  if (g->p_format != DCPMLA_P_SPLIT && g->p_format != DCPMLA_P_FP8) return DCPMLA_E_INVALID;
+  if (g->p_format == DCPMLA_P_FP8 && g->kv_dtype != DCPMLA_KV_FP8_E4M3) return DCPMLA_E_INVALID;
   if (g->row_boundary != DCPMLA_BOUNDARY_CAUSAL && g->row_boundary != DCPMLA_BOUNDARY_BLOCK)
     return DCPMLA_E_INVALID;
   // index arithmetic stays in 32 bits on the device

@@ -1,0 +1,986 @@
+// Segmented split-KV MLA attention for one DCP rank, FP8 (E4M3) latent cache,
+// gfx950.  Both products run on the FP8 matrix units with the cache bytes as
+// stored:
+//   S^T = K Q^T   v_mfma_f32_32x32x64_f8f6f4, Q as two E4M3 terms that sum to
+//                 the BF16 query exactly (q = (hi + lo) 2^-k, dcpmla_split_q),
+//                 or the hi term alone for the quantised-query variant;
+//   O^T += V^T P^T  v_mfma_f32_32x32x64_f8f6f4 over 64 tokens, P^T as an E4M3
+//                 term plus an E5M2 remainder (about 7 significant bits of
+//                 each probability, on a par with BF16), or the E4M3 term
+//                 alone for the FP8-probability variant.
+// No cache element is ever widened.
+//
+// What it computes, the work decomposition (persistent stream-K over the cost
+// partition of common.h) and the split-piece partials are those of the
+// BF16-cache kernel in attention.hip ("[ROCm][MLA][DCP] Support causal
+// multi-token verification", PR #51705, "Implementation" items 1-3); here a
+// unit is a 64-token stage.
+//
+// Inside a workgroup: 4 waves x 32 head-rows, one wave per SIMD; each wave
+// keeps its query rows in registers (128 VGPRs; the rope step of the split
+// query waits in LDS) and its 512 x 32 output accumulator in 256 AGPRs.  LDS
+// holds three stage tiles (36 KiB each: two halves of 32 tokens, each 36
+// blocks [32 token slots][16 bytes]), filled by direct global->LDS loads, and
+// per wave a staging area that holds the pending stage's probabilities and
+// the rope query until the piece ends.
+//
+// The stage loop is software-pipelined by one stage.  Stage u: one barrier
+// (tile u has landed, every wave is done with tile u-2), the scores of tile u
+// with the loads of tile u+1 issued between the first block's products, then
+// the p.v products of stage u-1 in eight chunks with the softmax of stage u
+// between them, so the exponentials and conversions issue while the matrix
+// unit is busy.  The tile being loaded, the tile being scored and the tile
+// whose p.v is pending are three different buffers.  No memory-counter wait
+// falls between a tile's loads and the next barrier: the loop is free of
+// scratch reloads, which would wait for those loads (the counter retires in
+// order).
+//
+// Online softmax without accumulator rescaling: each stage's probabilities
+// are formed against the stage's own integer ceiling ms, and the p.v product
+// applies 2^(ms - mref) as the E8M0 scale of its P operand, mref being the
+// row's reference; only a jump of more than kMaxUp moves mref (and rescales).
+#include "attention_common.h"
+#include "launch.h"
+
+namespace dcpmla {
+
+namespace {
+
+using namespace attn;
+
+constexpr int kStage = kStageTokensFp8;   // tokens per stage (two 32-token score tiles)
+
+struct Tile8 {
+  static constexpr int kRow = 16;                        // bytes of one token slot in a block
+  static constexpr int kBlock = 32 * kRow;               // 32 slots x 16 dims
+  static constexpr int kHalfBytes = kKBlocks * kBlock;   // 32 tokens x 576 dims
+  static constexpr int kBytes = 2 * kHalfBytes;          // one stage
+};
+constexpr int kBufs = 3;
+typedef Staging<2> Stage8;   // BF16 outputs and fp16 partials
+
+// Probabilities of a stage are formed against the stage's own ceiling ms (the
+// row maximum of its scores, rounded up to an integer in base 2):
+// p' = 2^(score - ms + kPShift) <= 2^8 = 256 stays inside E4M3's range (448).
+// The product carries 2^(ms - mref) as the E8M0 scale of the P operand, so the
+// accumulator stays in the frame of the row reference mref (an integer) and is
+// never rescaled while ms - mref <= kMaxUp; only a row whose scores jump by
+// more than that moves mref (the rare path).  Stages far below mref get the
+// smallest scale, 2^-127: their share of the row is below fp32 resolution.
+constexpr float kPShift = 8.0f;
+constexpr float kMaxUp = 64.0f;
+constexpr int kScaleOne = 127;   // E8M0 encoding of 2^0
+
+// ------------------------------------------------------------ staging
+//
+// Direct loads of a stage: waves 0, 1 fill tile half 0 (tokens 0..31), waves
+// 2, 3 half 1 (32..63).  Load k (k < 9) of wave w fills half bytes
+// [1024 j, 1024 j + 1024) with j = (w & 1) + 2k: lane l writes 16 bytes at
+// 1024 j + 16 l, i.e. slot l % 32 of blocks 2j and 2j + 1, so every lane
+// reads 16-byte pieces of one token row (the token of slot l % 32 of its
+// wave's half) for the whole stage.
+__device__ inline int load_half(int wave) { return wave >> 1; }
+
+// Address of this lane's token row for stage s (page id fetched one stage
+// earlier), plus the lane's fixed byte offset inside the row.  A token past
+// the longest row, or on a page outside the pool, reads the zero row, so the
+// tile never holds stale bytes (an FP8 NaN pattern times a zero probability
+// would poison the output).
+//
+// Lane-derived terms here and below come from a fresh lane id at each use:
+// kept live through the stage loop they would be spilled, and a scratch
+// reload after the stage's direct loads waits for those loads (memory
+// counters retire in order).
+__device__ inline const uint8_t *stage_row(const AttnArgs &a, int32_t page, int s, int lmax, int wave,
+                                           bool *bad) {
+  const int lane = fresh_lane_id();
+  const int t = s * kStage + 32 * load_half(wave) + tok_slot(lane & 31);
+  const bool in_seq = t < lmax;
+  const bool ok = page >= 0 && (int64_t)page < a.num_pages;
+  *bad = *bad || __any(in_seq && !ok);   // wave-uniform: a scalar flag
+  const uint8_t *row = a.zero_row;
+  if (in_seq && ok) {
+    const int64_t r = ((int64_t)page << a.page_shift) + (t & ((1 << a.page_shift) - 1));
+    row = a.pool + r * kDqk;
+  }
+  return row + 32 * (wave & 1) + 16 * (lane >> 5);
+}
+
+__device__ inline int32_t fetch_page(const AttnArgs &a, const int32_t *pt, int s, int lmax, int wave) {
+  const int lane = fresh_lane_id();
+  const int t = s * kStage + 32 * load_half(wave) + tok_slot(lane & 31);
+  return pt[t < lmax ? (t >> a.page_shift) : 0];
+}
+
+// This wave's nine loads of a stage: row bytes 64 k + (lane part, in row) to
+// tile bytes half * 18 KiB + 1024 (w & 1) + 2048 k.  One M0 save/restore.
+__device__ inline uint32_t stage_dst(uint32_t tile_lds, int wave_s) {
+  return tile_lds + load_half(wave_s) * Tile8::kHalfBytes + 1024 * (wave_s & 1);
+}
+__device__ inline void issue_stage(uint32_t tile_lds, const uint8_t *row, int wave_s) {
+  const uint32_t dst = stage_dst(tile_lds, wave_s);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %10\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %5, off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %6, off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %7, off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %8, off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %9, off\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(row), "v"(row + 64), "v"(row + 128), "v"(row + 192), "v"(row + 256), "v"(row + 320),
+        "v"(row + 384), "v"(row + 448), "v"(row + 512), "s"(dst)
+      : "memory", "scc");
+}
+
+// ------------------------------------------------------------ operands
+//
+// PV, value-dim block d: the A operand V^T holds, for lane (dim 32d + l % 32,
+// half h = l / 32), the 32 tokens of pattern h of the stage -- in each
+// 16-token group the eight tokens {4h..4h+3, 8+4h..8+4h+3}, which sit in
+// slots 8h..8h+7 -- in the order (half 0 group 0, half 0 group 1, half 1
+// group 0, half 1 group 1), eight per transposing read.  tr_b8: within a
+// 16-lane group, result lane 8a + b gets byte b of the 8-byte rows loaded by
+// lanes a, a + 2, ..., a + 14.  The same k order on the P^T side is
+// registers 0..15 of the half-0 score tile, then 0..15 of the half-1 tile:
+// exactly the lane's own probabilities in register order.
+__device__ inline int2v tr8(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) int2v *)(size_t)addr);
+}
+struct VOff {
+  uint32_t base;   // this lane's offset for d = 0, read (half 0, group 0)
+};
+__device__ inline VOff v_offsets(int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int h = g >> 1, k = j >> 1, a = j & 1;
+  VOff o;
+  o.base = (uint32_t)((g & 1) * Tile8::kBlock + (8 * h + k) * Tile8::kRow + 8 * a);
+  return o;
+}
+__device__ inline int8v lds_v(uint32_t tile, VOff o, int d) {
+  const uint32_t p = tile + o.base + 2 * d * Tile8::kBlock;
+  const int2v r0 = tr8(p);
+  const int2v r1 = tr8(p + 16 * Tile8::kRow);
+  const int2v r2 = tr8(p + Tile8::kHalfBytes);
+  const int2v r3 = tr8(p + Tile8::kHalfBytes + 16 * Tile8::kRow);
+  int8v v;
+  v[0] = r0[0]; v[1] = r0[1]; v[2] = r1[0]; v[3] = r1[1];
+  v[4] = r2[0]; v[5] = r2[1]; v[6] = r3[0]; v[7] = r3[1];
+  return v;
+}
+
+// p.v products: A = V^T in E4M3 with unit scale; B = P^T in E4M3 (format 0)
+// or E5M2 (format 1) with the E8M0 scale e.  The scale of B lane l covers
+// column l % 32 -- the lane's head-row -- over scale block l / 32 of k, and
+// block j holds register bytes 16 j .. 16 j + 15 of both lane halves; the two
+// lanes of a row pass the same e, so it multiplies every probability of the
+// row in the stage.
+__device__ inline floatx16 mma_pv_hi(int8v a, int8v b, floatx16 c, int e) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kScaleOne, 0, e);
+}
+__device__ inline floatx16 mma_pv_lo(int8v a, int8v b, floatx16 c, int e) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 1, 0, kScaleOne, 0, e);
+}
+
+// The query operands held in registers: step st, term tm at v[kTerms st + tm].
+// The split query keeps its last (rope) step in LDS instead, in the wave's
+// staging area, and reads it back before each score block: in registers it
+// would be live through the p.v products, which with the softmax beside them
+// need the rest of the register file.
+template <bool QF8>
+struct QOp {
+  static constexpr int kTerms = QF8 ? 1 : 2;
+  static constexpr int kRegSteps = QF8 ? kDqk / 64 : kDqk / 64 - 1;
+  int8v v[kTerms * kRegSteps];
+};
+// Rope step of the split query in LDS: chunk 2 tm + j (16 bytes of every
+// lane) at 1024 (2 tm + j) + 16 lane.
+struct Rope {
+  int8v hi, lo;
+};
+__device__ inline void put_rope(uint8_t *area, int tm, uint4 a, uint4 b) {
+  uint4 *d = (uint4 *)(area + 16 * fresh_lane_id());
+  d[128 * tm] = a;
+  d[128 * tm + 64] = b;
+}
+__device__ inline Rope get_rope(const uint8_t *area) {
+  const uint4 *d = (const uint4 *)(area + 16 * fresh_lane_id());
+  Rope r;
+  r.hi = cat8(d[0], d[64]);
+  r.lo = cat8(d[128], d[192]);
+  return r;
+}
+
+// S^T for one 32-token half of a tile: the nine 64-dim steps' hi (and lo)
+// products in one asm block.  Per step two 16-byte tile reads (blocks
+// 4 st + 2h and 4 st + 2h + 1: 32 dims of this lane's token row) feed the
+// query terms; the reads run two steps ahead in three fixed register tuples
+// (declared clobbered, so the compiler keeps nothing there across the block)
+// and the scores stay in VGPRs.  Left to the compiler, the score accumulator
+// lands in AGPRs and the output accumulator is moved out of them.  The
+// closing nops are the wait states an XDL result needs before a VALU reads it.
+__device__ inline floatx16 scores_split(uint32_t kaddr, const QOp<false> &q, const Rope &rope) {
+  floatx16 acc;
+  asm volatile(
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "ds_read_b128 v[240:243], %[addr] offset:0\n\t"
+      "ds_read_b128 v[244:247], %[addr] offset:512\n\t"
+      "ds_read_b128 v[248:251], %[addr] offset:2048\n\t"
+      "ds_read_b128 v[252:255], %[addr] offset:2560\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q1], %[acc]\n\t"
+      "ds_read_b128 v[232:235], %[addr] offset:4096\n\t"
+      "ds_read_b128 v[236:239], %[addr] offset:4608\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q2], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q3], %[acc]\n\t"
+      "ds_read_b128 v[240:243], %[addr] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[addr] offset:6656\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q4], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
+      "ds_read_b128 v[248:251], %[addr] offset:8192\n\t"
+      "ds_read_b128 v[252:255], %[addr] offset:8704\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q7], %[acc]\n\t"
+      "ds_read_b128 v[232:235], %[addr] offset:10240\n\t"
+      "ds_read_b128 v[236:239], %[addr] offset:10752\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q8], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q9], %[acc]\n\t"
+      "ds_read_b128 v[240:243], %[addr] offset:12288\n\t"
+      "ds_read_b128 v[244:247], %[addr] offset:12800\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q10], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q11], %[acc]\n\t"
+      "ds_read_b128 v[248:251], %[addr] offset:14336\n\t"
+      "ds_read_b128 v[252:255], %[addr] offset:14848\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q12], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q13], %[acc]\n\t"
+      "ds_read_b128 v[232:235], %[addr] offset:16384\n\t"
+      "ds_read_b128 v[236:239], %[addr] offset:16896\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q14], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q15], %[acc]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q16], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q17], %[acc]\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3\n\t"
+      : [acc] "=&v"(acc)
+      : [addr] "v"(kaddr), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]), [q3] "v"(q.v[3]),
+        [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]), [q8] "v"(q.v[8]),
+        [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]),
+        [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(rope.hi),
+        [q17] "v"(rope.lo)
+      : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242",
+        "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253",
+        "v254", "v255", "memory");
+  return acc;
+}
+
+// The same with this wave's nine direct loads of the next tile (issue_stage
+// below) issued one after each step's products: issued back to back they
+// stall the wave in the memory pipe for about a thousand cycles, which the
+// products now cover.
+__device__ inline floatx16 scores_split_dma(uint32_t kaddr, const QOp<false> &q, const Rope &rope,
+                                            const uint8_t *row, uint32_t dst) {
+  floatx16 acc;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[m0s], m0\n\t"
+      "s_mov_b32 m0, %[dst]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "ds_read_b128 v[240:243], %[addr] offset:0\n\t"
+      "ds_read_b128 v[244:247], %[addr] offset:512\n\t"
+      "ds_read_b128 v[248:251], %[addr] offset:2048\n\t"
+      "ds_read_b128 v[252:255], %[addr] offset:2560\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q1], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g0], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[232:235], %[addr] offset:4096\n\t"
+      "ds_read_b128 v[236:239], %[addr] offset:4608\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q2], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q3], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g1], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[240:243], %[addr] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[addr] offset:6656\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q4], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g2], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[248:251], %[addr] offset:8192\n\t"
+      "ds_read_b128 v[252:255], %[addr] offset:8704\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q7], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g3], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[232:235], %[addr] offset:10240\n\t"
+      "ds_read_b128 v[236:239], %[addr] offset:10752\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q8], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q9], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g4], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[240:243], %[addr] offset:12288\n\t"
+      "ds_read_b128 v[244:247], %[addr] offset:12800\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q10], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q11], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g5], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[248:251], %[addr] offset:14336\n\t"
+      "ds_read_b128 v[252:255], %[addr] offset:14848\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q12], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q13], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g6], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[232:235], %[addr] offset:16384\n\t"
+      "ds_read_b128 v[236:239], %[addr] offset:16896\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q14], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q15], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g7], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q16], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q17], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g8], off\n\t"
+      "s_mov_b32 m0, %[m0s]\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3\n\t"
+      : [acc] "=&v"(acc), [m0s] "=&s"(saved)
+      : [addr] "v"(kaddr), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]), [q3] "v"(q.v[3]),
+        [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]), [q8] "v"(q.v[8]),
+        [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]),
+        [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(rope.hi),
+        [q17] "v"(rope.lo),
+        [g0] "v"(row), [g1] "v"(row + 64), [g2] "v"(row + 128), [g3] "v"(row + 192),
+        [g4] "v"(row + 256), [g5] "v"(row + 320), [g6] "v"(row + 384), [g7] "v"(row + 448),
+        [g8] "v"(row + 512), [dst] "s"(dst)
+      : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242",
+        "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253",
+        "v254", "v255", "memory", "scc");
+  return acc;
+}
+
+// The quantised query: the hi terms alone.
+__device__ inline floatx16 scores_fp8q(uint32_t kaddr, const QOp<true> &q) {
+  floatx16 acc;
+  asm volatile(
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "ds_read_b128 v[240:243], %[addr] offset:0\n\t"
+      "ds_read_b128 v[244:247], %[addr] offset:512\n\t"
+      "ds_read_b128 v[248:251], %[addr] offset:2048\n\t"
+      "ds_read_b128 v[252:255], %[addr] offset:2560\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
+      "ds_read_b128 v[232:235], %[addr] offset:4096\n\t"
+      "ds_read_b128 v[236:239], %[addr] offset:4608\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q1], %[acc]\n\t"
+      "ds_read_b128 v[240:243], %[addr] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[addr] offset:6656\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q2], %[acc]\n\t"
+      "ds_read_b128 v[248:251], %[addr] offset:8192\n\t"
+      "ds_read_b128 v[252:255], %[addr] offset:8704\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q3], %[acc]\n\t"
+      "ds_read_b128 v[232:235], %[addr] offset:10240\n\t"
+      "ds_read_b128 v[236:239], %[addr] offset:10752\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q4], %[acc]\n\t"
+      "ds_read_b128 v[240:243], %[addr] offset:12288\n\t"
+      "ds_read_b128 v[244:247], %[addr] offset:12800\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
+      "ds_read_b128 v[248:251], %[addr] offset:14336\n\t"
+      "ds_read_b128 v[252:255], %[addr] offset:14848\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
+      "ds_read_b128 v[232:235], %[addr] offset:16384\n\t"
+      "ds_read_b128 v[236:239], %[addr] offset:16896\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q7], %[acc]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q8], %[acc]\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3\n\t"
+      : [acc] "=&v"(acc)
+      : [addr] "v"(kaddr), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]), [q3] "v"(q.v[3]),
+        [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]), [q8] "v"(q.v[8])
+      : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242",
+        "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253",
+        "v254", "v255", "memory");
+  return acc;
+}
+
+// The quantised query with the next tile's direct loads, one per step.
+__device__ inline floatx16 scores_fp8q_dma(uint32_t kaddr, const QOp<true> &q, const uint8_t *row,
+                                           uint32_t dst) {
+  floatx16 acc;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[m0s], m0\n\t"
+      "s_mov_b32 m0, %[dst]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "ds_read_b128 v[240:243], %[addr] offset:0\n\t"
+      "ds_read_b128 v[244:247], %[addr] offset:512\n\t"
+      "ds_read_b128 v[248:251], %[addr] offset:2048\n\t"
+      "ds_read_b128 v[252:255], %[addr] offset:2560\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
+      "global_load_lds_dwordx4 %[g0], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[232:235], %[addr] offset:4096\n\t"
+      "ds_read_b128 v[236:239], %[addr] offset:4608\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q1], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g1], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[240:243], %[addr] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[addr] offset:6656\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q2], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g2], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[248:251], %[addr] offset:8192\n\t"
+      "ds_read_b128 v[252:255], %[addr] offset:8704\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q3], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g3], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[232:235], %[addr] offset:10240\n\t"
+      "ds_read_b128 v[236:239], %[addr] offset:10752\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q4], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g4], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[240:243], %[addr] offset:12288\n\t"
+      "ds_read_b128 v[244:247], %[addr] offset:12800\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g5], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[248:251], %[addr] offset:14336\n\t"
+      "ds_read_b128 v[252:255], %[addr] offset:14848\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g6], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[232:235], %[addr] offset:16384\n\t"
+      "ds_read_b128 v[236:239], %[addr] offset:16896\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q7], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g7], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q8], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g8], off\n\t"
+      "s_mov_b32 m0, %[m0s]\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3\n\t"
+      : [acc] "=&v"(acc), [m0s] "=&s"(saved)
+      : [addr] "v"(kaddr), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]), [q3] "v"(q.v[3]),
+        [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]), [q8] "v"(q.v[8]),
+        [g0] "v"(row), [g1] "v"(row + 64), [g2] "v"(row + 128), [g3] "v"(row + 192),
+        [g4] "v"(row + 256), [g5] "v"(row + 320), [g6] "v"(row + 384), [g7] "v"(row + 448),
+        [g8] "v"(row + 512), [dst] "s"(dst)
+      : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242",
+        "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253",
+        "v254", "v255", "memory", "scc");
+  return acc;
+}
+
+template <bool QF8>
+__device__ inline floatx16 scores(uint32_t kaddr, const QOp<QF8> &q, const Rope &rope) {
+  if constexpr (QF8) return scores_fp8q(kaddr, q);
+  else return scores_split(kaddr, q, rope);
+}
+template <bool QF8>
+__device__ inline floatx16 scores_dma(uint32_t kaddr, const QOp<QF8> &q, const Rope &rope, const uint8_t *row,
+                                      uint32_t dst) {
+  if constexpr (QF8) return scores_fp8q_dma(kaddr, q, row, dst);
+  else return scores_split_dma(kaddr, q, rope, row, dst);
+}
+
+// P of one stage: the E4M3 term (8 registers: 32 probabilities, one byte
+// each, in k order) and, unless P8, the E5M2 remainder.
+template <bool P8> struct POp;
+template <> struct POp<false> { int8v hi, lo; };
+template <> struct POp<true> { int8v hi; };
+
+// A stage's probabilities wait for their p.v in LDS, in the wave's output
+// staging area (unused until the piece ends): kept in registers they would be
+// live across the next stage's score products, where the split query, the
+// scores and the read-ahead tuples already fill the register file.  Chunk c
+// (16 bytes of every lane) sits at 1024 c + 16 lane.
+template <bool P8>
+__device__ inline void put_p(uint8_t *area, const POp<P8> &p) {
+  int4v *d = (int4v *)(area + 16 * fresh_lane_id());
+  d[0] = __builtin_shufflevector(p.hi, p.hi, 0, 1, 2, 3);
+  d[64] = __builtin_shufflevector(p.hi, p.hi, 4, 5, 6, 7);
+  if constexpr (!P8) {
+    d[128] = __builtin_shufflevector(p.lo, p.lo, 0, 1, 2, 3);
+    d[192] = __builtin_shufflevector(p.lo, p.lo, 4, 5, 6, 7);
+  }
+}
+template <bool P8>
+__device__ inline POp<P8> get_p(const uint8_t *area) {
+  const int4v *d = (const int4v *)(area + 16 * fresh_lane_id());
+  POp<P8> p;
+  p.hi = __builtin_shufflevector(d[0], d[64], 0, 1, 2, 3, 4, 5, 6, 7);
+  if constexpr (!P8) p.lo = __builtin_shufflevector(d[128], d[192], 0, 1, 2, 3, 4, 5, 6, 7);
+  return p;
+}
+
+// Group w (0..7) of the lane's 32 probabilities p' = 2^(score * sc2 - msub)
+// of one stage -- scores of tile half 0 in s0, half 1 in s1; masked scores
+// are -inf and give 0 -- packed as bytes w of the p.v B operand:
+// hi = E4M3(p') (round to nearest even), lo = E5M2(p' - hi).  Adds the fp32
+// sum of p' to sf and the sum of exactly the values fed to the products to sq.
+template <bool P8>
+__device__ inline void p_group(const floatx16 &s0, const floatx16 &s1, int w, float sc2, float msub, POp<P8> &o,
+                               float &sq, float &sf) {
+  float p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float sv = w < 4 ? s0[4 * w + e] : s1[4 * (w - 4) + e];
+    p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, sc2, -msub));
+    sf += p[e];
+  }
+  int hw = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+  hw = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], hw, true);
+  o.hi[w] = hw;
+  const float2v h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+  const float2v h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+  if constexpr (P8) {
+    sq += (h01[0] + h01[1]) + (h23[0] + h23[1]);
+  } else {
+    int lw = __builtin_amdgcn_cvt_pk_bf8_f32(p[0] - h01[0], p[1] - h01[1], 0, false);
+    lw = __builtin_amdgcn_cvt_pk_bf8_f32(p[2] - h23[0], p[3] - h23[1], lw, true);
+    o.lo[w] = lw;
+    const float2v l01 = __builtin_amdgcn_cvt_pk_f32_bf8(lw, false);
+    const float2v l23 = __builtin_amdgcn_cvt_pk_f32_bf8(lw, true);
+    sq += ((h01[0] + l01[0]) + (h01[1] + l01[1])) + ((h23[0] + l23[0]) + (h23[1] + l23[1]));
+  }
+}
+
+// O^T += V^T (2^(e - 127) P^T) for one stage (tile at `tile`), value-dim
+// blocks in order
+template <bool P8>
+__device__ inline void pv(floatx16 (&o)[kDv / 32], uint32_t tile, const POp<P8> &p, int e) {
+  const VOff vo = v_offsets(fresh_lane_id());
+  int8v va[2];
+  va[0] = lds_v(tile, vo, 0);
+#pragma unroll
+  for (int d = 0; d < kDv / 32; ++d) {
+    if (d + 1 < kDv / 32) va[(d + 1) % 2] = lds_v(tile, vo, d + 1);
+    o[d] = mma_pv_hi(va[d % 2], p.hi, o[d], e);
+    if constexpr (!P8) o[d] = mma_pv_lo(va[d % 2], p.lo, o[d], e);
+  }
+}
+
+// Issue order inside one chunk of the stage body below (two value blocks'
+// products and one group of the next stage's probabilities, which do not
+// depend on each other): the transposing reads for the block two ahead, a
+// product, a slice of the VALU work, and so on, so the VALU work issues while
+// the matrix unit is busy.  The closing barrier keeps chunks in order.
+template <bool P8>
+__device__ inline void chunk_order() {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // V reads, two blocks ahead
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // hi product
+    __builtin_amdgcn_sched_group_barrier(0x002, P8 ? 12 : 8, 0);
+    if constexpr (!P8) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // lo product
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Keeps the output accumulator in AGPRs across the stage loop: at each such
+// point the 16 tiles must sit in AGPRs, so the register allocator has no
+// reason to move them into VGPRs (or scratch) between the p.v products.
+__device__ inline void pin_agprs(floatx16 (&o)[kDv / 32]) {
+#pragma unroll
+  for (int d = 0; d < kDv / 32; ++d) asm volatile("" : "+a"(o[d]));
+}
+
+// Zeroes the output accumulator in place in its AGPRs.  Written as plain
+// zeros, the compiler hoists one zero vector out of the piece loop and keeps
+// it in scratch, and its reload at each piece start waits for the tile loads
+// in flight.
+__device__ inline void zero_agprs(floatx16 (&o)[kDv / 32]) {
+#pragma unroll
+  for (int d = 0; d < kDv / 32; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) asm volatile("v_accvgpr_write_b32 %0, 0" : "=a"(o[d][r]));
+}
+
+// Rare path: scale every accumulator element of this lane's row in place
+// (read from its AGPR, multiply, write back) so the 256-element accumulator
+// never has to be copied into VGPRs as a whole; the trailing nops cover the
+// VALU-writes-AGPR -> MFMA-reads-SrcC wait states.
+__device__ __attribute__((always_inline)) inline void rescale_o(floatx16 (&o)[kDv / 32], float alpha) {
+#pragma unroll
+  for (int d = 0; d < kDv / 32; ++d) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float t;
+      asm volatile(
+          "v_accvgpr_read_b32 %0, %1\n\t"
+          "s_nop 1\n\t"
+          "v_mul_f32 %0, %0, %2\n\t"
+          "v_accvgpr_write_b32 %1, %0\n\t"
+          "s_nop 2"
+          : "=&v"(t), "+a"(o[d][r])
+          : "v"(alpha));
+    }
+  }
+}
+
+// LDS: three stage tiles, the four waves' output staging areas, then
+// (PartLds) the work partition and the row lengths.
+template <bool PartLds, bool QF8, bool P8>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attention_fp8_kernel(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
+  const int lane = tid & 63;
+  const int h = lane >> 5;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.ws_scale = a.out_scale;
+  const int64_t U = a.work[0];
+  if (U == 0) return;
+  const int64_t G = effective_groups(gridDim.x, U, DCPMLA_KV_FP8_E4M3);
+  if ((int64_t)blockIdx.x >= G) return;
+  const int64_t w = xcd_group(blockIdx.x, G);
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_char *)lds);
+  int32_t *part = (int32_t *)(lds + kBufs * Tile8::kBytes + Stage8::kBytes);
+  const int nwork = 4 * a.B + 2;
+  if constexpr (PartLds) {
+    for (int i = tid; i < nwork; i += kThreads) part[i] = a.work[i];
+    for (int i = tid; i < a.B * a.qlen; i += kThreads) part[nwork + i] = a.row_len[i];
+    __syncthreads();
+  }
+  Walk<PartLds> wk;
+  wk.work = a.work;
+  wk.part = part;
+  wk.row_len = a.row_len;
+  wk.B = a.B;
+  wk.n_mt = a.n_mt;
+  wk.nwork = nwork;
+  wk.U = U;
+  wk.pc = piece_cost(DCPMLA_KV_FP8_E4M3);
+  wk.C = total_cost(U, a.n_mt, a.B, wk.pc);
+  wk.hi = U;
+  const int64_t lo = wk.units_before(group_cost_lo(w, wk.C, G));
+  const int64_t hi = wk.units_before(group_cost_lo(w + 1, wk.C, G));
+  if (lo >= hi) return;   // a cost range of piece overheads only
+  wk.hi = hi;
+  bool bad = false;
+
+  auto pt_of = [&](const Cursor &c) { return a.page_table + (int64_t)c.lrow * a.max_local_pages; };
+  auto page_of = [&](const Cursor &c) { return fetch_page(a, pt_of(c), c.s, c.lmax, wave); };
+  auto load_stage = [&](const Cursor &c, int32_t page, int buf) {
+    issue_stage(lds_base + buf * Tile8::kBytes, stage_row(a, page, c.s, c.lmax, wave, &bad), wave);
+  };
+  // the wave's staging area holds, until the piece ends, the pending stage's
+  // probabilities (4 KiB) and the rope step of the split query (4 KiB)
+  uint8_t *parea = lds + kBufs * Tile8::kBytes + wave * Stage8::kWaveBytes;
+  uint8_t *qarea = parea + 4096;
+  static_assert(Stage8::kWaveBytes >= 8192, "staging area too small for P and the rope query");
+  QOp<QF8> q;
+  float sc2 = a.score_scale2;   // this lane's score scale (times 2^-k of the split query)
+  // this lane's head-row of the piece at c, and the query row it loads
+  auto load_q = [&](const Cursor &c) {
+    // lane-derived addresses and kernel arguments are re-derived per piece:
+    // kept live across the piece loop they end up in scratch
+    const int ln = fresh_lane_id();
+    const KernargArgs ka = kernarg_args();
+    const int M = ka->M;
+    const int m = c.mt * kTileRows + wave * kWaveRows + (ln & 31);
+    // rows past M score with row M-1 (a valid address): finite values whose
+    // results are never stored
+    const int64_t qr = (int64_t)c.b * M + (m < M ? m : M - 1);
+    // tiled split: chunk 4 st + 2 term + half holds this lane's 16 bytes at
+    // 16 (32 h + row % 32), so each load below reads one contiguous KiB
+    // across the wave (two runs when a wave's rows straddle a 32-row block)
+    const uint8_t *qrow = ka->qsplit + qsplit_off(qr, 0, ln >> 5);
+    constexpr int kT = QOp<QF8>::kTerms;
+#pragma unroll
+    for (int st = 0; st < kDqk / 64; ++st) {
+#pragma unroll
+      for (int tm = 0; tm < kT; ++tm) {
+        const uint4 c0 = *(const uint4 *)(qrow + (4 * st + 2 * tm) * kQSplitChunk);
+        const uint4 c1 = *(const uint4 *)(qrow + (4 * st + 2 * tm + 1) * kQSplitChunk);
+        if (st < QOp<QF8>::kRegSteps) q.v[kT * st + tm] = cat8(c0, c1);
+        else put_rope(qarea, tm, c0, c1);
+      }
+    }
+    sc2 = ka->score_scale2 * ka->qscale[qr];
+  };
+
+  Cursor P = wk.locate(lo);
+  Cursor nx = P;       // cursor of the unit whose tile is loaded next
+  int32_t page = 0;    // page id of that unit
+  load_stage(P, page_of(P), 0);
+  if (lo + 1 < hi) {
+    nx = wk.advance(P, lo + 1);
+    page = page_of(nx);
+  }
+  int buf = 0;         // buffer of the current unit
+  int64_t u = lo;
+
+  while (true) {
+    load_q(P);
+    floatx16 oacc[kDv / 32];
+    zero_agprs(oacc);
+    float mref = kNegInf;  // row reference (an integer, base 2): the accumulator's frame
+    float lsum_q = 0.f;  // sum of the probabilities as multiplied (hi + lo): normalises O
+    float lsum_f = 0.f;  // fp32 sum of the probabilities before conversion: gives the LSE
+    const int b = P.b;
+    const int mt = P.mt;
+    const bool complete = P.st_begin == 0 && P.st_end == P.stages;
+    // this lane's head-row and its verify-row window
+    const int m = mt * kTileRows + wave * kWaveRows + (fresh_lane_id() & 31);
+    const bool mvalid = m < a.M;
+    const int vrow = mvalid ? m / kernarg_args()->H : 0;
+    // rows past M (zero queries) see every token: their results are never
+    // stored, and they keep the wave on the unmasked path
+    const int rlen = mvalid ? wk.row_len_at(b * a.qlen + vrow) : 0x3FFFFFFF;
+    const int nst = P.st_end - P.st_begin;
+    Cursor following = P;   // first unit after this piece, when there is one
+    auto prev_tile = [&]() { return lds_base + (buf == 0 ? kBufs - 1 : buf - 1) * Tile8::kBytes; };
+    // Stage k: wait for its tile, start the next tile's loads, the scores,
+    // the softmax and the probabilities (pc, with E8M0 scale ec) -- and, with
+    // PREV, the pending p.v of stage k - 1 (pp, scale ep) interleaved with
+    // that softmax.  A row whose reference moves has its accumulator (after
+    // the pending product, which used the old frame) and sums rescaled.
+    int epend = kScaleOne;   // E8M0 scale of the pending stage
+    Rope rope;               // rope step of the split query, read one stage ahead
+    if constexpr (!QF8) rope = get_rope(qarea);
+    auto stage = [&](auto prev_tag, int k) __attribute__((always_inline)) {
+      constexpr bool PREV = decltype(prev_tag)::value;
+      const int s = P.st_begin + k;
+      const int64_t uu = u + k;
+      // tile uu has landed (this wave's share: the wait; every wave's: the
+      // barrier), and every wave is done with the tile of unit uu - 2
+      wait_direct_loads();
+      __syncthreads();
+      const uint32_t tile = lds_base + buf * Tile8::kBytes;
+      const int ln = fresh_lane_id();
+      const int hh = ln >> 5;
+      const uint32_t kaddr = tile + 1024 * hh + 16 * tok_slot(ln & 31);
+      // online softmax in base 2 on this lane's 32 tokens of head-row m.
+      // Register r of half t holds token 64 s + 32 t + 4h + 8(r/4) + r%4; a
+      // stage lies wholly inside every row window of the wave when
+      // rlen - 64 s - 4h > 59 on all lanes.
+      const int lim = rlen - s * kStage - 4 * hh;
+      // the first score block also issues the next unit's tile loads
+      floatx16 s0;
+      if (uu + 1 < hi) {
+        const uint32_t nb = buf == kBufs - 1 ? 0 : buf + 1;
+        s0 = scores_dma<QF8>(kaddr, q, rope, stage_row(a, page, nx.s, nx.lmax, wave, &bad),
+                             stage_dst(lds_base + nb * Tile8::kBytes, wave));
+        if (k == nst - 1) following = nx;
+        if (uu + 2 < hi) {
+          nx = wk.advance(nx, uu + 2);
+          page = page_of(nx);
+        }
+      } else {
+        s0 = scores<QF8>(kaddr, q, rope);
+      }
+      floatx16 s1 = scores<QF8>(kaddr + Tile8::kHalfBytes, q, rope);
+      // the pending stage's probabilities and first value blocks: their LDS
+      // latency runs under the masking and the row maximum
+      const uint32_t vt = prev_tile();
+      const VOff vo = v_offsets(fresh_lane_id());
+      POp<P8> pp;
+      int8v va[3];
+      if constexpr (PREV) {
+        pp = get_p<P8>(parea);
+        va[0] = lds_v(vt, vo, 0);
+        va[1] = lds_v(vt, vo, 1);
+      }
+      if (!__all(lim > 59)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = 8 * (r >> 2) + (r & 3);
+          s0[r] = off < lim ? s0[r] : kNegInf;
+          s1[r] = off + 32 < lim ? s1[r] : kNegInf;
+        }
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+      mx = fmaxf(mx, other_half(mx, hh)) * sc2;
+      // the stage ceiling; a row with nothing visible in the stage (all p'
+      // are 0) takes the reference, or 0 before the row has one
+      const bool vis = mx > kNegInf;
+      const bool started = mref > kNegInf;
+      const float cm = __builtin_ceilf(mx);
+      const float ms = vis ? cm : (started ? mref : 0.f);
+      mref = started ? mref : (vis ? ms : kNegInf);   // nothing accumulated yet
+      const float delta = (started || vis) ? ms - mref : 0.f;
+      const float msub = ms - kPShift;
+      float sq = 0.f, sf = 0.f;
+      POp<P8> pc;
+      if constexpr (PREV) {
+        // the pending p.v with this stage's probabilities between its
+        // products: eight chunks of one group of four probabilities and two
+        // value blocks each, V read two blocks ahead
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          p_group<P8>(s0, s1, c, sc2, msub, pc, sq, sf);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int d = 2 * c + j;
+            if (d + 2 < kDv / 32) va[(d + 2) % 3] = lds_v(vt, vo, d + 2);
+            oacc[d] = mma_pv_hi(va[d % 3], pp.hi, oacc[d], epend);
+            if constexpr (!P8) oacc[d] = mma_pv_lo(va[d % 3], pp.lo, oacc[d], epend);
+          }
+          chunk_order<P8>();
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) p_group<P8>(s0, s1, c, sc2, msub, pc, sq, sf);
+      }
+      put_p<P8>(parea, pc);
+      // the stage sums join the row sums here, in the reference frame before
+      // any move; a row whose reference moves (the first stage of a piece
+      // never does: mref was -inf) redoes it below
+      const float lq_old = lsum_q, lf_old = lsum_f;
+      const int di = (int)__builtin_fmaxf(__builtin_fminf(delta, kMaxUp), -127.f);
+      epend = kScaleOne + di;
+      lsum_q += __builtin_ldexpf(sq, di);
+      lsum_f += __builtin_ldexpf(sf, di);
+      const bool move = PREV && delta > kMaxUp;
+      if (PREV && __any(move)) {
+        // exact power of two; the pending product is already in oacc
+        const float alpha = move ? __builtin_ldexpf(1.0f, -(int)__builtin_fminf(delta, 1024.f)) : 1.0f;
+        rescale_o(oacc, alpha);
+        if (move) {
+          mref = ms;
+          epend = kScaleOne;
+          lsum_q = lq_old * alpha + sq;
+          lsum_f = lf_old * alpha + sf;
+        }
+      }
+      pin_agprs(oacc);
+      buf = buf == kBufs - 1 ? 0 : buf + 1;
+      // the next stage's rope operands: read now, they arrive during the barrier
+      if constexpr (!QF8) rope = get_rope(qarea);
+    };
+    using NoPrev = std::integral_constant<bool, false>;
+    using Prev = std::integral_constant<bool, true>;
+    stage(NoPrev{}, 0);
+    for (int k = 1; k < nst; ++k) stage(Prev{}, k);
+    // the last stage's p.v
+    pv<P8>(oacc, prev_tile(), get_p<P8>(parea), epend);
+    u += nst;
+    const bool more = u < hi;
+    // finish the piece
+    const float ltot = lsum_q + other_half(lsum_q, h);
+    const float ltot_f = lsum_f + other_half(lsum_f, h);
+    const bool has = ltot > 0.f;
+    const float lse2 = has ? mref - kPShift + __builtin_amdgcn_logf(ltot_f) : kNegInf;
+    // rows of this wave that exist (m < M)
+    const int nrows = min(kWaveRows, a.M - (mt * kTileRows + wave * kWaveRows));
+    uint8_t *stg = lds + kBufs * Tile8::kBytes + wave * Stage8::kWaveBytes;
+    const KernargArgs ka = kernarg_args();
+    if (complete) {
+      const float inv = has ? a.out_scale / ltot : 0.f;
+      __bf16 *orow0 = (__bf16 *)ka->out + ((int64_t)b * a.M + mt * kTileRows + wave * kWaveRows) * kDv;
+      store_rows<2>(oacc, inv, stg, orow0, nrows);
+      if (mvalid && h == 0)
+        ka->lse[(int64_t)b * a.M + mt * kTileRows + wave * kWaveRows + (fresh_lane_id() & 31)] =
+            has ? lse2 * kLn2 : kNegInf;
+    } else {
+      // fp16 partial of o / kv_scale: a weighted mean of E4M3 values, so
+      // |value| <= 448 and fp16 keeps 11 significant bits of it
+      const int64_t prow0 = (w * kSlots + piece_slot(P.st_begin)) * kTileRows + wave * kWaveRows;
+      const float invr = has ? 1.0f / ltot : 0.f;
+      store_rows<2>(oacc, invr, stg, (_Float16 *)ka->ws_o + prow0 * kDv, nrows);
+      if (mvalid && h == 0) ka->ws_lse2[prow0 + (fresh_lane_id() & 31)] = lse2;
+    }
+    if (!more) break;
+    P = following;
+  }
+  if (bad && lane == 0) atomicOr(a.err, DCPMLA_ERR_PAGE_RANGE);
+}
+
+constexpr size_t kLdsLimit = 160 * 1024;   // gfx950 LDS per workgroup
+constexpr size_t kTilesBytes = kBufs * Tile8::kBytes + Stage8::kBytes;
+static_assert(kTilesBytes < kLdsLimit, "tiles and staging must fit in LDS");
+
+template <bool PartLds, bool QF8, bool P8>
+hipError_t launch_variant(const AttnArgs &a, int groups, size_t shmem, hipStream_t stream) {
+  static DeviceOnce once;
+  const size_t cap = PartLds ? kLdsLimit : kTilesBytes;
+  const hipError_t e = once.run([&] {
+    return hipFuncSetAttribute((const void *)attention_fp8_kernel<PartLds, QF8, P8>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)cap);
+  });
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attention_fp8_kernel<PartLds, QF8, P8>), dim3(groups), dim3(kThreads), shmem, stream, a);
+  return hipGetLastError();
+}
+
+template <bool QF8, bool P8>
+hipError_t launch_formats(AttnArgs a, int groups, hipStream_t stream) {
+  const size_t part = (size_t)(4 * (int64_t)a.B + 2 + (int64_t)a.B * a.qlen) * 4;
+  if (kTilesBytes + part <= kLdsLimit) {
+    a.part_ints = (int)(part / 4);
+    return launch_variant<true, QF8, P8>(a, groups, kTilesBytes + part, stream);
+  }
+  a.part_ints = 0;
+  return launch_variant<false, QF8, P8>(a, groups, kTilesBytes, stream);
+}
+
+}  // namespace
+
+hipError_t launch_attention_fp8(const AttnArgs &a, int groups, bool q_fp8, bool p_fp8, hipStream_t stream) {
+  if (q_fp8) return p_fp8 ? launch_formats<true, true>(a, groups, stream) : launch_formats<true, false>(a, groups, stream);
+  return p_fp8 ? launch_formats<false, true>(a, groups, stream) : launch_formats<false, false>(a, groups, stream);
+}
+
+}  // namespace dcpmla

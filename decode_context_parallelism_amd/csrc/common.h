@@ -11,18 +11,24 @@ namespace dcpmla {
 constexpr int kDqk = 576;          // 512 latent + 64 rope
 constexpr int kDv = 512;
 constexpr int kRopeDims = kDqk - kDv;
-constexpr int kStageTokens = 32;   // tokens per LDS stage = one 32x32 MFMA score tile
+constexpr int kStageTokens = 32;   // tokens per LDS stage with a BF16 cache (one 32x32 score tile)
+constexpr int kStageTokensFp8 = 64;  // with an FP8 cache: two score tiles, one K = 64 product of p.v
 constexpr int kWaveRows = 32;      // head-rows (M) per wave
 constexpr int kWaves = 4;          // waves per attention workgroup
 constexpr int kTileRows = kWaveRows * kWaves;  // head-rows per workgroup (M tile)
 constexpr int kThreads = kWaves * 64;
 constexpr int kSlots = 2;          // partial slots per persistent workgroup
 
+// Stage size by cache format: the unit of the work partition below.
+__host__ __device__ inline int stage_tokens(int kv_dtype) {
+  return kv_dtype == DCPMLA_KV_FP8_E4M3 ? kStageTokensFp8 : kStageTokens;
+}
+
 // Work buffer layout (int32): [0] total units U; [1 .. B+1] unit_base[b]
 // (prefix of n_mtiles * stages over sequences, unit_base[B] = U);
 // [B+2 .. 2B+2) stages[b]; [2B+2 .. 3B+2) longest rank-local row length lmax[b];
 // [3B+2 .. 4B+2) the verify row (b*qlen + i) that has that length.  A unit is
-// one 32-token stage of one (sequence, head-row tile).
+// one stage (stage_tokens(kv_dtype) tokens) of one (sequence, head-row tile).
 // Past the partition, a zero row of kZeroInts int32 (one 576-element latent
 // row in either cache format) that attention reads for tokens outside a
 // sequence; the builder rewrites it with every forward.
@@ -90,37 +96,43 @@ __host__ __device__ inline int64_t ws_total_bytes(int groups, int64_t rows) {
 }
 
 // Workgroups that actually take work: every one gets at least about
-// kMinUnitsPerGroup stages, because each split costs a partial of 128 rows
-// x 512 values (written here, read back by the segment merge) and a reload of
-// the tile's query rows.  Four keeps every compute unit busy on the small
-// verify workload (about 1,200 stages per rank) and is measured faster there
-// than eight.
-constexpr int64_t kMinUnitsPerGroup = 4;
-__host__ __device__ inline int64_t effective_groups(int64_t launched, int64_t U) {
-  int64_t g = (U + kMinUnitsPerGroup - 1) / kMinUnitsPerGroup;
+// min_units(kv_dtype) stages (128 tokens), because each split costs a partial
+// of 128 rows x 512 values (written here, read back by the segment merge) and
+// a reload of the tile's query rows.  Four 32-token stages keep every compute
+// unit busy on the small verify workload (about 1,200 stages per rank) and
+// were measured faster there than eight.
+__host__ __device__ inline int64_t min_units(int kv_dtype) {
+  return kv_dtype == DCPMLA_KV_FP8_E4M3 ? 2 : 4;
+}
+__host__ __device__ inline int64_t effective_groups(int64_t launched, int64_t U, int kv_dtype) {
+  const int64_t mu = min_units(kv_dtype);
+  int64_t g = (U + mu - 1) / mu;
   if (g < 1) g = 1;
   return g < launched ? g : launched;
 }
 
 // Scheduling cost.  Besides its stages, every (sequence, head-row tile) item
-// costs kPieceCost stage-equivalents for its query load and output stores,
-// which dominate when sequences are short.  Measured, a piece's query load
-// and output stores take about 16-18k cycles against about 4k per stage;
-// every split piece pays them while the axis below charges them once per
-// item, and 5 measured best over the five workloads (6 and 4 were close).  Items are laid out on a cost
-// axis in (sequence, tile) order, each as kPieceCost of overhead followed by
-// its stages: item (b, mt) starts at
-//   item_cost(b, mt) = unit_base[b] + kPieceCost * n_mt * b + mt * (stages[b] + kPieceCost)
-// and its stage s sits at item_cost + kPieceCost + s.  Workgroup w of G owns
-// the units whose cost position lies in [w C / G, (w + 1) C / G) with
-// C = U + kPieceCost * n_mt * B.  Every group's cost range is non-empty
-// (G <= U <= C), but it may hold only overhead and so no unit.
-constexpr int64_t kPieceCost = 5;
-__host__ __device__ inline int64_t total_cost(int64_t U, int n_mt, int batch) {
-  return U + kPieceCost * n_mt * (int64_t)batch;
+// costs piece_cost(kv_dtype) stage-equivalents for its query load and output
+// stores, which dominate when sequences are short.  Measured, a piece's query
+// load and output stores take about 16-18k cycles against about 4k per
+// 32-token stage of the BF16-operand loop (5 measured best over the five
+// workloads, 6 and 4 close), and about 4.5k per 64-token stage of the FP8 loop
+// (3).  Every split piece pays them while the axis below charges them once per
+// item.  Items are laid out on a cost axis in (sequence, tile) order, each as
+// pc = piece_cost of overhead followed by its stages: item (b, mt) starts at
+//   item_cost(b, mt) = unit_base[b] + pc * n_mt * b + mt * (stages[b] + pc)
+// and its stage s sits at item_cost + pc + s.  Workgroup w of G owns the
+// units whose cost position lies in [w C / G, (w + 1) C / G) with
+// C = U + pc * n_mt * B.  Every group's cost range is non-empty (G <= U <= C),
+// but it may hold only overhead and so no unit.
+__host__ __device__ inline int64_t piece_cost(int kv_dtype) {
+  return kv_dtype == DCPMLA_KV_FP8_E4M3 ? 3 : 5;
 }
-__host__ __device__ inline int64_t seq_cost(int64_t unit_base_b, int n_mt, int b) {
-  return unit_base_b + kPieceCost * n_mt * (int64_t)b;
+__host__ __device__ inline int64_t total_cost(int64_t U, int n_mt, int batch, int64_t pc) {
+  return U + pc * n_mt * (int64_t)batch;
+}
+__host__ __device__ inline int64_t seq_cost(int64_t unit_base_b, int n_mt, int b, int64_t pc) {
+  return unit_base_b + pc * n_mt * (int64_t)b;
 }
 __host__ __device__ inline int64_t group_cost_lo(int64_t w, int64_t C, int64_t G) { return (w * C) / G; }
 // the group whose cost range holds position x (0 <= x < C)

@@ -164,7 +164,7 @@ __device__ inline void load_partial8(const _Float16 *row, int lane, float v[8]) 
 
 template <typename PT>
 __global__ void __launch_bounds__(256) merge_segments_kernel(
-    int B, int qlen, int heads, int n_mt, int G, const int32_t *__restrict__ work,
+    int B, int qlen, int heads, int n_mt, int G, int kv_dtype, const int32_t *__restrict__ work,
     const PT *__restrict__ ws_o, const float *__restrict__ ws_lse2, const float *__restrict__ ws_scale,
     uint4 *__restrict__ out, float *__restrict__ lse) {
   constexpr int kChunks = kTileRows / kMergeRows;
@@ -192,10 +192,10 @@ __global__ void __launch_bounds__(256) merge_segments_kernel(
   // the groups holding this item's first and last stage (cost positions
   // x0 and x0 + stages - 1); when they differ, the first of them wrote its
   // share to its slot 1 and each later one to its slot 0
-  const int64_t Geff = effective_groups(G, U);
-  const int64_t C = total_cost(U, n_mt, B);
-  const int64_t x0 = seq_cost(work[work_unit_base_off() + b], n_mt, b) +
-                     (int64_t)mt * (stages + kPieceCost) + kPieceCost;
+  const int64_t pc = piece_cost(kv_dtype);
+  const int64_t Geff = effective_groups(G, U, kv_dtype);
+  const int64_t C = total_cost(U, n_mt, B, pc);
+  const int64_t x0 = seq_cost(work[work_unit_base_off() + b], n_mt, b, pc) + (int64_t)mt * (stages + pc) + pc;
   const int64_t w0 = cost_group(x0, C, Geff);
   const int64_t w1 = cost_group(x0 + stages - 1, C, Geff);
   if (w0 == w1) return;   // finished inside one workgroup
@@ -283,11 +283,11 @@ hipError_t launch_merge_segments(const dcpmla_geom &g, int groups, const dcpmla_
   const dim3 grid(g.batch * n_mt * chunks);
   if (g.kv_dtype == DCPMLA_KV_FP8_E4M3) {
     hipLaunchKernelGGL(merge_segments_kernel<_Float16>, grid, dim3(256), 0, stream, g.batch, g.qlen,
-                       g.num_heads, n_mt, groups, m.work, (const _Float16 *)workspace,
+                       g.num_heads, n_mt, groups, g.kv_dtype, m.work, (const _Float16 *)workspace,
                        ws + ws_o_floats(groups), ws + ws_scale_off(groups), (uint4 *)out_rank, lse_rank);
   } else {
     hipLaunchKernelGGL(merge_segments_kernel<float>, grid, dim3(256), 0, stream, g.batch, g.qlen,
-                       g.num_heads, n_mt, groups, m.work, ws, ws + ws_o_floats(groups),
+                       g.num_heads, n_mt, groups, g.kv_dtype, m.work, ws, ws + ws_o_floats(groups),
                        ws + ws_scale_off(groups), (uint4 *)out_rank, lse_rank);
   }
   return hipGetLastError();

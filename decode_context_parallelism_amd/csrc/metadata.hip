@@ -94,7 +94,7 @@ __global__ void __launch_bounds__(256) meta_rows_kernel(
 }
 
 // One workgroup: longest row per sequence, stages, and the unit prefix.
-__global__ void __launch_bounds__(256) meta_work_kernel(int B, int qlen, int n_mt,
+__global__ void __launch_bounds__(256) meta_work_kernel(int B, int qlen, int n_mt, int stage,
                                                         const int32_t *__restrict__ row_len,
                                                         int32_t *__restrict__ work) {
   __shared__ int s_scan[256];
@@ -111,7 +111,7 @@ __global__ void __launch_bounds__(256) meta_work_kernel(int B, int qlen, int n_m
         const int v = row_len[b * qlen + i];
         if (v > lm) { lm = v; lrow = b * qlen + i; }
       }
-      const int st = (lm + kStageTokens - 1) / kStageTokens;
+      const int st = (lm + stage - 1) / stage;
       work[work_lmax_off(B) + b] = lm;
       work[work_lrow_off(B) + b] = lrow;
       work[work_stages_off(B) + b] = st;
@@ -145,7 +145,7 @@ constexpr int kSmallEntries = 8192;
 
 __global__ void __launch_bounds__(kSmallThreads) meta_small_kernel(
     int W, int S, int block_size, int qlen, int max_blocks, int max_local_pages, int64_t num_blocks,
-    int rank, int block_rows, int B, int n_mt, const int32_t *__restrict__ ctx_lens,
+    int rank, int block_rows, int B, int n_mt, int stage, const int32_t *__restrict__ ctx_lens,
     const int32_t *__restrict__ block_table, int32_t *__restrict__ row_len,
     int32_t *__restrict__ page_table, int32_t *__restrict__ last_len, int32_t *__restrict__ err,
     int32_t *__restrict__ work) {
@@ -220,7 +220,7 @@ __global__ void __launch_bounds__(kSmallThreads) meta_small_kernel(
       const int v = s_len[tid * qlen + i];
       if (v > lm) { lm = v; lrow = tid * qlen + i; }
     }
-    const int st = (lm + kStageTokens - 1) / kStageTokens;
+    const int st = (lm + stage - 1) / stage;
     work[work_lmax_off(B) + tid] = lm;
     work[work_lrow_off(B) + tid] = lrow;
     work[work_stages_off(B) + tid] = st;
@@ -260,7 +260,8 @@ hipError_t launch_build_metadata(const dcpmla_geom &g, int rank, const int32_t *
     hipLaunchKernelGGL(meta_small_kernel, dim3(1), dim3(kSmallThreads), 0, stream, g.dcp_world,
                        g.interleave, g.block_size, g.qlen, g.max_blocks_per_seq, g.max_local_pages,
                        g.num_blocks, rank, g.row_boundary == DCPMLA_BOUNDARY_BLOCK ? 1 : 0, g.batch,
-                       n_mtiles(g.qlen, g.num_heads), ctx_lens, block_table, m.row_local_len,
+                       n_mtiles(g.qlen, g.num_heads), stage_tokens(g.kv_dtype), ctx_lens, block_table,
+                       m.row_local_len,
                        m.page_table, m.last_page_len, m.err, m.work);
     return hipGetLastError();
   }
@@ -272,7 +273,7 @@ hipError_t launch_build_metadata(const dcpmla_geom &g, int rank, const int32_t *
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(meta_work_kernel, dim3(1), dim3(256), 0, stream, g.batch, g.qlen,
-                     n_mtiles(g.qlen, g.num_heads), m.row_local_len, m.work);
+                     n_mtiles(g.qlen, g.num_heads), stage_tokens(g.kv_dtype), m.row_local_len, m.work);
   return hipGetLastError();
 }
 

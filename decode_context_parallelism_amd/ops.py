@@ -67,13 +67,15 @@ class Geometry:
     groups: int = 0
     row_boundary: str = "causal"   # "causal" verify rows | "block" (bidirectional draft block)
     q_format: str = "split"        # FP8 cache: "split" (exact BF16 query) | "fp8" (quantised query)
+    p_format: str = "split"        # FP8 cache: "split" (two-term probabilities) | "fp8" (one E4M3 term)
 
     def c(self) -> _lib.Geom:
         return _lib.Geom(self.dcp_world, self.interleave, self.block_size, self.qlen,
                          self.num_heads, self.batch, self.max_blocks_per_seq,
                          self.max_local_pages, self.kv_code, self.groups, self.num_blocks,
                          {"causal": _lib.BOUNDARY_CAUSAL, "block": _lib.BOUNDARY_BLOCK}[self.row_boundary],
-                         {"split": _lib.Q_SPLIT, "fp8": _lib.Q_FP8}[self.q_format])
+                         {"split": _lib.Q_SPLIT, "fp8": _lib.Q_FP8}[self.q_format],
+                         {"split": _lib.P_SPLIT, "fp8": _lib.P_FP8}[self.p_format])
 
     @property
     def kv_code(self) -> int:

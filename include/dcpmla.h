@@ -93,6 +93,22 @@ enum {
   DCPMLA_Q_FP8 = 1
 };
 
+/*
+ * How an FP8-cache attention feeds the softmax probabilities p to the p.v
+ * products (the value operand is the E4M3 cache itself).  SPLIT (default): p,
+ * scaled by a power of two, as an E4M3 term plus an E5M2 remainder -- about 7
+ * significant bits, on a par with a BF16 p -- in two FP8 products; the output
+ * is normalised by the sum of exactly the values multiplied.  FP8: the E4M3
+ * term alone, one product (half the p.v matrix work; the probabilities carry
+ * 4 significant bits), after "Context Parallel Guide (PCP & DCP)", "How it
+ * works" item 4 and "Sparse DCP persistent attention and gqa=64" (decode runs
+ * MLA with FP8 operands against an FP8 cache).  FP8 requires an FP8 cache.
+ */
+enum {
+  DCPMLA_P_SPLIT = 0,
+  DCPMLA_P_FP8 = 1
+};
+
 /* Bits of the device error word. */
 enum {
   DCPMLA_ERR_CTX_LT_QLEN = 1,    /* ctx < qlen: rows whose boundary would be < 1 get no tokens */
@@ -124,6 +140,7 @@ typedef struct dcpmla_geom {
   int64_t num_blocks;         /* physical blocks in each rank's pool */
   int32_t row_boundary;       /* DCPMLA_BOUNDARY_CAUSAL (default) or DCPMLA_BOUNDARY_BLOCK */
   int32_t q_format;           /* DCPMLA_Q_SPLIT (default) or DCPMLA_Q_FP8 (FP8 cache only) */
+  int32_t p_format;           /* DCPMLA_P_SPLIT (default) or DCPMLA_P_FP8 (FP8 cache only) */
 } dcpmla_geom;
 
 /*

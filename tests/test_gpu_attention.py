@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import layout
+from oracle import formats, layout
 from synth import make_config, make_workload
 from gpu_util import (bf16_to_f64, check_merged, check_rank, count_rejected, fmt_stats,
                       rank_expectations, run_group)
@@ -212,3 +212,29 @@ def test_fp8_query_sampled(k):
     assert grp.errors() == 0
     _check_all(w, grp, _sample_rows(w, 3, 60 + k), ranks=(0, w.world - 1), q_format="fp8",
                tag=f"config {k} fp8 query")
+
+
+def _spiked_workload(seed, kv_format="fp8_e4m3"):
+    """FP8 workload whose cache holds a few keys aligned with one head's query
+    at full E4M3 magnitude: that head's scores jump by about 240 (base 2)
+    at those tokens, far past any running maximum of ordinary N(0, 1) data.
+    A spike inside a later stage makes the row move its reference mid-piece;
+    one in the first stage leaves every later stage far below it."""
+    w = make_workload(name="spiked", world=2, interleave=1, batch=2, qlen=3, heads=16, block_size=64,
+                      kv_format=kv_format, ctx=("fixed", 2000), table="shuffled", max_local_pages=24,
+                      seed=seed)
+    q = formats.decode_bf16(w.q_bits)
+    top = 0x7E   # E4M3 code of 448
+    for b, pos, h in ((0, 1200, 3), (0, 10, 7), (1, 700, 0), (1, 1600, 0), (1, 1601, 12)):
+        sign = q[b, 0, h] < 0
+        w.kv[w.seq_start[b] + pos] = np.where(sign, top | 0x80, top).astype(np.uint8)
+    return w
+
+
+@pytest.mark.parametrize("groups", [0, 5])
+def test_score_jumps(groups):
+    w = _spiked_workload(3001)
+    print(f"spiked workload groups {groups}", flush=True)
+    grp, _ = run_group(w, groups=groups)
+    assert grp.errors() == 0
+    _check_all(w, grp, _all_rows(w), tag=f"spiked groups {groups}")

@@ -50,6 +50,10 @@ using namespace attn;
 
 constexpr int kStage = kStageTokensFp8;   // tokens per stage (two 32-token score tiles)
 
+// In an odd block (dims 16 (2j + 1) .. + 15) the slots are stored XOR 8: the
+// two 16-lane groups of a transposing read take blocks 2j and 2j + 1 at the
+// same slots, 512 bytes apart -- the same banks -- and the XOR moves the
+// second group into the other half of the 256-byte bank window.
 struct Tile8 {
   static constexpr int kRow = 16;                        // bytes of one token slot in a block
   static constexpr int kBlock = 32 * kRow;               // 32 slots x 16 dims
@@ -76,9 +80,10 @@ constexpr int kScaleOne = 127;   // E8M0 encoding of 2^0
 // Direct loads of a stage: waves 0, 1 fill tile half 0 (tokens 0..31), waves
 // 2, 3 half 1 (32..63).  Load k (k < 9) of wave w fills half bytes
 // [1024 j, 1024 j + 1024) with j = (w & 1) + 2k: lane l writes 16 bytes at
-// 1024 j + 16 l, i.e. slot l % 32 of blocks 2j and 2j + 1, so every lane
-// reads 16-byte pieces of one token row (the token of slot l % 32 of its
-// wave's half) for the whole stage.
+// 1024 j + 16 l, i.e. slot l % 32 of block 2j (l < 32) or 2j + 1 (l >= 32),
+// so every lane reads 16-byte pieces of one token row for the whole stage:
+// the token of slot l % 32, XOR 8 in the odd blocks.
+__device__ inline int load_slot(int lane) { return (lane & 31) ^ (8 * (lane >> 5)); }
 __device__ inline int load_half(int wave) { return wave >> 1; }
 
 // Address of this lane's token row for stage s (page id fetched one stage
@@ -94,7 +99,7 @@ __device__ inline int load_half(int wave) { return wave >> 1; }
 __device__ inline const uint8_t *stage_row(const AttnArgs &a, int32_t page, int s, int lmax, int wave,
                                            bool *bad) {
   const int lane = fresh_lane_id();
-  const int t = s * kStage + 32 * load_half(wave) + tok_slot(lane & 31);
+  const int t = s * kStage + 32 * load_half(wave) + tok_slot(load_slot(lane));
   const bool in_seq = t < lmax;
   const bool ok = page >= 0 && (int64_t)page < a.num_pages;
   *bad = *bad || __any(in_seq && !ok);   // wave-uniform: a scalar flag
@@ -107,8 +112,7 @@ __device__ inline const uint8_t *stage_row(const AttnArgs &a, int32_t page, int 
 }
 
 __device__ inline int32_t fetch_page(const AttnArgs &a, const int32_t *pt, int s, int lmax, int wave) {
-  const int lane = fresh_lane_id();
-  const int t = s * kStage + 32 * load_half(wave) + tok_slot(lane & 31);
+  const int t = s * kStage + 32 * load_half(wave) + tok_slot(load_slot(fresh_lane_id()));
   return pt[t < lmax ? (t >> a.page_shift) : 0];
 }
 
@@ -162,7 +166,7 @@ __device__ inline void issue_stage(uint32_t tile_lds, const uint8_t *row, int wa
 // PV, value-dim block d: the A operand V^T holds, for lane (dim 32d + l % 32,
 // half h = l / 32), the 32 tokens of pattern h of the stage -- in each
 // 16-token group the eight tokens {4h..4h+3, 8+4h..8+4h+3}, which sit in
-// slots 8h..8h+7 -- in the order (half 0 group 0, half 0 group 1, half 1
+// slots 8h..8h+7 (XOR 8 in the odd blocks) -- in the order (half 0 group 0, half 0 group 1, half 1
 // group 0, half 1 group 1), eight per transposing read.  tr_b8: within a
 // 16-lane group, result lane 8a + b gets byte b of the 8-byte rows loaded by
 // lanes a, a + 2, ..., a + 14.  The same k order on the P^T side is
@@ -178,7 +182,7 @@ __device__ inline VOff v_offsets(int lane) {
   const int g = lane >> 4, j = lane & 15;
   const int h = g >> 1, k = j >> 1, a = j & 1;
   VOff o;
-  o.base = (uint32_t)((g & 1) * Tile8::kBlock + (8 * h + k) * Tile8::kRow + 8 * a);
+  o.base = (uint32_t)((g & 1) * Tile8::kBlock + ((8 * h + k) ^ (8 * (g & 1))) * Tile8::kRow + 8 * a);
   return o;
 }
 __device__ inline int8v lds_v(uint32_t tile, VOff o, int d) {
@@ -235,6 +239,23 @@ __device__ inline Rope get_rope(const uint8_t *area) {
   return r;
 }
 
+// This lane's two tile addresses for the score reads of step 0 of a tile
+// half: A-operand row r = lane % 32 is token r of the half, found in slot
+// tok_slot(r) of the even blocks and tok_slot(r) ^ 8 of the odd ones; lane
+// half hh reads blocks 2 hh and 2 hh + 1 of each 4-block step (step st adds
+// 2048 st).
+struct KAddr {
+  uint32_t a0, a1;
+};
+__device__ inline KAddr k_addr(uint32_t half_base) {
+  const int ln = fresh_lane_id();
+  const int sl = tok_slot(ln & 31), hh = ln >> 5;
+  KAddr k;
+  k.a0 = half_base + 1024 * hh + Tile8::kRow * sl;
+  k.a1 = half_base + 1024 * hh + Tile8::kBlock + Tile8::kRow * (sl ^ 8);
+  return k;
+}
+
 // S^T for one 32-token half of a tile: the nine 64-dim steps' hi (and lo)
 // products in one asm block.  Per step two 16-byte tile reads (blocks
 // 4 st + 2h and 4 st + 2h + 1: 32 dims of this lane's token row) feed the
@@ -243,49 +264,49 @@ __device__ inline Rope get_rope(const uint8_t *area) {
 // and the scores stay in VGPRs.  Left to the compiler, the score accumulator
 // lands in AGPRs and the output accumulator is moved out of them.  The
 // closing nops are the wait states an XDL result needs before a VALU reads it.
-__device__ inline floatx16 scores_split(uint32_t kaddr, const QOp<false> &q, const Rope &rope) {
+__device__ inline floatx16 scores_split(KAddr ka, const QOp<false> &q, const Rope &rope) {
   floatx16 acc;
   asm volatile(
       "s_waitcnt lgkmcnt(0)\n\t"
-      "ds_read_b128 v[240:243], %[addr] offset:0\n\t"
-      "ds_read_b128 v[244:247], %[addr] offset:512\n\t"
-      "ds_read_b128 v[248:251], %[addr] offset:2048\n\t"
-      "ds_read_b128 v[252:255], %[addr] offset:2560\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:0\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:2048\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q1], %[acc]\n\t"
-      "ds_read_b128 v[232:235], %[addr] offset:4096\n\t"
-      "ds_read_b128 v[236:239], %[addr] offset:4608\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q2], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q3], %[acc]\n\t"
-      "ds_read_b128 v[240:243], %[addr] offset:6144\n\t"
-      "ds_read_b128 v[244:247], %[addr] offset:6656\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q4], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
-      "ds_read_b128 v[248:251], %[addr] offset:8192\n\t"
-      "ds_read_b128 v[252:255], %[addr] offset:8704\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q7], %[acc]\n\t"
-      "ds_read_b128 v[232:235], %[addr] offset:10240\n\t"
-      "ds_read_b128 v[236:239], %[addr] offset:10752\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q8], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q9], %[acc]\n\t"
-      "ds_read_b128 v[240:243], %[addr] offset:12288\n\t"
-      "ds_read_b128 v[244:247], %[addr] offset:12800\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q10], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q11], %[acc]\n\t"
-      "ds_read_b128 v[248:251], %[addr] offset:14336\n\t"
-      "ds_read_b128 v[252:255], %[addr] offset:14848\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q12], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q13], %[acc]\n\t"
-      "ds_read_b128 v[232:235], %[addr] offset:16384\n\t"
-      "ds_read_b128 v[236:239], %[addr] offset:16896\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q14], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q15], %[acc]\n\t"
@@ -295,7 +316,7 @@ __device__ inline floatx16 scores_split(uint32_t kaddr, const QOp<false> &q, con
       "s_nop 15\n\t"
       "s_nop 3\n\t"
       : [acc] "=&v"(acc)
-      : [addr] "v"(kaddr), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]), [q3] "v"(q.v[3]),
+      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]), [q3] "v"(q.v[3]),
         [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]), [q8] "v"(q.v[8]),
         [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]),
         [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(rope.hi),
@@ -310,7 +331,7 @@ __device__ inline floatx16 scores_split(uint32_t kaddr, const QOp<false> &q, con
 // below) issued one after each step's products: issued back to back they
 // stall the wave in the memory pipe for about a thousand cycles, which the
 // products now cover.
-__device__ inline floatx16 scores_split_dma(uint32_t kaddr, const QOp<false> &q, const Rope &rope,
+__device__ inline floatx16 scores_split_dma(KAddr ka, const QOp<false> &q, const Rope &rope,
                                             const uint8_t *row, uint32_t dst) {
   floatx16 acc;
   uint32_t saved;
@@ -318,59 +339,59 @@ __device__ inline floatx16 scores_split_dma(uint32_t kaddr, const QOp<false> &q,
       "s_mov_b32 %[m0s], m0\n\t"
       "s_mov_b32 m0, %[dst]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
-      "ds_read_b128 v[240:243], %[addr] offset:0\n\t"
-      "ds_read_b128 v[244:247], %[addr] offset:512\n\t"
-      "ds_read_b128 v[248:251], %[addr] offset:2048\n\t"
-      "ds_read_b128 v[252:255], %[addr] offset:2560\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:0\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:2048\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q1], %[acc]\n\t"
       "global_load_lds_dwordx4 %[g0], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[232:235], %[addr] offset:4096\n\t"
-      "ds_read_b128 v[236:239], %[addr] offset:4608\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q2], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q3], %[acc]\n\t"
       "global_load_lds_dwordx4 %[g1], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[240:243], %[addr] offset:6144\n\t"
-      "ds_read_b128 v[244:247], %[addr] offset:6656\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q4], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
       "global_load_lds_dwordx4 %[g2], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[248:251], %[addr] offset:8192\n\t"
-      "ds_read_b128 v[252:255], %[addr] offset:8704\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q7], %[acc]\n\t"
       "global_load_lds_dwordx4 %[g3], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[232:235], %[addr] offset:10240\n\t"
-      "ds_read_b128 v[236:239], %[addr] offset:10752\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q8], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q9], %[acc]\n\t"
       "global_load_lds_dwordx4 %[g4], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[240:243], %[addr] offset:12288\n\t"
-      "ds_read_b128 v[244:247], %[addr] offset:12800\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q10], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q11], %[acc]\n\t"
       "global_load_lds_dwordx4 %[g5], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[248:251], %[addr] offset:14336\n\t"
-      "ds_read_b128 v[252:255], %[addr] offset:14848\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q12], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q13], %[acc]\n\t"
       "global_load_lds_dwordx4 %[g6], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[232:235], %[addr] offset:16384\n\t"
-      "ds_read_b128 v[236:239], %[addr] offset:16896\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q14], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q15], %[acc]\n\t"
@@ -384,7 +405,7 @@ __device__ inline floatx16 scores_split_dma(uint32_t kaddr, const QOp<false> &q,
       "s_nop 15\n\t"
       "s_nop 3\n\t"
       : [acc] "=&v"(acc), [m0s] "=&s"(saved)
-      : [addr] "v"(kaddr), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]), [q3] "v"(q.v[3]),
+      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]), [q3] "v"(q.v[3]),
         [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]), [q8] "v"(q.v[8]),
         [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]),
         [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(rope.hi),
@@ -399,42 +420,42 @@ __device__ inline floatx16 scores_split_dma(uint32_t kaddr, const QOp<false> &q,
 }
 
 // The quantised query: the hi terms alone.
-__device__ inline floatx16 scores_fp8q(uint32_t kaddr, const QOp<true> &q) {
+__device__ inline floatx16 scores_fp8q(KAddr ka, const QOp<true> &q) {
   floatx16 acc;
   asm volatile(
       "s_waitcnt lgkmcnt(0)\n\t"
-      "ds_read_b128 v[240:243], %[addr] offset:0\n\t"
-      "ds_read_b128 v[244:247], %[addr] offset:512\n\t"
-      "ds_read_b128 v[248:251], %[addr] offset:2048\n\t"
-      "ds_read_b128 v[252:255], %[addr] offset:2560\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:0\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:2048\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
-      "ds_read_b128 v[232:235], %[addr] offset:4096\n\t"
-      "ds_read_b128 v[236:239], %[addr] offset:4608\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q1], %[acc]\n\t"
-      "ds_read_b128 v[240:243], %[addr] offset:6144\n\t"
-      "ds_read_b128 v[244:247], %[addr] offset:6656\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q2], %[acc]\n\t"
-      "ds_read_b128 v[248:251], %[addr] offset:8192\n\t"
-      "ds_read_b128 v[252:255], %[addr] offset:8704\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q3], %[acc]\n\t"
-      "ds_read_b128 v[232:235], %[addr] offset:10240\n\t"
-      "ds_read_b128 v[236:239], %[addr] offset:10752\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q4], %[acc]\n\t"
-      "ds_read_b128 v[240:243], %[addr] offset:12288\n\t"
-      "ds_read_b128 v[244:247], %[addr] offset:12800\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
-      "ds_read_b128 v[248:251], %[addr] offset:14336\n\t"
-      "ds_read_b128 v[252:255], %[addr] offset:14848\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
-      "ds_read_b128 v[232:235], %[addr] offset:16384\n\t"
-      "ds_read_b128 v[236:239], %[addr] offset:16896\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q7], %[acc]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
@@ -442,7 +463,7 @@ __device__ inline floatx16 scores_fp8q(uint32_t kaddr, const QOp<true> &q) {
       "s_nop 15\n\t"
       "s_nop 3\n\t"
       : [acc] "=&v"(acc)
-      : [addr] "v"(kaddr), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]), [q3] "v"(q.v[3]),
+      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]), [q3] "v"(q.v[3]),
         [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]), [q8] "v"(q.v[8])
       : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242",
         "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253",
@@ -451,7 +472,7 @@ __device__ inline floatx16 scores_fp8q(uint32_t kaddr, const QOp<true> &q) {
 }
 
 // The quantised query with the next tile's direct loads, one per step.
-__device__ inline floatx16 scores_fp8q_dma(uint32_t kaddr, const QOp<true> &q, const uint8_t *row,
+__device__ inline floatx16 scores_fp8q_dma(KAddr ka, const QOp<true> &q, const uint8_t *row,
                                            uint32_t dst) {
   floatx16 acc;
   uint32_t saved;
@@ -459,52 +480,52 @@ __device__ inline floatx16 scores_fp8q_dma(uint32_t kaddr, const QOp<true> &q, c
       "s_mov_b32 %[m0s], m0\n\t"
       "s_mov_b32 m0, %[dst]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
-      "ds_read_b128 v[240:243], %[addr] offset:0\n\t"
-      "ds_read_b128 v[244:247], %[addr] offset:512\n\t"
-      "ds_read_b128 v[248:251], %[addr] offset:2048\n\t"
-      "ds_read_b128 v[252:255], %[addr] offset:2560\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:0\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:2048\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
       "global_load_lds_dwordx4 %[g0], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[232:235], %[addr] offset:4096\n\t"
-      "ds_read_b128 v[236:239], %[addr] offset:4608\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q1], %[acc]\n\t"
       "global_load_lds_dwordx4 %[g1], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[240:243], %[addr] offset:6144\n\t"
-      "ds_read_b128 v[244:247], %[addr] offset:6656\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q2], %[acc]\n\t"
       "global_load_lds_dwordx4 %[g2], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[248:251], %[addr] offset:8192\n\t"
-      "ds_read_b128 v[252:255], %[addr] offset:8704\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q3], %[acc]\n\t"
       "global_load_lds_dwordx4 %[g3], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[232:235], %[addr] offset:10240\n\t"
-      "ds_read_b128 v[236:239], %[addr] offset:10752\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q4], %[acc]\n\t"
       "global_load_lds_dwordx4 %[g4], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[240:243], %[addr] offset:12288\n\t"
-      "ds_read_b128 v[244:247], %[addr] offset:12800\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
       "global_load_lds_dwordx4 %[g5], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[248:251], %[addr] offset:14336\n\t"
-      "ds_read_b128 v[252:255], %[addr] offset:14848\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
       "global_load_lds_dwordx4 %[g6], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[232:235], %[addr] offset:16384\n\t"
-      "ds_read_b128 v[236:239], %[addr] offset:16896\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q7], %[acc]\n\t"
       "global_load_lds_dwordx4 %[g7], off\n\t"
@@ -516,7 +537,7 @@ __device__ inline floatx16 scores_fp8q_dma(uint32_t kaddr, const QOp<true> &q, c
       "s_nop 15\n\t"
       "s_nop 3\n\t"
       : [acc] "=&v"(acc), [m0s] "=&s"(saved)
-      : [addr] "v"(kaddr), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]), [q3] "v"(q.v[3]),
+      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]), [q3] "v"(q.v[3]),
         [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]), [q8] "v"(q.v[8]),
         [g0] "v"(row), [g1] "v"(row + 64), [g2] "v"(row + 128), [g3] "v"(row + 192),
         [g4] "v"(row + 256), [g5] "v"(row + 320), [g6] "v"(row + 384), [g7] "v"(row + 448),
@@ -528,15 +549,15 @@ __device__ inline floatx16 scores_fp8q_dma(uint32_t kaddr, const QOp<true> &q, c
 }
 
 template <bool QF8>
-__device__ inline floatx16 scores(uint32_t kaddr, const QOp<QF8> &q, const Rope &rope) {
-  if constexpr (QF8) return scores_fp8q(kaddr, q);
-  else return scores_split(kaddr, q, rope);
+__device__ inline floatx16 scores(KAddr ka, const QOp<QF8> &q, const Rope &rope) {
+  if constexpr (QF8) return scores_fp8q(ka, q);
+  else return scores_split(ka, q, rope);
 }
 template <bool QF8>
-__device__ inline floatx16 scores_dma(uint32_t kaddr, const QOp<QF8> &q, const Rope &rope, const uint8_t *row,
+__device__ inline floatx16 scores_dma(KAddr ka, const QOp<QF8> &q, const Rope &rope, const uint8_t *row,
                                       uint32_t dst) {
-  if constexpr (QF8) return scores_fp8q_dma(kaddr, q, row, dst);
-  else return scores_split_dma(kaddr, q, rope, row, dst);
+  if constexpr (QF8) return scores_fp8q_dma(ka, q, row, dst);
+  else return scores_split_dma(ka, q, rope, row, dst);
 }
 
 // P of one stage: the E4M3 term (8 registers: 32 probabilities, one byte
@@ -569,14 +590,37 @@ __device__ inline POp<P8> get_p(const uint8_t *area) {
   return p;
 }
 
+// max(a, b, c) in one instruction.  fmaxf in the default IEEE mode first
+// quiets each input with a max against itself, doubling the work; NaN
+// scores have no meaning here, so the plain instruction suffices.
+__device__ inline float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// Maximum of the lane's 32 scores: a three-way tree, 16 instructions deep 4.
+__device__ inline float row_max(const floatx16 &s0, const floatx16 &s1) {
+  float t[11];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) t[i] = max3(s0[3 * i], s0[3 * i + 1], s0[3 * i + 2]);
+#pragma unroll
+  for (int i = 0; i < 5; ++i) t[5 + i] = max3(s1[3 * i], s1[3 * i + 1], s1[3 * i + 2]);
+  t[10] = max3(s0[15], s1[15], t[9]);
+  const float u0 = max3(t[0], t[1], t[2]), u1 = max3(t[3], t[4], t[5]), u2 = max3(t[6], t[7], t[8]);
+  return max3(max3(u0, u1, u2), t[10], t[10]);
+}
+
 // Group w (0..7) of the lane's 32 probabilities p' = 2^(score * sc2 - msub)
 // of one stage -- scores of tile half 0 in s0, half 1 in s1; masked scores
 // are -inf and give 0 -- packed as bytes w of the p.v B operand:
 // hi = E4M3(p') (round to nearest even), lo = E5M2(p' - hi).  Adds the fp32
-// sum of p' to sf and the sum of exactly the values fed to the products to sq.
+// sum of p' to sf: the row sum that normalises the output and gives the LSE
+// is taken before the conversion, as in flash attention, so each output is
+// the quantised weights' average divided by the exact weight sum -- within
+// the weights' own rounding (2^-7 relative with the remainder, 2^-4 without).
 template <bool P8>
 __device__ inline void p_group(const floatx16 &s0, const floatx16 &s1, int w, float sc2, float msub, POp<P8> &o,
-                               float &sq, float &sf) {
+                               float &sf) {
   float p[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -587,17 +631,12 @@ __device__ inline void p_group(const floatx16 &s0, const floatx16 &s1, int w, fl
   int hw = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
   hw = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], hw, true);
   o.hi[w] = hw;
-  const float2v h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
-  const float2v h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
-  if constexpr (P8) {
-    sq += (h01[0] + h01[1]) + (h23[0] + h23[1]);
-  } else {
+  if constexpr (!P8) {
+    const float2v h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+    const float2v h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
     int lw = __builtin_amdgcn_cvt_pk_bf8_f32(p[0] - h01[0], p[1] - h01[1], 0, false);
     lw = __builtin_amdgcn_cvt_pk_bf8_f32(p[2] - h23[0], p[3] - h23[1], lw, true);
     o.lo[w] = lw;
-    const float2v l01 = __builtin_amdgcn_cvt_pk_f32_bf8(lw, false);
-    const float2v l23 = __builtin_amdgcn_cvt_pk_f32_bf8(lw, true);
-    sq += ((h01[0] + l01[0]) + (h01[1] + l01[1])) + ((h23[0] + l23[0]) + (h23[1] + l23[1]));
   }
 }
 
@@ -775,8 +814,7 @@ attention_fp8_kernel(AttnArgs a) {
     floatx16 oacc[kDv / 32];
     zero_agprs(oacc);
     float mref = kNegInf;  // row reference (an integer, base 2): the accumulator's frame
-    float lsum_q = 0.f;  // sum of the probabilities as multiplied (hi + lo): normalises O
-    float lsum_f = 0.f;  // fp32 sum of the probabilities before conversion: gives the LSE
+    float lsum_f = 0.f;  // fp32 sum of the probabilities before conversion: normalises O, gives the LSE
     const int b = P.b;
     const int mt = P.mt;
     const bool complete = P.st_begin == 0 && P.st_end == P.stages;
@@ -807,9 +845,7 @@ attention_fp8_kernel(AttnArgs a) {
       wait_direct_loads();
       __syncthreads();
       const uint32_t tile = lds_base + buf * Tile8::kBytes;
-      const int ln = fresh_lane_id();
-      const int hh = ln >> 5;
-      const uint32_t kaddr = tile + 1024 * hh + 16 * tok_slot(ln & 31);
+      const int hh = fresh_lane_id() >> 5;
       // online softmax in base 2 on this lane's 32 tokens of head-row m.
       // Register r of half t holds token 64 s + 32 t + 4h + 8(r/4) + r%4; a
       // stage lies wholly inside every row window of the wave when
@@ -819,7 +855,7 @@ attention_fp8_kernel(AttnArgs a) {
       floatx16 s0;
       if (uu + 1 < hi) {
         const uint32_t nb = buf == kBufs - 1 ? 0 : buf + 1;
-        s0 = scores_dma<QF8>(kaddr, q, rope, stage_row(a, page, nx.s, nx.lmax, wave, &bad),
+        s0 = scores_dma<QF8>(k_addr(tile), q, rope, stage_row(a, page, nx.s, nx.lmax, wave, &bad),
                              stage_dst(lds_base + nb * Tile8::kBytes, wave));
         if (k == nst - 1) following = nx;
         if (uu + 2 < hi) {
@@ -827,9 +863,9 @@ attention_fp8_kernel(AttnArgs a) {
           page = page_of(nx);
         }
       } else {
-        s0 = scores<QF8>(kaddr, q, rope);
+        s0 = scores<QF8>(k_addr(tile), q, rope);
       }
-      floatx16 s1 = scores<QF8>(kaddr + Tile8::kHalfBytes, q, rope);
+      floatx16 s1 = scores<QF8>(k_addr(tile + Tile8::kHalfBytes), q, rope);
       // the pending stage's probabilities and first value blocks: their LDS
       // latency runs under the masking and the row maximum
       const uint32_t vt = prev_tile();
@@ -849,10 +885,8 @@ attention_fp8_kernel(AttnArgs a) {
           s1[r] = off + 32 < lim ? s1[r] : kNegInf;
         }
       }
-      float mx = kNegInf;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-      mx = fmaxf(mx, other_half(mx, hh)) * sc2;
+      float mx = row_max(s0, s1);
+      mx = max3(mx, other_half(mx, hh), mx) * sc2;
       // the stage ceiling; a row with nothing visible in the stage (all p'
       // are 0) takes the reference, or 0 before the row has one
       const bool vis = mx > kNegInf;
@@ -862,7 +896,7 @@ attention_fp8_kernel(AttnArgs a) {
       mref = started ? mref : (vis ? ms : kNegInf);   // nothing accumulated yet
       const float delta = (started || vis) ? ms - mref : 0.f;
       const float msub = ms - kPShift;
-      float sq = 0.f, sf = 0.f;
+      float sf = 0.f;
       POp<P8> pc;
       if constexpr (PREV) {
         // the pending p.v with this stage's probabilities between its
@@ -870,7 +904,7 @@ attention_fp8_kernel(AttnArgs a) {
         // value blocks each, V read two blocks ahead
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          p_group<P8>(s0, s1, c, sc2, msub, pc, sq, sf);
+          p_group<P8>(s0, s1, c, sc2, msub, pc, sf);
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const int d = 2 * c + j;
@@ -882,16 +916,15 @@ attention_fp8_kernel(AttnArgs a) {
         }
       } else {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) p_group<P8>(s0, s1, c, sc2, msub, pc, sq, sf);
+        for (int c = 0; c < 8; ++c) p_group<P8>(s0, s1, c, sc2, msub, pc, sf);
       }
       put_p<P8>(parea, pc);
       // the stage sums join the row sums here, in the reference frame before
       // any move; a row whose reference moves (the first stage of a piece
       // never does: mref was -inf) redoes it below
-      const float lq_old = lsum_q, lf_old = lsum_f;
+      const float lf_old = lsum_f;
       const int di = (int)__builtin_fmaxf(__builtin_fminf(delta, kMaxUp), -127.f);
       epend = kScaleOne + di;
-      lsum_q += __builtin_ldexpf(sq, di);
       lsum_f += __builtin_ldexpf(sf, di);
       const bool move = PREV && delta > kMaxUp;
       if (PREV && __any(move)) {
@@ -901,7 +934,6 @@ attention_fp8_kernel(AttnArgs a) {
         if (move) {
           mref = ms;
           epend = kScaleOne;
-          lsum_q = lq_old * alpha + sq;
           lsum_f = lf_old * alpha + sf;
         }
       }
@@ -919,10 +951,9 @@ attention_fp8_kernel(AttnArgs a) {
     u += nst;
     const bool more = u < hi;
     // finish the piece
-    const float ltot = lsum_q + other_half(lsum_q, h);
-    const float ltot_f = lsum_f + other_half(lsum_f, h);
+    const float ltot = lsum_f + other_half(lsum_f, h);
     const bool has = ltot > 0.f;
-    const float lse2 = has ? mref - kPShift + __builtin_amdgcn_logf(ltot_f) : kNegInf;
+    const float lse2 = has ? mref - kPShift + __builtin_amdgcn_logf(ltot) : kNegInf;
     // rows of this wave that exist (m < M)
     const int nrows = min(kWaveRows, a.M - (mt * kTileRows + wave * kWaveRows));
     uint8_t *stg = lds + kBufs * Tile8::kBytes + wave * Stage8::kWaveBytes;

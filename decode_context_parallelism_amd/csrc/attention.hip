@@ -167,9 +167,12 @@ attention_kernel(AttnArgs a) {
   if (blockIdx.x == 0 && threadIdx.x == 0) *a.ws_scale = a.out_scale;
   const int64_t U = a.work[0];
   if (U == 0) return;
-  const int64_t G = effective_groups(gridDim.x, U, DCPMLA_KV_BF16);
+  const Split sp = work_split(gridDim.x, U, a.n_mt, a.B, DCPMLA_KV_BF16);
+  const int64_t G = sp.T * sp.tm;
   if ((int64_t)blockIdx.x >= G) return;
   const int64_t w = xcd_group(blockIdx.x, G);
+  const int64_t team = w / sp.tm;
+  const int tpos = (int)(w - team * sp.tm);   // this group's head-row tile in each team item
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_char *)lds);
   int32_t *part = (int32_t *)(lds + 2 * Tile::kBytes + Stage::kBytes);
   const int nwork = 4 * a.B + 2;
@@ -183,14 +186,15 @@ attention_kernel(AttnArgs a) {
   wk.part = part;
   wk.row_len = a.row_len;
   wk.B = a.B;
-  wk.n_mt = a.n_mt;
+  wk.n_mt = sp.n_items;
+  wk.tm = sp.tm;
   wk.nwork = nwork;
-  wk.U = U;
-  wk.pc = piece_cost(DCPMLA_KV_BF16);
-  wk.C = total_cost(U, a.n_mt, a.B, wk.pc);
-  wk.hi = U;
-  const int64_t lo = wk.units_before(group_cost_lo(w, wk.C, G));
-  const int64_t hi = wk.units_before(group_cost_lo(w + 1, wk.C, G));
+  wk.U = sp.cols;
+  wk.pc = sp.pc;
+  wk.C = sp.C;
+  wk.hi = sp.cols;
+  const int64_t lo = wk.units_before(group_cost_lo(team, sp.C, sp.T));
+  const int64_t hi = wk.units_before(group_cost_lo(team + 1, sp.C, sp.T));
   if (lo >= hi) return;   // a cost range of piece overheads only
   wk.hi = hi;
   int32_t bad = 0;
@@ -210,7 +214,7 @@ attention_kernel(AttnArgs a) {
     const int ln = fresh_lane_id();
     const KernargArgs ka = kernarg_args();
     const int M = ka->M;
-    const int m = c.mt * kTileRows + wave * kWaveRows + (ln & 31);
+    const int m = (c.mt * sp.tm + tpos) * kTileRows + wave * kWaveRows + (ln & 31);
     const bool mvalid = m < M;
     // rows past M read row M-1 (a valid address) and are zeroed
     const int64_t qr = (int64_t)c.b * M + (mvalid ? m : M - 1);
@@ -256,7 +260,7 @@ attention_kernel(AttnArgs a) {
     float lsum = 0.f;    // sum of the BF16 probabilities fed to the PV MFMAs: normalises O
     float lsum_f = 0.f;  // fp32 sum of the same probabilities before rounding: gives the LSE
     const int b = P.b;
-    const int mt = P.mt;
+    const int mt = P.mt * sp.tm + tpos;   // head-row tile
     const bool complete = P.st_begin == 0 && P.st_end == P.stages;
     // this lane's head-row and its verify-row window
     const int m = mt * kTileRows + wave * kWaveRows + (fresh_lane_id() & 31);

@@ -219,13 +219,15 @@ struct Walk {
   const int32_t *work;       // global partition
   const int32_t *part;       // its LDS copy (PartLds), then the row lengths
   const int32_t *row_len;    // global row lengths
-  int B, n_mt, nwork;
+  int B, n_mt, nwork;        // n_mt: items per sequence in this walk (Split::n_items)
+  int tm;                    // groups per team: the partition's unit bases / tm are the walk's
   int64_t U, C, pc, hi;
 
   __device__ int32_t at(int i) const {
     if constexpr (PartLds) return __builtin_amdgcn_readfirstlane(part[i]);
     else return __builtin_amdgcn_readfirstlane(work[i]);
   }
+  __device__ int64_t base_at(int b) const { return (int64_t)at(work_unit_base_off() + b) / tm; }
   __device__ int32_t row_len_at(int i) const {
     if constexpr (PartLds) return part[nwork + i];
     else return row_len[i];
@@ -236,9 +238,9 @@ struct Walk {
     int blo = 0, bhi = B;   // seq_cost(blo) <= x < seq_cost(bhi)
     while (bhi - blo > 1) {
       const int mid = (blo + bhi) >> 1;
-      if (seq_cost(at(work_unit_base_off() + mid), n_mt, mid, pc) <= x) blo = mid; else bhi = mid;
+      if (seq_cost(base_at(mid), n_mt, mid, pc) <= x) blo = mid; else bhi = mid;
     }
-    const int64_t base = at(work_unit_base_off() + blo);
+    const int64_t base = base_at(blo);
     const int64_t st = at(work_stages_off(B) + blo);
     const int64_t rem = x - seq_cost(base, n_mt, blo, pc);
     const int64_t mt = rem / (st + pc);
@@ -255,12 +257,12 @@ struct Walk {
     int blo = 0, bhi = B;   // unit_base[blo] <= u < unit_base[bhi]
     while (bhi - blo > 1) {
       const int mid = (blo + bhi) >> 1;
-      if ((int64_t)at(work_unit_base_off() + mid) <= u) blo = mid; else bhi = mid;
+      if (base_at(mid) <= u) blo = mid; else bhi = mid;
     }
     Cursor c;
     c.b = blo;
     enter_seq(c);
-    const int64_t rem = u - at(work_unit_base_off() + blo);
+    const int64_t rem = u - base_at(blo);
     c.mt = (int)(rem / c.stages);
     c.s = (int)(rem - (int64_t)c.mt * c.stages);
     c.st_begin = c.s;

@@ -104,12 +104,6 @@ __host__ __device__ inline int64_t ws_total_bytes(int groups, int64_t rows) {
 __host__ __device__ inline int64_t min_units(int kv_dtype) {
   return kv_dtype == DCPMLA_KV_FP8_E4M3 ? 2 : 4;
 }
-__host__ __device__ inline int64_t effective_groups(int64_t launched, int64_t U, int kv_dtype) {
-  const int64_t mu = min_units(kv_dtype);
-  int64_t g = (U + mu - 1) / mu;
-  if (g < 1) g = 1;
-  return g < launched ? g : launched;
-}
 
 // Scheduling cost.  Besides its stages, every (sequence, head-row tile) item
 // costs piece_cost(kv_dtype) stage-equivalents for its query load and output
@@ -133,6 +127,35 @@ __host__ __device__ inline int64_t total_cost(int64_t U, int n_mt, int batch, in
 }
 __host__ __device__ inline int64_t seq_cost(int64_t unit_base_b, int n_mt, int b, int64_t pc) {
   return unit_base_b + pc * n_mt * (int64_t)b;
+}
+// Head-row tiles run in teams: tm = n_mt consecutive logical groups (which
+// share an XCD) walk the same columns -- (sequence, stage) -- in step, group
+// t * tm + p taking tile p of each, so a stage's KV pages come from HBM once
+// and the team's other tiles find them in that XCD's L2.  With fewer groups
+// than tiles, tm = 1 and each group walks (sequence, tile, stage) alone.  The
+// walk then sees n_mt / tm items per sequence of `stages` columns each; its
+// unit bases are the partition's unit bases divided by tm.
+struct Split {
+  int tm;           // groups per team
+  int n_items;      // items per sequence in a team's walk
+  int64_t T;        // teams that take work
+  int64_t cols;     // columns in the walk
+  int64_t pc;       // cost of a piece's query load and output
+  int64_t C;        // total cost of the walk
+};
+__host__ __device__ inline Split work_split(int64_t launched, int64_t U, int n_mt, int batch, int kv_dtype) {
+  Split s;
+  s.tm = launched >= n_mt ? n_mt : 1;
+  s.n_items = n_mt / s.tm;
+  s.cols = U / s.tm;
+  const int64_t mu = min_units(kv_dtype);
+  int64_t t = (s.cols + mu - 1) / mu;
+  if (t < 1) t = 1;
+  const int64_t tmax = launched / s.tm;
+  s.T = t < tmax ? t : tmax;
+  s.pc = piece_cost(kv_dtype);
+  s.C = total_cost(s.cols, s.n_items, batch, s.pc);
+  return s;
 }
 __host__ __device__ inline int64_t group_cost_lo(int64_t w, int64_t C, int64_t G) { return (w * C) / G; }
 // the group whose cost range holds position x (0 <= x < C)

@@ -189,19 +189,22 @@ __global__ void __launch_bounds__(256) merge_segments_kernel(
     }
     return;
   }
-  // the groups holding this item's first and last stage (cost positions
-  // x0 and x0 + stages - 1); when they differ, the first of them wrote its
-  // share to its slot 1 and each later one to its slot 0
-  const int64_t pc = piece_cost(kv_dtype);
-  const int64_t Geff = effective_groups(G, U, kv_dtype);
-  const int64_t C = total_cost(U, n_mt, B, pc);
-  const int64_t x0 = seq_cost(work[work_unit_base_off() + b], n_mt, b, pc) + (int64_t)mt * (stages + pc) + pc;
-  const int64_t w0 = cost_group(x0, C, Geff);
-  const int64_t w1 = cost_group(x0 + stages - 1, C, Geff);
-  if (w0 == w1) return;   // finished inside one workgroup
+  // the teams holding this item's first and last stage (cost positions x0
+  // and x0 + stages - 1 of the walk); when they differ, the tile's group in
+  // the first of them wrote its share to its slot 1 and each later one to
+  // its slot 0
+  const Split sp = work_split(G, U, n_mt, B, kv_dtype);
+  const int item = mt / sp.tm, tpos = mt - item * sp.tm;
+  const int64_t x0 = seq_cost(work[work_unit_base_off() + b] / sp.tm, sp.n_items, b, sp.pc) +
+                     (int64_t)item * (stages + sp.pc) + sp.pc;
+  const int64_t t0 = cost_group(x0, sp.C, sp.T);
+  const int64_t t1 = cost_group(x0 + stages - 1, sp.C, sp.T);
+  if (t0 == t1) return;   // finished inside one workgroup
   if (wave >= nrows) return;
-  const int n = (int)(w1 - w0 + 1);
-  auto src_of = [&](int k) { return (w0 + k) * kSlots + (k == 0 ? piece_slot(0) : piece_slot(1)); };
+  const int n = (int)(t1 - t0 + 1);
+  auto src_of = [&](int k) {
+    return ((t0 + k) * sp.tm + tpos) * kSlots + (k == 0 ? piece_slot(0) : piece_slot(1));
+  };
   const int pr0 = chunk * kMergeRows + wave;   // row index inside the tile (partial rows)
   // One pass with a running maximum: each batch's base-2 LSEs and partial
   // rows are requested together, the sums are rescaled when the maximum

@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--q-format", choices=("split", "fp8"), default="split",
                     help="FP8 cache: the exact two-term split of the BF16 query (default) or the "
                          "quantised FP8 query variant")
+    ap.add_argument("--p-format", choices=("split", "fp8"), default="split",
+                    help="FP8 cache: probabilities as two FP8 terms (E4M3 + E5M2 remainder, default) or "
+                         "one E4M3 term against a per-stage power-of-two scale")
     ap.add_argument("--row-boundary", choices=("causal", "block"), default="causal",
                     help="causal verify rows (default) or a bidirectional draft block "
                          "(every row sees the whole cache)")
@@ -84,6 +87,27 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
+
+
+def dtype_name(kv_format, q_format, p_format):
+    """Arithmetic type of the attention products: "bf16" where each runs as
+    BF16 or as two FP8 terms carrying BF16's precision, "fp8e4m3" where both
+    take one FP8 term, "fp8e4m3+bf16" where one does."""
+    if kv_format != "fp8_e4m3":
+        return "bf16"
+    n = (q_format == "fp8") + (p_format == "fp8")
+    return ("bf16", "fp8e4m3+bf16", "fp8e4m3")[n]
+
+
+def dtype_detail(kv_format, q_format, p_format):
+    if kv_format != "fp8_e4m3":
+        return "BF16 cache: q.k and p.v on the BF16 units, fp32 accumulation"
+    qk = ("q.k on the FP8 units as two E4M3 terms that sum exactly to the BF16 query"
+          if q_format == "split" else "q.k with the per-row E4M3-quantised query on the FP8 units")
+    pv = ("p.v on the FP8 units with the probabilities as an E4M3 term plus its E5M2 remainder"
+          if p_format == "split" else
+          "p.v with E4M3 probabilities against a per-stage power-of-two scale on the FP8 units")
+    return f"{qk}; {pv}; fp32 accumulation"
 
 
 def copy_calibration(mib):
@@ -268,11 +292,15 @@ def main():
     torch.cuda.set_device(0)
     dev_info = ops.device_info(0)
     w = make_config(args.config)
+    if w.kv_format != "fp8_e4m3" and (args.q_format == "fp8" or args.p_format == "fp8"):
+        print(f"--q-format fp8 and --p-format fp8 need an FP8 cache; {w.name} holds {w.kv_format}",
+              file=sys.stderr)
+        sys.exit(2)
     g = ops.Geometry(dcp_world=w.world, interleave=w.interleave, block_size=w.block_size,
                      qlen=w.qlen, num_heads=w.heads, batch=w.batch,
                      max_blocks_per_seq=w.block_table.shape[1], max_local_pages=w.max_local_pages,
                      kv_dtype=w.kv_format, num_blocks=w.num_blocks, groups=args.groups,
-                     row_boundary=args.row_boundary, q_format=args.q_format)
+                     row_boundary=args.row_boundary, q_format=args.q_format, p_format=args.p_format)
     dev = "cuda"
     q0 = torch.from_numpy(w.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     if w.kv_format == "fp8_e4m3":
@@ -471,23 +499,27 @@ def main():
         attn_timing = ("HIP events around K replays of a graph of every rank's attention launch, "
                        "back to back; per-rank split from the eager pass")
 
-    # roofline of the attention kernel against the published peaks.  The
-    # default path runs q.k as two E4M3 products on the FP8 units (twice the
-    # flops at twice the rate) and p.v on BF16, so its MFMA time is that of an
-    # all-BF16 kernel: the BF16 peak is the roofline.  The FP8-query variant
-    # runs q.k once at the FP8 rate: its roofline is the time-weighted mix of
-    # the two peaks.
-    peak_mfma = PEAK_MFMA_BF16_TFLOPS
-    if args.q_format == "fp8":
-        f_qk = sum(flops) * 576.0 / (576 + 512)
-        f_pv = sum(flops) - f_qk
-        peak_mfma = sum(flops) / (f_qk / PEAK_MFMA_FP8_TFLOPS + f_pv / PEAK_MFMA_BF16_TFLOPS)
+    # roofline of the attention kernel against the published peaks.  With an
+    # FP8 cache the default path runs q.k and p.v each as two FP8 products
+    # (the query, and the probabilities, split into two FP8 terms): twice the
+    # flops at twice the rate, so its MFMA time is that of an all-BF16 kernel
+    # and the BF16 peak is the roofline.  The FP8-query variant runs q.k once
+    # at the FP8 rate, the FP8-probability variant p.v; the roofline of a
+    # product taken once is the FP8 peak, and of the kernel the time-weighted
+    # mix of its two products' peaks.
+    fp8_cache = w.kv_format == "fp8_e4m3"
+    peak_qk = PEAK_MFMA_FP8_TFLOPS if fp8_cache and args.q_format == "fp8" else PEAK_MFMA_BF16_TFLOPS
+    peak_pv = PEAK_MFMA_FP8_TFLOPS if fp8_cache and args.p_format == "fp8" else PEAK_MFMA_BF16_TFLOPS
+    f_qk = sum(flops) * 576.0 / (576 + 512)
+    f_pv = sum(flops) - f_qk
+    peak_mfma = sum(flops) / (f_qk / peak_qk + f_pv / peak_pv)
     t_mfma = sum(flops) / (peak_mfma * 1e12)
     t_hbm = sum(alg_bytes) / (PEAK_HBM_GBS * 1e9)
     tflops = sum(flops) / (float(per_rank_ms.sum()) * 1e-3) / 1e12
     gbs = sum(alg_bytes) / (float(per_rank_ms.sum()) * 1e-3) / 1e9
     digest = source_digest()
-    traffic, traffic_src = read_traffic(w.name, digest)
+    variant = ("fp8_query_" if args.q_format == "fp8" else "") + ("fp8_p_" if args.p_format == "fp8" else "")
+    traffic, traffic_src = read_traffic(variant + w.name, digest)
     if t_mfma >= t_hbm:
         roof = {"bound": "mfma", "achieved": tflops, "peak": peak_mfma, "unit": "TFLOP/s",
                 "frac": tflops / peak_mfma}
@@ -496,7 +528,9 @@ def main():
                 "frac": gbs / PEAK_HBM_GBS}
     roof["traffic"] = traffic
     roof.update({
-        "kernel": "attention_kernel (segmented split-KV MLA, one rank per launch)",
+        "kernel": (("attention_fp8_kernel" if fp8_cache else "attention_kernel") +
+                   " (segmented split-KV MLA, one rank per launch)"),
+        "peak_qk_tflops": peak_qk, "peak_pv_tflops": peak_pv,
         "avg_launch_ms": avg_launch_ms, "launches": int(attn_ms.size), "launch_timing": attn_timing,
         "algorithmic_flops_per_launch": sum(flops) / W,
         "algorithmic_bytes_per_launch": sum(alg_bytes) / W,
@@ -505,7 +539,7 @@ def main():
         "kernel_source_sha256": digest,
     })
     # the matrix units' measured busy share of the launch, at the clock they ran
-    busy, busy_src = read_mfma_busy(w.name, digest)
+    busy, busy_src = read_mfma_busy(variant + w.name, digest)
     roof["mfma_busy_counters"] = busy if busy is not None else busy_src
 
     clk_ghz = dev_info["clock_khz"] / 1e6
@@ -528,16 +562,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if args.q_format == "split" else "fp8e4m3+bf16",
-        "dtype_detail": ("q.k on the FP8 units as two E4M3 terms that sum exactly to the BF16 query "
-                         "(FP8 cache), p.v BF16, fp32 accumulation" if args.q_format == "split" else
-                         "q.k with the E4M3-quantised query on the FP8 units, p.v BF16, fp32 accumulation"),
+        "dtype": dtype_name(w.kv_format, args.q_format, args.p_format),
+        "dtype_detail": dtype_detail(w.kv_format, args.q_format, args.p_format),
         "data": "synthetic",
         "config": {"workload": w.name, "dcp_world": W, "interleave": w.interleave,
                    "batch": w.batch, "qlen": w.qlen, "heads": w.heads,
                    "block_size": w.block_size, "kv_cache": w.kv_format,
                    "kv_tokens_per_step": kv_tokens, "ranks_per_step": W, "input_sets": n_sets,
                    "row_boundary": args.row_boundary, "merge": args.merge, "q_format": args.q_format,
+                   "p_format": args.p_format,
                    "streams": 1 if args.no_graph else args.streams},
         "verify_rows_per_s": w.batch * w.qlen / (ms_per_step * 1e-3),
         "step_mode": step_mode,

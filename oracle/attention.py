@@ -33,11 +33,13 @@ D_V = 512
 LN2 = np.log(2.0)
 
 
-def attend(q_rows: np.ndarray, keys: np.ndarray, softmax_scale: float):
+def attend(q_rows: np.ndarray, keys: np.ndarray, softmax_scale: float, abs_values: bool = False):
     """Softmax attention of ``q_rows[H, 576]`` over ``keys[n, 576]`` (float64).
 
     Returns ``(out[H, 512], lse[H])`` with natural-log LSE; n = 0 gives
-    ``(0, -inf)``.
+    ``(0, -inf)``.  With ``abs_values`` the values are |v| under the same
+    weights: sum_t w_t |v_t|, the scale of the error that rounding each weight
+    to a relative precision puts on the output.
     """
     q_rows = np.asarray(q_rows, dtype=np.float64)
     keys = np.asarray(keys, dtype=np.float64)
@@ -49,7 +51,8 @@ def attend(q_rows: np.ndarray, keys: np.ndarray, softmax_scale: float):
     e = np.exp(scores - mx)
     z = e.sum(axis=1, keepdims=True)
     lse = (mx + np.log(z))[:, 0]
-    out = (e / z) @ keys[:, :D_V]
+    vals = keys[:, :D_V]
+    out = (e / z) @ (np.abs(vals) if abs_values else vals)
     return out, lse
 
 
@@ -62,7 +65,7 @@ def _visible_positions(ctx, qlen, i, world, interleave, rank, boundary):
 
 def verify_attention(q: np.ndarray, latents, ctx_lens, softmax_scale: float, *,
                      world: int = 1, interleave: int = 1, rank=None, rows=None,
-                     boundary=layout.verify_row_boundary):
+                     boundary=layout.verify_row_boundary, abs_values: bool = False):
     """Causal-verify attention for selected rows, globally or for one rank.
 
     ``q``: float64 ``[B, qlen, H, 576]``.  ``latents``: callable
@@ -70,7 +73,8 @@ def verify_attention(q: np.ndarray, latents, ctx_lens, softmax_scale: float, *,
     latent rows of sequence b.  ``rank=None`` attends to every visible global
     position; an int restricts to the positions that rank owns.  ``rows``:
     iterable of ``(b, i)``; default all.  ``boundary`` is the row-boundary
-    rule (replaceable only by the negative-control tests).
+    rule (replaceable only by the negative-control tests).  ``abs_values``:
+    see ``attend``.
 
     Returns ``(out[B, qlen, H, 512], lse[B, qlen, H])``; rows not selected
     are NaN.
@@ -83,7 +87,8 @@ def verify_attention(q: np.ndarray, latents, ctx_lens, softmax_scale: float, *,
     for b, i in rows:
         pos = _visible_positions(int(ctx_lens[b]), qlen, i, world, interleave, rank, boundary)
         keys = latents(b, pos) if pos.shape[0] else np.zeros((0, D_QK))
-        out[b, i], lse[b, i] = attend(q[b, i], keys, softmax_scale)
+        out[b, i], lse[b, i] = (attend(q[b, i], keys, softmax_scale, abs_values=True) if abs_values
+                                else attend(q[b, i], keys, softmax_scale))
     return out, lse
 
 

@@ -95,6 +95,40 @@ def test_single_visible_token():
     assert np.allclose(lse[0, 0], scale * q[0, 0] @ X[0], rtol=0, atol=1e-12)
 
 
+def test_abs_value_attention_brute_force():
+    # sum_t w_t |v_t| with the softmax weights written out as loops
+    q, X = _tiny(11, qlen=2, H=2, ctx=9)
+    scale = 0.09
+    out, _ = A.verify_attention(q, _latents_of(X), [9], scale, abs_values=True)
+    for i in range(2):
+        g = 9 - 2 + 1 + i
+        for h in range(2):
+            s = [scale * float(np.dot(q[0, i, h], X[t])) for t in range(g)]
+            m = max(s)
+            e = [math.exp(v - m) for v in s]
+            z = sum(e)
+            want = [sum(e[t] / z * abs(X[t, d]) for t in range(g)) for d in range(512)]
+            assert np.abs(out[0, i, h] - np.array(want)).max() < 1e-12
+
+
+def test_abs_value_attention_bounds_and_special_cases():
+    q, X = _tiny(12, qlen=3, H=3, ctx=40)
+    scale = 0.11
+    lat = _latents_of(X)
+    out, lse = A.verify_attention(q, lat, [40], scale)
+    oabs, lse_abs = A.verify_attention(q, lat, [40], scale, abs_values=True)
+    assert np.array_equal(lse, lse_abs)                 # same weights
+    assert (np.abs(out) <= oabs + 1e-15).all()           # triangle inequality
+    # one visible token: |v_0|
+    o1, _ = A.verify_attention(q, lat, [3], scale, abs_values=True)
+    assert np.array_equal(o1[0, 0], np.broadcast_to(np.abs(X[0, :512]), (3, 512)))
+    # non-negative values: the two coincide
+    latp = _latents_of(np.abs(X))
+    a, _ = A.verify_attention(q, latp, [40], scale)
+    b, _ = A.verify_attention(q, latp, [40], scale, abs_values=True)
+    assert np.abs(a - b).max() < 1e-12
+
+
 def merge_identity_error(seed, W, S, qlen=3, H=3, ctx=53, scale=0.07):
     q, X = _tiny(seed, qlen, H, ctx)
     lat = _latents_of(X)

@@ -19,14 +19,15 @@
 // Inside a workgroup: 4 waves x 32 head-rows, one wave per SIMD; each wave
 // keeps its query rows in registers (128 VGPRs; the rope step of the split
 // query waits in LDS) and its 512 x 32 output accumulator in 256 AGPRs.  LDS
-// holds three stage tiles (36 KiB each: two halves of 32 tokens, each 36
-// blocks [32 token slots][16 bytes]), filled by direct global->LDS loads, and
-// per wave a staging area that holds the pending stage's probabilities and
-// the rope query until the piece ends.
+// holds three stage tiles (36 KiB each: two halves of 32 tokens, each nine
+// 64-dim steps of two 1 KiB units [4 blocks of 16 dims][16 token slots][16
+// bytes]), filled by direct global->LDS loads, and per wave a staging area
+// that holds the pending stage's probabilities and the rope query until the
+// piece ends.
 //
 // The stage loop is software-pipelined by one stage.  Stage u: one barrier
 // (tile u has landed, every wave is done with tile u-2), the scores of tile u
-// with the loads of tile u+1 issued between the first block's products, then
+// with the loads of tile u+1 issued between the products, then
 // the p.v products of stage u-1 in eight chunks with the softmax of stage u
 // between them, so the exponentials and conversions issue while the matrix
 // unit is busy.  The tile being loaded, the tile being scored and the tile
@@ -50,16 +51,24 @@ using namespace attn;
 
 constexpr int kStage = kStageTokensFp8;   // tokens per stage (two 32-token score tiles)
 
-// In an odd block (dims 16 (2j + 1) .. + 15) the slots are stored XOR 8: the
-// two 16-lane groups of a transposing read take blocks 2j and 2j + 1 at the
-// same slots, 512 bytes apart -- the same banks -- and the XOR moves the
-// second group into the other half of the 256-byte bank window.
+// A tile half (32 tokens x 576 dims) is nine 64-dim steps of 2 KiB; a step is
+// two 1 KiB units, slots 0..15 then 16..31; a unit is four 256-byte blocks of
+// 16 dims, each [16 slots][16 bytes].  A unit is what one direct load fills:
+// 16 token rows x 64 contiguous bytes, so each load touches 16 64-byte
+// segments of the cache.  In an odd block (dims 16 (2j + 1) .. + 15) slot s
+// sits at position s ^ 8: the two 16-lane groups of a transposing read take
+// blocks 2j and 2j + 1 at the same slots, 256 bytes apart -- the same banks
+// -- and the XOR moves the second group into the other half of the 256-byte
+// bank window.
 struct Tile8 {
   static constexpr int kRow = 16;                        // bytes of one token slot in a block
-  static constexpr int kBlock = 32 * kRow;               // 32 slots x 16 dims
-  static constexpr int kHalfBytes = kKBlocks * kBlock;   // 32 tokens x 576 dims
+  static constexpr int kBlock = 16 * kRow;               // 16 slots x 16 dims
+  static constexpr int kUnit = 4 * kBlock;               // 16 slots x 64 dims: one direct load
+  static constexpr int kStep = 2 * kUnit;                // 32 slots x 64 dims
+  static constexpr int kHalfBytes = kDqk / 64 * kStep;   // 32 tokens x 576 dims
   static constexpr int kBytes = 2 * kHalfBytes;          // one stage
 };
+static_assert(Tile8::kHalfBytes == kKBlocks * 16 * 32, "a tile half holds 32 tokens x 576 dims");
 constexpr int kBufs = 3;
 typedef Staging<2> Stage8;   // BF16 outputs and fp16 partials
 
@@ -78,12 +87,14 @@ constexpr int kScaleOne = 127;   // E8M0 encoding of 2^0
 // ------------------------------------------------------------ staging
 //
 // Direct loads of a stage: waves 0, 1 fill tile half 0 (tokens 0..31), waves
-// 2, 3 half 1 (32..63).  Load k (k < 9) of wave w fills half bytes
-// [1024 j, 1024 j + 1024) with j = (w & 1) + 2k: lane l writes 16 bytes at
-// 1024 j + 16 l, i.e. slot l % 32 of block 2j (l < 32) or 2j + 1 (l >= 32),
-// so every lane reads 16-byte pieces of one token row for the whole stage:
-// the token of slot l % 32, XOR 8 in the odd blocks.
-__device__ inline int load_slot(int lane) { return (lane & 31) ^ (8 * (lane >> 5)); }
+// 2, 3 half 1 (32..63).  Load k (k < 9) of wave w fills unit w & 1 of step k:
+// lane l writes 16 bytes at 2048 k + 1024 (w & 1) + 16 l, i.e. position l % 16
+// of block 4k + l / 16, which holds slot 16 (w & 1) + l % 16, XOR 8 in the odd
+// blocks.  So every lane reads one token row for the whole stage, 16 bytes at
+// 64 k + 16 (l / 16), and four lanes read each 64-byte segment.
+__device__ inline int load_slot(int wave, int lane) {
+  return (16 * (wave & 1) + (lane & 15)) ^ (8 * ((lane >> 4) & 1));
+}
 __device__ inline int load_half(int wave) { return wave >> 1; }
 
 // Address of this lane's token row for stage s (page id fetched one stage
@@ -99,7 +110,7 @@ __device__ inline int load_half(int wave) { return wave >> 1; }
 __device__ inline const uint8_t *stage_row(const AttnArgs &a, int32_t page, int s, int lmax, int wave,
                                            bool *bad) {
   const int lane = fresh_lane_id();
-  const int t = s * kStage + 32 * load_half(wave) + tok_slot(load_slot(lane));
+  const int t = s * kStage + 32 * load_half(wave) + tok_slot(load_slot(wave, lane));
   const bool in_seq = t < lmax;
   const bool ok = page >= 0 && (int64_t)page < a.num_pages;
   *bad = *bad || __any(in_seq && !ok);   // wave-uniform: a scalar flag
@@ -108,19 +119,20 @@ __device__ inline const uint8_t *stage_row(const AttnArgs &a, int32_t page, int 
     const int64_t r = ((int64_t)page << a.page_shift) + (t & ((1 << a.page_shift) - 1));
     row = a.pool + r * kDqk;
   }
-  return row + 32 * (wave & 1) + 16 * (lane >> 5);
+  return row + 16 * (lane >> 4);
 }
 
 __device__ inline int32_t fetch_page(const AttnArgs &a, const int32_t *pt, int s, int lmax, int wave) {
-  const int t = s * kStage + 32 * load_half(wave) + tok_slot(load_slot(fresh_lane_id()));
+  const int t = s * kStage + 32 * load_half(wave) + tok_slot(load_slot(wave, fresh_lane_id()));
   return pt[t < lmax ? (t >> a.page_shift) : 0];
 }
 
 // This wave's nine loads of a stage: row bytes 64 k + (lane part, in row) to
 // tile bytes half * 18 KiB + 1024 (w & 1) + 2048 k.  One M0 save/restore.
 __device__ inline uint32_t stage_dst(uint32_t tile_lds, int wave_s) {
-  return tile_lds + load_half(wave_s) * Tile8::kHalfBytes + 1024 * (wave_s & 1);
+  return tile_lds + load_half(wave_s) * Tile8::kHalfBytes + Tile8::kUnit * (wave_s & 1);
 }
+static_assert(Tile8::kStep == 2048, "the direct loads and score reads step M0 and offsets by 2048");
 __device__ inline void issue_stage(uint32_t tile_lds, const uint8_t *row, int wave_s) {
   const uint32_t dst = stage_dst(tile_lds, wave_s);
   uint32_t saved;
@@ -166,8 +178,9 @@ __device__ inline void issue_stage(uint32_t tile_lds, const uint8_t *row, int wa
 // PV, value-dim block d: the A operand V^T holds, for lane (dim 32d + l % 32,
 // half h = l / 32), the 32 tokens of pattern h of the stage -- in each
 // 16-token group the eight tokens {4h..4h+3, 8+4h..8+4h+3}, which sit in
-// slots 8h..8h+7 (XOR 8 in the odd blocks) -- in the order (half 0 group 0, half 0 group 1, half 1
-// group 0, half 1 group 1), eight per transposing read.  tr_b8: within a
+// slots 8h..8h+7 (positions XOR 8 in the odd blocks) -- in the order (half 0
+// group 0, half 0 group 1, half 1 group 0, half 1 group 1), eight per
+// transposing read; dims 32d .. 32d + 31 are blocks 2d, 2d + 1 of step d / 2.  tr_b8: within a
 // 16-lane group, result lane 8a + b gets byte b of the 8-byte rows loaded by
 // lanes a, a + 2, ..., a + 14.  The same k order on the P^T side is
 // registers 0..15 of the half-0 score tile, then 0..15 of the half-1 tile:
@@ -186,11 +199,11 @@ __device__ inline VOff v_offsets(int lane) {
   return o;
 }
 __device__ inline int8v lds_v(uint32_t tile, VOff o, int d) {
-  const uint32_t p = tile + o.base + 2 * d * Tile8::kBlock;
+  const uint32_t p = tile + o.base + (d >> 1) * Tile8::kStep + (d & 1) * 2 * Tile8::kBlock;
   const int2v r0 = tr8(p);
-  const int2v r1 = tr8(p + 16 * Tile8::kRow);
+  const int2v r1 = tr8(p + Tile8::kUnit);
   const int2v r2 = tr8(p + Tile8::kHalfBytes);
-  const int2v r3 = tr8(p + Tile8::kHalfBytes + 16 * Tile8::kRow);
+  const int2v r3 = tr8(p + Tile8::kHalfBytes + Tile8::kUnit);
   int8v v;
   v[0] = r0[0]; v[1] = r0[1]; v[2] = r1[0]; v[3] = r1[1];
   v[4] = r2[0]; v[5] = r2[1]; v[6] = r3[0]; v[7] = r3[1];
@@ -240,10 +253,10 @@ __device__ inline Rope get_rope(const uint8_t *area) {
 }
 
 // This lane's two tile addresses for the score reads of step 0 of a tile
-// half: A-operand row r = lane % 32 is token r of the half, found in slot
-// tok_slot(r) of the even blocks and tok_slot(r) ^ 8 of the odd ones; lane
-// half hh reads blocks 2 hh and 2 hh + 1 of each 4-block step (step st adds
-// 2048 st).
+// half: A-operand row r = lane % 32 is token r of the half, slot
+// sl = tok_slot(r) in unit sl / 16, at position sl % 16 of the even blocks and
+// (sl % 16) ^ 8 of the odd ones; lane half hh reads blocks 2 hh and 2 hh + 1
+// of each step (step st adds 2048 st).
 struct KAddr {
   uint32_t a0, a1;
 };
@@ -251,8 +264,9 @@ __device__ inline KAddr k_addr(uint32_t half_base) {
   const int ln = fresh_lane_id();
   const int sl = tok_slot(ln & 31), hh = ln >> 5;
   KAddr k;
-  k.a0 = half_base + 1024 * hh + Tile8::kRow * sl;
-  k.a1 = half_base + 1024 * hh + Tile8::kBlock + Tile8::kRow * (sl ^ 8);
+  const uint32_t u = half_base + Tile8::kUnit * (sl >> 4) + 2 * Tile8::kBlock * hh;
+  k.a0 = u + Tile8::kRow * (sl & 15);
+  k.a1 = u + Tile8::kBlock + Tile8::kRow * ((sl ^ 8) & 15);
   return k;
 }
 
@@ -327,98 +341,6 @@ __device__ inline floatx16 scores_split(KAddr ka, const QOp<false> &q, const Rop
   return acc;
 }
 
-// The same with this wave's nine direct loads of the next tile (issue_stage
-// below) issued one after each step's products: issued back to back they
-// stall the wave in the memory pipe for about a thousand cycles, which the
-// products now cover.
-__device__ inline floatx16 scores_split_dma(KAddr ka, const QOp<false> &q, const Rope &rope,
-                                            const uint8_t *row, uint32_t dst) {
-  floatx16 acc;
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %[m0s], m0\n\t"
-      "s_mov_b32 m0, %[dst]\n\t"
-      "s_waitcnt lgkmcnt(0)\n\t"
-      "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
-      "ds_read_b128 v[244:247], %[a1] offset:0\n\t"
-      "ds_read_b128 v[248:251], %[a0] offset:2048\n\t"
-      "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q1], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g0], off\n\t"
-      "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
-      "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q2], %[acc]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q3], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g1], off\n\t"
-      "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
-      "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q4], %[acc]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g2], off\n\t"
-      "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
-      "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q7], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g3], off\n\t"
-      "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
-      "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q8], %[acc]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q9], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g4], off\n\t"
-      "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
-      "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q10], %[acc]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q11], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g5], off\n\t"
-      "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
-      "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q12], %[acc]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q13], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g6], off\n\t"
-      "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
-      "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q14], %[acc]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q15], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g7], off\n\t"
-      "s_add_u32 m0, m0, 2048\n\t"
-      "s_waitcnt lgkmcnt(0)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q16], %[acc]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q17], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g8], off\n\t"
-      "s_mov_b32 m0, %[m0s]\n\t"
-      "s_nop 15\n\t"
-      "s_nop 3\n\t"
-      : [acc] "=&v"(acc), [m0s] "=&s"(saved)
-      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]), [q3] "v"(q.v[3]),
-        [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]), [q8] "v"(q.v[8]),
-        [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]),
-        [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(rope.hi),
-        [q17] "v"(rope.lo),
-        [g0] "v"(row), [g1] "v"(row + 64), [g2] "v"(row + 128), [g3] "v"(row + 192),
-        [g4] "v"(row + 256), [g5] "v"(row + 320), [g6] "v"(row + 384), [g7] "v"(row + 448),
-        [g8] "v"(row + 512), [dst] "s"(dst)
-      : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242",
-        "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253",
-        "v254", "v255", "memory", "scc");
-  return acc;
-}
-
 // The quantised query: the hi terms alone.
 __device__ inline floatx16 scores_fp8q(KAddr ka, const QOp<true> &q) {
   floatx16 acc;
@@ -471,9 +393,166 @@ __device__ inline floatx16 scores_fp8q(KAddr ka, const QOp<true> &q) {
   return acc;
 }
 
-// The quantised query with the next tile's direct loads, one per step.
-__device__ inline floatx16 scores_fp8q_dma(KAddr ka, const QOp<true> &q, const uint8_t *row,
-                                           uint32_t dst) {
+// The same with this wave's direct loads of the next tile: loads 0..4 after
+// the products of steps 0, 2, 4, 6, 8 of the first score block, loads 5..8
+// after steps 1, 3, 5, 7 of the second (load k reads row bytes 64 k on, into
+// M0 + 2048 k).  A load stalls the wave in the memory pipe for up to a
+// hundred cycles; between products the matrix unit keeps working meanwhile.
+// The instruction's immediate offset would move the LDS destination as well
+// as the source, so each load takes its own address.
+__device__ inline floatx16 scores_split_dma0(KAddr ka, const QOp<false> &q, const Rope &rope,
+                                             const uint8_t *row, uint32_t dst) {
+  floatx16 acc;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[m0s], m0\n\t"
+      "s_mov_b32 m0, %[dst]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:0\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:2048\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q1], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g0], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q2], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q3], %[acc]\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q4], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g1], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q7], %[acc]\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q8], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q9], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g2], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q10], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q11], %[acc]\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q12], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q13], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g3], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q14], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q15], %[acc]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q16], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q17], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g4], off\n\t"
+      "s_mov_b32 m0, %[m0s]\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3\n\t"
+      : [acc] "=&v"(acc), [m0s] "=&s"(saved)
+      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
+        [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
+        [q8] "v"(q.v[8]), [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]),
+        [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(rope.hi), [q17] "v"(rope.lo),
+        [g0] "v"(row + 0), [g1] "v"(row + 64), [g2] "v"(row + 128), [g3] "v"(row + 192), [g4] "v"(row + 256),
+        [dst] "s"(dst)
+      : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244",
+        "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "scc");
+  return acc;
+}
+
+__device__ inline floatx16 scores_split_dma1(KAddr ka, const QOp<false> &q, const Rope &rope,
+                                             const uint8_t *row, uint32_t dst) {
+  floatx16 acc;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[m0s], m0\n\t"
+      "s_add_u32 m0, %[dst], 10240\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:0\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:2048\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q1], %[acc]\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q2], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q3], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g0], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q4], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q7], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g1], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q8], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q9], %[acc]\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q10], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q11], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g2], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q12], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q13], %[acc]\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q14], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q15], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g3], off\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q16], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q17], %[acc]\n\t"
+      "s_mov_b32 m0, %[m0s]\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3\n\t"
+      : [acc] "=&v"(acc), [m0s] "=&s"(saved)
+      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
+        [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
+        [q8] "v"(q.v[8]), [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]),
+        [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(rope.hi), [q17] "v"(rope.lo),
+        [g0] "v"(row + 320), [g1] "v"(row + 384), [g2] "v"(row + 448), [g3] "v"(row + 512), [dst] "s"(dst)
+      : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244",
+        "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "scc");
+  return acc;
+}
+
+// The quantised query with the next tile's direct loads, split the same way.
+__device__ inline floatx16 scores_fp8q_dma0(KAddr ka, const QOp<true> &q, const uint8_t *row, uint32_t dst) {
   floatx16 acc;
   uint32_t saved;
   asm volatile(
@@ -492,59 +571,112 @@ __device__ inline floatx16 scores_fp8q_dma(KAddr ka, const QOp<true> &q, const u
       "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q1], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g1], off\n\t"
-      "s_add_u32 m0, m0, 2048\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q2], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g2], off\n\t"
+      "global_load_lds_dwordx4 %[g1], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
       "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
       "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q3], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g3], off\n\t"
-      "s_add_u32 m0, m0, 2048\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q4], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g4], off\n\t"
+      "global_load_lds_dwordx4 %[g2], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g5], off\n\t"
-      "s_add_u32 m0, m0, 2048\n\t"
       "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
       "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g6], off\n\t"
+      "global_load_lds_dwordx4 %[g3], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q7], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g7], off\n\t"
-      "s_add_u32 m0, m0, 2048\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q8], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g8], off\n\t"
+      "global_load_lds_dwordx4 %[g4], off\n\t"
       "s_mov_b32 m0, %[m0s]\n\t"
       "s_nop 15\n\t"
       "s_nop 3\n\t"
       : [acc] "=&v"(acc), [m0s] "=&s"(saved)
-      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]), [q3] "v"(q.v[3]),
-        [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]), [q8] "v"(q.v[8]),
-        [g0] "v"(row), [g1] "v"(row + 64), [g2] "v"(row + 128), [g3] "v"(row + 192),
-        [g4] "v"(row + 256), [g5] "v"(row + 320), [g6] "v"(row + 384), [g7] "v"(row + 448),
-        [g8] "v"(row + 512), [dst] "s"(dst)
-      : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242",
-        "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253",
-        "v254", "v255", "memory", "scc");
+      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
+        [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
+        [q8] "v"(q.v[8]), [g0] "v"(row + 0), [g1] "v"(row + 64), [g2] "v"(row + 128), [g3] "v"(row + 192),
+        [g4] "v"(row + 256), [dst] "s"(dst)
+      : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244",
+        "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "scc");
+  return acc;
+}
+
+__device__ inline floatx16 scores_fp8q_dma1(KAddr ka, const QOp<true> &q, const uint8_t *row, uint32_t dst) {
+  floatx16 acc;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[m0s], m0\n\t"
+      "s_add_u32 m0, %[dst], 10240\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:0\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:2048\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q1], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g0], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q2], %[acc]\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q3], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g1], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q4], %[acc]\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g2], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q7], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g3], off\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q8], %[acc]\n\t"
+      "s_mov_b32 m0, %[m0s]\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3\n\t"
+      : [acc] "=&v"(acc), [m0s] "=&s"(saved)
+      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
+        [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
+        [q8] "v"(q.v[8]), [g0] "v"(row + 320), [g1] "v"(row + 384), [g2] "v"(row + 448), [g3] "v"(row + 512),
+        [dst] "s"(dst)
+      : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244",
+        "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "scc");
   return acc;
 }
 
@@ -553,11 +685,16 @@ __device__ inline floatx16 scores(KAddr ka, const QOp<QF8> &q, const Rope &rope)
   if constexpr (QF8) return scores_fp8q(ka, q);
   else return scores_split(ka, q, rope);
 }
-template <bool QF8>
+template <bool QF8, int Part>
 __device__ inline floatx16 scores_dma(KAddr ka, const QOp<QF8> &q, const Rope &rope, const uint8_t *row,
                                       uint32_t dst) {
-  if constexpr (QF8) return scores_fp8q_dma(ka, q, row, dst);
-  else return scores_split_dma(ka, q, rope, row, dst);
+  if constexpr (QF8) {
+    if constexpr (Part == 0) return scores_fp8q_dma0(ka, q, row, dst);
+    else return scores_fp8q_dma1(ka, q, row, dst);
+  } else {
+    if constexpr (Part == 0) return scores_split_dma0(ka, q, rope, row, dst);
+    else return scores_split_dma1(ka, q, rope, row, dst);
+  }
 }
 
 // P of one stage: the E4M3 term (8 registers: 32 probabilities, one byte
@@ -621,13 +758,16 @@ __device__ inline float row_max(const floatx16 &s0, const floatx16 &s1) {
 template <bool P8>
 __device__ inline void p_group(const floatx16 &s0, const floatx16 &s1, int w, float sc2, float msub, POp<P8> &o,
                                float &sf) {
-  float p[4];
+  float x[4], p[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const float sv = w < 4 ? s0[4 * w + e] : s1[4 * (w - 4) + e];
-    p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, sc2, -msub));
-    sf += p[e];
+    x[e] = __builtin_fmaf(sv, sc2, -msub);
   }
+  // the four exponentials issue back to back, not each behind its fma
+#pragma unroll
+  for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(x[e]);
+  sf += (p[0] + p[1]) + (p[2] + p[3]);
   int hw = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
   hw = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], hw, true);
   o.hi[w] = hw;
@@ -855,12 +995,14 @@ attention_fp8_kernel(AttnArgs a) {
       // stage lies wholly inside every row window of the wave when
       // rlen - 64 s - 4h > 59 on all lanes.
       const int lim = rlen - s * kStage - 4 * hh;
-      // the first score block also issues the next unit's tile loads
-      floatx16 s0;
+      // the score blocks also issue the next unit's tile loads
+      floatx16 s0, s1;
       if (uu + 1 < hi) {
         const uint32_t nb = buf == kBufs - 1 ? 0 : buf + 1;
-        s0 = scores_dma<QF8>(k_addr(tile), q, rope, stage_row(a, page, nx.s, nx.lmax, wave, &bad),
-                             stage_dst(lds_base + nb * Tile8::kBytes, wave));
+        const uint8_t *nrow = stage_row(a, page, nx.s, nx.lmax, wave, &bad);
+        const uint32_t ndst = stage_dst(lds_base + nb * Tile8::kBytes, wave);
+        s0 = scores_dma<QF8, 0>(k_addr(tile), q, rope, nrow, ndst);
+        s1 = scores_dma<QF8, 1>(k_addr(tile + Tile8::kHalfBytes), q, rope, nrow, ndst);
         if (k == nst - 1) following = nx;
         if (uu + 2 < hi) {
           nx = wk.advance(nx, uu + 2);
@@ -868,8 +1010,8 @@ attention_fp8_kernel(AttnArgs a) {
         }
       } else {
         s0 = scores<QF8>(k_addr(tile), q, rope);
+        s1 = scores<QF8>(k_addr(tile + Tile8::kHalfBytes), q, rope);
       }
-      floatx16 s1 = scores<QF8>(k_addr(tile + Tile8::kHalfBytes), q, rope);
       // the pending stage's probabilities and first value blocks: their LDS
       // latency runs under the masking and the row maximum
       const uint32_t vt = prev_tile();

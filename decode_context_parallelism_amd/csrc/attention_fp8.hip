@@ -26,20 +26,22 @@
 // piece ends.
 //
 // The stage loop is software-pipelined by one stage.  Stage u: one barrier
-// (tile u has landed, every wave is done with tile u-2), the scores of tile u
-// with the loads of tile u+1 issued between the products, then
-// the p.v products of stage u-1 in eight chunks with the softmax of stage u
-// between them, so the exponentials and conversions issue while the matrix
-// unit is busy.  The tile being loaded, the tile being scored and the tile
+// (tile u has landed, every wave is done with tile u-2), the scores of tile
+// half 0 with the loads of tile u+1 issued between the products, the scores
+// of tile half 1 with the softmax of half 0 between the products, then the
+// p.v products of stage u-1 in eight chunks with the softmax of half 1
+// between them: the exponentials and conversions issue while the matrix unit
+// is busy.  The tile being loaded, the tile being scored and the tile
 // whose p.v is pending are three different buffers.  No memory-counter wait
 // falls between a tile's loads and the next barrier: the loop is free of
 // scratch reloads, which would wait for those loads (the counter retires in
 // order).
 //
-// Online softmax without accumulator rescaling: each stage's probabilities
-// are formed against the stage's own integer ceiling ms, and the p.v product
-// applies 2^(ms - mref) as the E8M0 scale of its P operand, mref being the
-// row's reference; only a jump of more than kMaxUp moves mref (and rescales).
+// Online softmax without accumulator rescaling: each half-stage's
+// probabilities (32 tokens) are formed against the half's own integer
+// ceiling ms, and the p.v product applies 2^(ms - mref) as the E8M0 scale of
+// its P operand (one scale block per half), mref being the row's reference;
+// only a jump of more than kMaxUp moves mref (and rescales).
 #include "attention_common.h"
 #include "launch.h"
 
@@ -72,15 +74,18 @@ static_assert(Tile8::kHalfBytes == kKBlocks * 16 * 32, "a tile half holds 32 tok
 constexpr int kBufs = 3;
 typedef Staging<2> Stage8;   // BF16 outputs and fp16 partials
 
-// Probabilities of a stage are formed against the stage's own ceiling ms (the
-// row maximum of its scores, rounded up to an integer in base 2):
-// p' = 2^(score - ms + kPShift) <= 2^8 = 256 stays inside E4M3's range (448).
-// The product carries 2^(ms - mref) as the E8M0 scale of the P operand, so the
-// accumulator stays in the frame of the row reference mref (an integer) and is
-// never rescaled while ms - mref <= kMaxUp; only a row whose scores jump by
-// more than that moves mref (the rare path).  Stages far below mref get the
-// smallest scale, 2^-127: their share of the row is below fp32 resolution.
+// Probabilities of a half-stage (32 tokens, one tile half) are formed against
+// the half's own ceiling ms (the row maximum of its scores, rounded up to an
+// integer in base 2): p' = 2^(score - ms + kPShift) <= 2^8 = 256 stays inside
+// E4M3's range (448).  The product carries 2^(ms - mref) as the E8M0 scale of
+// the P operand's scale block for that half (the 32 k of block 0 are tile half
+// 0, those of block 1 tile half 1), so the accumulator stays in the frame of
+// the row reference mref (an integer) and is never rescaled while
+// ms - mref <= kMaxUp; only a row whose scores jump by more than that moves
+// mref (the rare path).  Halves far below mref get the smallest scale, 2^-127:
+// their share of the row is below fp32 resolution.
 constexpr float kPShift = 8.0f;
+constexpr float kHidden = -1073741824.0f;   // -2^30: the ceiling of a half with nothing visible
 constexpr float kMaxUp = 64.0f;
 constexpr int kScaleOne = 127;   // E8M0 encoding of 2^0
 
@@ -393,15 +398,14 @@ __device__ inline floatx16 scores_fp8q(KAddr ka, const QOp<true> &q) {
   return acc;
 }
 
-// The same with this wave's direct loads of the next tile: loads 0..4 after
-// the products of steps 0, 2, 4, 6, 8 of the first score block, loads 5..8
-// after steps 1, 3, 5, 7 of the second (load k reads row bytes 64 k on, into
-// M0 + 2048 k).  A load stalls the wave in the memory pipe for up to a
-// hundred cycles; between products the matrix unit keeps working meanwhile.
-// The instruction's immediate offset would move the LDS destination as well
-// as the source, so each load takes its own address.
-__device__ inline floatx16 scores_split_dma0(KAddr ka, const QOp<false> &q, const Rope &rope,
-                                             const uint8_t *row, uint32_t dst) {
+// The same with this wave's nine direct loads of the next tile, one after
+// each step's products (load k reads row bytes 64 k on, into M0 + 2048 k).  A
+// load can stall the wave in the memory pipe for up to a hundred cycles; the
+// matrix unit keeps working meanwhile.  The instruction's immediate offset
+// would move the LDS destination as well as the source, so each load takes
+// its own address.
+__device__ inline floatx16 scores_split_dma(KAddr ka, const QOp<false> &q, const Rope &rope,
+                                            const uint8_t *row, uint32_t dst) {
   floatx16 acc;
   uint32_t saved;
   asm volatile(
@@ -422,46 +426,54 @@ __device__ inline floatx16 scores_split_dma0(KAddr ka, const QOp<false> &q, cons
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q2], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q3], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g1], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q4], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g1], off\n\t"
+      "global_load_lds_dwordx4 %[g2], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
       "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
       "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q7], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g3], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q8], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q9], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g2], off\n\t"
+      "global_load_lds_dwordx4 %[g4], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q10], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q11], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g5], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
       "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
       "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q12], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q13], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g3], off\n\t"
+      "global_load_lds_dwordx4 %[g6], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q14], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q15], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g7], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q16], %[acc]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q17], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g4], off\n\t"
+      "global_load_lds_dwordx4 %[g8], off\n\t"
       "s_mov_b32 m0, %[m0s]\n\t"
       "s_nop 15\n\t"
       "s_nop 3\n\t"
@@ -471,88 +483,14 @@ __device__ inline floatx16 scores_split_dma0(KAddr ka, const QOp<false> &q, cons
         [q8] "v"(q.v[8]), [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]),
         [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(rope.hi), [q17] "v"(rope.lo),
         [g0] "v"(row + 0), [g1] "v"(row + 64), [g2] "v"(row + 128), [g3] "v"(row + 192), [g4] "v"(row + 256),
-        [dst] "s"(dst)
+        [g5] "v"(row + 320), [g6] "v"(row + 384), [g7] "v"(row + 448), [g8] "v"(row + 512), [dst] "s"(dst)
       : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244",
         "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "scc");
   return acc;
 }
 
-__device__ inline floatx16 scores_split_dma1(KAddr ka, const QOp<false> &q, const Rope &rope,
-                                             const uint8_t *row, uint32_t dst) {
-  floatx16 acc;
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %[m0s], m0\n\t"
-      "s_add_u32 m0, %[dst], 10240\n\t"
-      "s_waitcnt lgkmcnt(0)\n\t"
-      "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
-      "ds_read_b128 v[244:247], %[a1] offset:0\n\t"
-      "ds_read_b128 v[248:251], %[a0] offset:2048\n\t"
-      "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q1], %[acc]\n\t"
-      "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
-      "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q2], %[acc]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q3], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g0], off\n\t"
-      "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
-      "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q4], %[acc]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
-      "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
-      "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q7], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g1], off\n\t"
-      "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
-      "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q8], %[acc]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q9], %[acc]\n\t"
-      "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
-      "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q10], %[acc]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q11], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g2], off\n\t"
-      "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
-      "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q12], %[acc]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q13], %[acc]\n\t"
-      "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
-      "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q14], %[acc]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q15], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g3], off\n\t"
-      "s_waitcnt lgkmcnt(0)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q16], %[acc]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q17], %[acc]\n\t"
-      "s_mov_b32 m0, %[m0s]\n\t"
-      "s_nop 15\n\t"
-      "s_nop 3\n\t"
-      : [acc] "=&v"(acc), [m0s] "=&s"(saved)
-      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
-        [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
-        [q8] "v"(q.v[8]), [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]),
-        [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(rope.hi), [q17] "v"(rope.lo),
-        [g0] "v"(row + 320), [g1] "v"(row + 384), [g2] "v"(row + 448), [g3] "v"(row + 512), [dst] "s"(dst)
-      : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244",
-        "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "scc");
-  return acc;
-}
-
-// The quantised query with the next tile's direct loads, split the same way.
-__device__ inline floatx16 scores_fp8q_dma0(KAddr ka, const QOp<true> &q, const uint8_t *row, uint32_t dst) {
+// The quantised query with the next tile's direct loads.
+__device__ inline floatx16 scores_fp8q_dma(KAddr ka, const QOp<true> &q, const uint8_t *row, uint32_t dst) {
   floatx16 acc;
   uint32_t saved;
   asm volatile(
@@ -571,39 +509,47 @@ __device__ inline floatx16 scores_fp8q_dma0(KAddr ka, const QOp<true> &q, const 
       "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q1], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g1], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q2], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g1], off\n\t"
+      "global_load_lds_dwordx4 %[g2], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
       "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
       "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q3], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g3], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q4], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g2], off\n\t"
+      "global_load_lds_dwordx4 %[g4], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g5], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
       "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
       "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g3], off\n\t"
+      "global_load_lds_dwordx4 %[g6], off\n\t"
       "s_add_u32 m0, m0, 2048\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q7], %[acc]\n\t"
+      "global_load_lds_dwordx4 %[g7], off\n\t"
+      "s_add_u32 m0, m0, 2048\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q8], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g4], off\n\t"
+      "global_load_lds_dwordx4 %[g8], off\n\t"
       "s_mov_b32 m0, %[m0s]\n\t"
       "s_nop 15\n\t"
       "s_nop 3\n\t"
@@ -611,69 +557,7 @@ __device__ inline floatx16 scores_fp8q_dma0(KAddr ka, const QOp<true> &q, const 
       : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
         [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
         [q8] "v"(q.v[8]), [g0] "v"(row + 0), [g1] "v"(row + 64), [g2] "v"(row + 128), [g3] "v"(row + 192),
-        [g4] "v"(row + 256), [dst] "s"(dst)
-      : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244",
-        "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "scc");
-  return acc;
-}
-
-__device__ inline floatx16 scores_fp8q_dma1(KAddr ka, const QOp<true> &q, const uint8_t *row, uint32_t dst) {
-  floatx16 acc;
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %[m0s], m0\n\t"
-      "s_add_u32 m0, %[dst], 10240\n\t"
-      "s_waitcnt lgkmcnt(0)\n\t"
-      "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
-      "ds_read_b128 v[244:247], %[a1] offset:0\n\t"
-      "ds_read_b128 v[248:251], %[a0] offset:2048\n\t"
-      "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
-      "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
-      "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q1], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g0], off\n\t"
-      "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
-      "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q2], %[acc]\n\t"
-      "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
-      "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q3], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g1], off\n\t"
-      "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
-      "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q4], %[acc]\n\t"
-      "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
-      "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g2], off\n\t"
-      "s_add_u32 m0, m0, 2048\n\t"
-      "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
-      "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
-      "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
-      "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q7], %[acc]\n\t"
-      "global_load_lds_dwordx4 %[g3], off\n\t"
-      "s_waitcnt lgkmcnt(0)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q8], %[acc]\n\t"
-      "s_mov_b32 m0, %[m0s]\n\t"
-      "s_nop 15\n\t"
-      "s_nop 3\n\t"
-      : [acc] "=&v"(acc), [m0s] "=&s"(saved)
-      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
-        [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
-        [q8] "v"(q.v[8]), [g0] "v"(row + 320), [g1] "v"(row + 384), [g2] "v"(row + 448), [g3] "v"(row + 512),
+        [g4] "v"(row + 256), [g5] "v"(row + 320), [g6] "v"(row + 384), [g7] "v"(row + 448), [g8] "v"(row + 512),
         [dst] "s"(dst)
       : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244",
         "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "scc");
@@ -685,16 +569,11 @@ __device__ inline floatx16 scores(KAddr ka, const QOp<QF8> &q, const Rope &rope)
   if constexpr (QF8) return scores_fp8q(ka, q);
   else return scores_split(ka, q, rope);
 }
-template <bool QF8, int Part>
+template <bool QF8>
 __device__ inline floatx16 scores_dma(KAddr ka, const QOp<QF8> &q, const Rope &rope, const uint8_t *row,
                                       uint32_t dst) {
-  if constexpr (QF8) {
-    if constexpr (Part == 0) return scores_fp8q_dma0(ka, q, row, dst);
-    else return scores_fp8q_dma1(ka, q, row, dst);
-  } else {
-    if constexpr (Part == 0) return scores_split_dma0(ka, q, rope, row, dst);
-    else return scores_split_dma1(ka, q, rope, row, dst);
-  }
+  if constexpr (QF8) return scores_fp8q_dma(ka, q, row, dst);
+  else return scores_split_dma(ka, q, rope, row, dst);
 }
 
 // P of one stage: the E4M3 term (8 registers: 32 probabilities, one byte
@@ -702,6 +581,646 @@ __device__ inline floatx16 scores_dma(KAddr ka, const QOp<QF8> &q, const Rope &r
 template <bool P8> struct POp;
 template <> struct POp<false> { int8v hi, lo; };
 template <> struct POp<true> { int8v hi; };
+
+// What the second score block hands back besides the half-1 scores s1: the
+// half-0 ceiling ms0 (-2^30 when the row sees nothing in that half), the
+// probabilities of groups 0..3 (registers 0..3 of the P operand) and their
+// fp32 sum.
+template <bool P8> struct Half0;
+template <> struct Half0<false> { floatx16 s1; float ms0, sf0; int hi[4], lo[4]; };
+template <> struct Half0<true> { floatx16 s1; float ms0, sf0; int hi[4]; };
+
+// The scores of tile half 1, with the half-0 softmax between the products:
+// the row maximum of s0 over this lane and its partner lane (l ^ 32), the
+// ceiling ms0 = ceil(max * sc2) in base 2, and groups 0..3 of the
+// probabilities p' = 2^(s0 * sc2 - ms0 + 8), converted as in p_group below.
+// The half-0 scores are final when the block starts (the first block ends
+// with the wait states an XDL result needs before a VALU reads it).  The
+// VALU work uses v222 and v224..v231 as scratch; besides the exponentials'
+// one wait state, it touches no register the products read or write.
+__device__ inline void qk1_split_p16(KAddr ka, const QOp<false> &q, const Rope &rope,
+                                     const floatx16 &s0, float sc2, Half0<false> &o) {
+  asm volatile(
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:0\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:2048\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
+      "v_max3_f32 v224, %[s0], %[s1], %[s2]\n\t"
+      "v_max3_f32 v225, %[s3], %[s4], %[s5]\n\t"
+      "v_max3_f32 v226, %[s6], %[s7], %[s8]\n\t"
+      "v_max3_f32 v227, %[s9], %[s10], %[s11]\n\t"
+      "v_max3_f32 v228, %[s12], %[s13], %[s14]\n\t"
+      "v_max3_f32 v224, v224, v225, v226\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q1], %[acc]\n\t"
+      "v_max3_f32 v227, v227, v228, %[s15]\n\t"
+      "v_max_f32 v224, v224, v227\n\t"
+      "v_mov_b32 v225, v224\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 v224, v225\n\t"
+      "v_max_f32 v224, v224, v225\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q2], %[acc]\n\t"
+      "v_mul_f32 v224, v224, %[sc2]\n\t"
+      "v_ceil_f32 v224, v224\n\t"
+      "v_max_f32 %[ms0], 0xce800000, v224\n\t"
+      "v_sub_f32 v222, 0x41000000, %[ms0]\n\t"
+      "v_fma_f32 v224, %[s0], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s1], %[sc2], v222\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q3], %[acc]\n\t"
+      "v_fma_f32 v226, %[s2], %[sc2], v222\n\t"
+      "v_fma_f32 v227, %[s3], %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q4], %[acc]\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi0], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi0], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_cvt_pk_f32_fp8 v[228:229], %[hi0]\n\t"
+      "v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi0] src0_sel:WORD_1\n\t"
+      "v_sub_f32 v228, v224, v228\n\t"
+      "v_sub_f32 v229, v225, v229\n\t"
+      "v_sub_f32 v230, v226, v230\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
+      "v_sub_f32 v231, v227, v231\n\t"
+      "v_cvt_pk_bf8_f32 %[lo0], v228, v229\n\t"
+      "v_cvt_pk_bf8_f32 %[lo0], v230, v231 op_sel:[0,0,1]\n\t"
+      "v_fma_f32 v224, %[s4], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s5], %[sc2], v222\n\t"
+      "v_fma_f32 v226, %[s6], %[sc2], v222\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q7], %[acc]\n\t"
+      "v_fma_f32 v227, %[s7], %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q8], %[acc]\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi1], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi1], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q9], %[acc]\n\t"
+      "v_cvt_pk_f32_fp8 v[228:229], %[hi1]\n\t"
+      "v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi1] src0_sel:WORD_1\n\t"
+      "v_sub_f32 v228, v224, v228\n\t"
+      "v_sub_f32 v229, v225, v229\n\t"
+      "v_sub_f32 v230, v226, v230\n\t"
+      "v_sub_f32 v231, v227, v231\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q10], %[acc]\n\t"
+      "v_cvt_pk_bf8_f32 %[lo1], v228, v229\n\t"
+      "v_cvt_pk_bf8_f32 %[lo1], v230, v231 op_sel:[0,0,1]\n\t"
+      "v_fma_f32 v224, %[s8], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s9], %[sc2], v222\n\t"
+      "v_fma_f32 v226, %[s10], %[sc2], v222\n\t"
+      "v_fma_f32 v227, %[s11], %[sc2], v222\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q11], %[acc]\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q12], %[acc]\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi2], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi2], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_cvt_pk_f32_fp8 v[228:229], %[hi2]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q13], %[acc]\n\t"
+      "v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi2] src0_sel:WORD_1\n\t"
+      "v_sub_f32 v228, v224, v228\n\t"
+      "v_sub_f32 v229, v225, v229\n\t"
+      "v_sub_f32 v230, v226, v230\n\t"
+      "v_sub_f32 v231, v227, v231\n\t"
+      "v_cvt_pk_bf8_f32 %[lo2], v228, v229\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q14], %[acc]\n\t"
+      "v_cvt_pk_bf8_f32 %[lo2], v230, v231 op_sel:[0,0,1]\n\t"
+      "v_fma_f32 v224, %[s12], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s13], %[sc2], v222\n\t"
+      "v_fma_f32 v226, %[s14], %[sc2], v222\n\t"
+      "v_fma_f32 v227, %[s15], %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q15], %[acc]\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q16], %[acc]\n\t"
+      "v_cvt_pk_fp8_f32 %[hi3], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi3], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_cvt_pk_f32_fp8 v[228:229], %[hi3]\n\t"
+      "v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi3] src0_sel:WORD_1\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q17], %[acc]\n\t"
+      "v_sub_f32 v228, v224, v228\n\t"
+      "v_sub_f32 v229, v225, v229\n\t"
+      "v_sub_f32 v230, v226, v230\n\t"
+      "v_sub_f32 v231, v227, v231\n\t"
+      "v_cvt_pk_bf8_f32 %[lo3], v228, v229\n\t"
+      "v_cvt_pk_bf8_f32 %[lo3], v230, v231 op_sel:[0,0,1]\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3\n\t"
+      : [acc] "=&v"(o.s1), [ms0] "=&v"(o.ms0), [sf] "+v"(o.sf0), [hi0] "=&v"(o.hi[0]), [hi1] "=&v"(o.hi[1]),
+        [hi2] "=&v"(o.hi[2]), [hi3] "=&v"(o.hi[3]), [lo0] "=&v"(o.lo[0]), [lo1] "=&v"(o.lo[1]),
+        [lo2] "=&v"(o.lo[2]), [lo3] "=&v"(o.lo[3])
+      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
+        [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
+        [q8] "v"(q.v[8]), [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]),
+        [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(rope.hi), [q17] "v"(rope.lo),
+        [s0] "v"(s0[0]), [s1] "v"(s0[1]), [s2] "v"(s0[2]), [s3] "v"(s0[3]), [s4] "v"(s0[4]), [s5] "v"(s0[5]),
+        [s6] "v"(s0[6]), [s7] "v"(s0[7]), [s8] "v"(s0[8]), [s9] "v"(s0[9]), [s10] "v"(s0[10]),
+        [s11] "v"(s0[11]), [s12] "v"(s0[12]), [s13] "v"(s0[13]), [s14] "v"(s0[14]), [s15] "v"(s0[15]),
+        [sc2] "v"(sc2)
+      : "v222", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235",
+        "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248",
+        "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory");
+}
+
+__device__ inline void qk1_split_p8(KAddr ka, const QOp<false> &q, const Rope &rope,
+                                    const floatx16 &s0, float sc2, Half0<true> &o) {
+  asm volatile(
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:0\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:2048\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
+      "v_max3_f32 v224, %[s0], %[s1], %[s2]\n\t"
+      "v_max3_f32 v225, %[s3], %[s4], %[s5]\n\t"
+      "v_max3_f32 v226, %[s6], %[s7], %[s8]\n\t"
+      "v_max3_f32 v227, %[s9], %[s10], %[s11]\n\t"
+      "v_max3_f32 v228, %[s12], %[s13], %[s14]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q1], %[acc]\n\t"
+      "v_max3_f32 v224, v224, v225, v226\n\t"
+      "v_max3_f32 v227, v227, v228, %[s15]\n\t"
+      "v_max_f32 v224, v224, v227\n\t"
+      "v_mov_b32 v225, v224\n\t"
+      "s_nop 1\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q2], %[acc]\n\t"
+      "v_permlane32_swap_b32 v224, v225\n\t"
+      "v_max_f32 v224, v224, v225\n\t"
+      "v_mul_f32 v224, v224, %[sc2]\n\t"
+      "v_ceil_f32 v224, v224\n\t"
+      "v_max_f32 %[ms0], 0xce800000, v224\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q3], %[acc]\n\t"
+      "v_sub_f32 v222, 0x41000000, %[ms0]\n\t"
+      "v_fma_f32 v224, %[s0], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s1], %[sc2], v222\n\t"
+      "v_fma_f32 v226, %[s2], %[sc2], v222\n\t"
+      "v_fma_f32 v227, %[s3], %[sc2], v222\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q4], %[acc]\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi0], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi0], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_fma_f32 v224, %[s4], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s5], %[sc2], v222\n\t"
+      "v_fma_f32 v226, %[s6], %[sc2], v222\n\t"
+      "v_fma_f32 v227, %[s7], %[sc2], v222\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q7], %[acc]\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q8], %[acc]\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi1], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi1], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q9], %[acc]\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_fma_f32 v224, %[s8], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s9], %[sc2], v222\n\t"
+      "v_fma_f32 v226, %[s10], %[sc2], v222\n\t"
+      "v_fma_f32 v227, %[s11], %[sc2], v222\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q10], %[acc]\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q11], %[acc]\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi2], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi2], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q12], %[acc]\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_fma_f32 v224, %[s12], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s13], %[sc2], v222\n\t"
+      "v_fma_f32 v226, %[s14], %[sc2], v222\n\t"
+      "v_fma_f32 v227, %[s15], %[sc2], v222\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q13], %[acc]\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q14], %[acc]\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi3], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi3], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q15], %[acc]\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q16], %[acc]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q17], %[acc]\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3\n\t"
+      : [acc] "=&v"(o.s1), [ms0] "=&v"(o.ms0), [sf] "+v"(o.sf0), [hi0] "=&v"(o.hi[0]), [hi1] "=&v"(o.hi[1]),
+        [hi2] "=&v"(o.hi[2]), [hi3] "=&v"(o.hi[3])
+      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
+        [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
+        [q8] "v"(q.v[8]), [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]),
+        [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(rope.hi), [q17] "v"(rope.lo),
+        [s0] "v"(s0[0]), [s1] "v"(s0[1]), [s2] "v"(s0[2]), [s3] "v"(s0[3]), [s4] "v"(s0[4]), [s5] "v"(s0[5]),
+        [s6] "v"(s0[6]), [s7] "v"(s0[7]), [s8] "v"(s0[8]), [s9] "v"(s0[9]), [s10] "v"(s0[10]),
+        [s11] "v"(s0[11]), [s12] "v"(s0[12]), [s13] "v"(s0[13]), [s14] "v"(s0[14]), [s15] "v"(s0[15]),
+        [sc2] "v"(sc2)
+      : "v222", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235",
+        "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248",
+        "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory");
+}
+
+__device__ inline void qk1_fp8q_p16(KAddr ka, const QOp<true> &q,
+                                    const floatx16 &s0, float sc2, Half0<false> &o) {
+  asm volatile(
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:0\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:2048\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
+      "v_max3_f32 v224, %[s0], %[s1], %[s2]\n\t"
+      "v_max3_f32 v225, %[s3], %[s4], %[s5]\n\t"
+      "v_max3_f32 v226, %[s6], %[s7], %[s8]\n\t"
+      "v_max3_f32 v227, %[s9], %[s10], %[s11]\n\t"
+      "v_max3_f32 v228, %[s12], %[s13], %[s14]\n\t"
+      "v_max3_f32 v224, v224, v225, v226\n\t"
+      "v_max3_f32 v227, v227, v228, %[s15]\n\t"
+      "v_max_f32 v224, v224, v227\n\t"
+      "v_mov_b32 v225, v224\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 v224, v225\n\t"
+      "v_max_f32 v224, v224, v225\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q1], %[acc]\n\t"
+      "v_mul_f32 v224, v224, %[sc2]\n\t"
+      "v_ceil_f32 v224, v224\n\t"
+      "v_max_f32 %[ms0], 0xce800000, v224\n\t"
+      "v_sub_f32 v222, 0x41000000, %[ms0]\n\t"
+      "v_fma_f32 v224, %[s0], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s1], %[sc2], v222\n\t"
+      "v_fma_f32 v226, %[s2], %[sc2], v222\n\t"
+      "v_fma_f32 v227, %[s3], %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q2], %[acc]\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi0], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi0], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_cvt_pk_f32_fp8 v[228:229], %[hi0]\n\t"
+      "v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi0] src0_sel:WORD_1\n\t"
+      "v_sub_f32 v228, v224, v228\n\t"
+      "v_sub_f32 v229, v225, v229\n\t"
+      "v_sub_f32 v230, v226, v230\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q3], %[acc]\n\t"
+      "v_sub_f32 v231, v227, v231\n\t"
+      "v_cvt_pk_bf8_f32 %[lo0], v228, v229\n\t"
+      "v_cvt_pk_bf8_f32 %[lo0], v230, v231 op_sel:[0,0,1]\n\t"
+      "v_fma_f32 v224, %[s4], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s5], %[sc2], v222\n\t"
+      "v_fma_f32 v226, %[s6], %[sc2], v222\n\t"
+      "v_fma_f32 v227, %[s7], %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q4], %[acc]\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi1], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi1], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_cvt_pk_f32_fp8 v[228:229], %[hi1]\n\t"
+      "v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi1] src0_sel:WORD_1\n\t"
+      "v_sub_f32 v228, v224, v228\n\t"
+      "v_sub_f32 v229, v225, v229\n\t"
+      "v_sub_f32 v230, v226, v230\n\t"
+      "v_sub_f32 v231, v227, v231\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
+      "v_cvt_pk_bf8_f32 %[lo1], v228, v229\n\t"
+      "v_cvt_pk_bf8_f32 %[lo1], v230, v231 op_sel:[0,0,1]\n\t"
+      "v_fma_f32 v224, %[s8], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s9], %[sc2], v222\n\t"
+      "v_fma_f32 v226, %[s10], %[sc2], v222\n\t"
+      "v_fma_f32 v227, %[s11], %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi2], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi2], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_cvt_pk_f32_fp8 v[228:229], %[hi2]\n\t"
+      "v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi2] src0_sel:WORD_1\n\t"
+      "v_sub_f32 v228, v224, v228\n\t"
+      "v_sub_f32 v229, v225, v229\n\t"
+      "v_sub_f32 v230, v226, v230\n\t"
+      "v_sub_f32 v231, v227, v231\n\t"
+      "v_cvt_pk_bf8_f32 %[lo2], v228, v229\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q7], %[acc]\n\t"
+      "v_cvt_pk_bf8_f32 %[lo2], v230, v231 op_sel:[0,0,1]\n\t"
+      "v_fma_f32 v224, %[s12], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s13], %[sc2], v222\n\t"
+      "v_fma_f32 v226, %[s14], %[sc2], v222\n\t"
+      "v_fma_f32 v227, %[s15], %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q8], %[acc]\n\t"
+      "v_cvt_pk_fp8_f32 %[hi3], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi3], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_cvt_pk_f32_fp8 v[228:229], %[hi3]\n\t"
+      "v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi3] src0_sel:WORD_1\n\t"
+      "v_sub_f32 v228, v224, v228\n\t"
+      "v_sub_f32 v229, v225, v229\n\t"
+      "v_sub_f32 v230, v226, v230\n\t"
+      "v_sub_f32 v231, v227, v231\n\t"
+      "v_cvt_pk_bf8_f32 %[lo3], v228, v229\n\t"
+      "v_cvt_pk_bf8_f32 %[lo3], v230, v231 op_sel:[0,0,1]\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3\n\t"
+      : [acc] "=&v"(o.s1), [ms0] "=&v"(o.ms0), [sf] "+v"(o.sf0), [hi0] "=&v"(o.hi[0]), [hi1] "=&v"(o.hi[1]),
+        [hi2] "=&v"(o.hi[2]), [hi3] "=&v"(o.hi[3]), [lo0] "=&v"(o.lo[0]), [lo1] "=&v"(o.lo[1]),
+        [lo2] "=&v"(o.lo[2]), [lo3] "=&v"(o.lo[3])
+      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
+        [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
+        [q8] "v"(q.v[8]), [s0] "v"(s0[0]), [s1] "v"(s0[1]), [s2] "v"(s0[2]), [s3] "v"(s0[3]), [s4] "v"(s0[4]),
+        [s5] "v"(s0[5]), [s6] "v"(s0[6]), [s7] "v"(s0[7]), [s8] "v"(s0[8]), [s9] "v"(s0[9]), [s10] "v"(s0[10]),
+        [s11] "v"(s0[11]), [s12] "v"(s0[12]), [s13] "v"(s0[13]), [s14] "v"(s0[14]), [s15] "v"(s0[15]),
+        [sc2] "v"(sc2)
+      : "v222", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235",
+        "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248",
+        "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory");
+}
+
+__device__ inline void qk1_fp8q_p8(KAddr ka, const QOp<true> &q,
+                                   const floatx16 &s0, float sc2, Half0<true> &o) {
+  asm volatile(
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:0\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:2048\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q0], 0\n\t"
+      "v_max3_f32 v224, %[s0], %[s1], %[s2]\n\t"
+      "v_max3_f32 v225, %[s3], %[s4], %[s5]\n\t"
+      "v_max3_f32 v226, %[s6], %[s7], %[s8]\n\t"
+      "v_max3_f32 v227, %[s9], %[s10], %[s11]\n\t"
+      "v_max3_f32 v228, %[s12], %[s13], %[s14]\n\t"
+      "v_max3_f32 v224, v224, v225, v226\n\t"
+      "v_max3_f32 v227, v227, v228, %[s15]\n\t"
+      "v_max_f32 v224, v224, v227\n\t"
+      "v_mov_b32 v225, v224\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q1], %[acc]\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 v224, v225\n\t"
+      "v_max_f32 v224, v224, v225\n\t"
+      "v_mul_f32 v224, v224, %[sc2]\n\t"
+      "v_ceil_f32 v224, v224\n\t"
+      "v_max_f32 %[ms0], 0xce800000, v224\n\t"
+      "v_sub_f32 v222, 0x41000000, %[ms0]\n\t"
+      "v_fma_f32 v224, %[s0], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s1], %[sc2], v222\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q2], %[acc]\n\t"
+      "v_fma_f32 v226, %[s2], %[sc2], v222\n\t"
+      "v_fma_f32 v227, %[s3], %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q3], %[acc]\n\t"
+      "v_cvt_pk_fp8_f32 %[hi0], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi0], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_fma_f32 v224, %[s4], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s5], %[sc2], v222\n\t"
+      "v_fma_f32 v226, %[s6], %[sc2], v222\n\t"
+      "v_fma_f32 v227, %[s7], %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q4], %[acc]\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi1], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi1], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q5], %[acc]\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_fma_f32 v224, %[s8], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s9], %[sc2], v222\n\t"
+      "v_fma_f32 v226, %[s10], %[sc2], v222\n\t"
+      "v_fma_f32 v227, %[s11], %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[240:247], %[q6], %[acc]\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi2], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi2], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_fma_f32 v224, %[s12], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s13], %[sc2], v222\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[248:255], %[q7], %[acc]\n\t"
+      "v_fma_f32 v226, %[s14], %[sc2], v222\n\t"
+      "v_fma_f32 v227, %[s15], %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[acc], v[232:239], %[q8], %[acc]\n\t"
+      "v_cvt_pk_fp8_f32 %[hi3], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi3], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3\n\t"
+      : [acc] "=&v"(o.s1), [ms0] "=&v"(o.ms0), [sf] "+v"(o.sf0), [hi0] "=&v"(o.hi[0]), [hi1] "=&v"(o.hi[1]),
+        [hi2] "=&v"(o.hi[2]), [hi3] "=&v"(o.hi[3])
+      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
+        [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
+        [q8] "v"(q.v[8]), [s0] "v"(s0[0]), [s1] "v"(s0[1]), [s2] "v"(s0[2]), [s3] "v"(s0[3]), [s4] "v"(s0[4]),
+        [s5] "v"(s0[5]), [s6] "v"(s0[6]), [s7] "v"(s0[7]), [s8] "v"(s0[8]), [s9] "v"(s0[9]), [s10] "v"(s0[10]),
+        [s11] "v"(s0[11]), [s12] "v"(s0[12]), [s13] "v"(s0[13]), [s14] "v"(s0[14]), [s15] "v"(s0[15]),
+        [sc2] "v"(sc2)
+      : "v222", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235",
+        "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248",
+        "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory");
+}
+
+template <bool QF8, bool P8>
+__device__ inline void qk1(KAddr ka, const QOp<QF8> &q, const Rope &rope, const floatx16 &s0, float sc2,
+                           Half0<P8> &o) {
+  if constexpr (QF8) {
+    if constexpr (P8) qk1_fp8q_p8(ka, q, s0, sc2, o);
+    else qk1_fp8q_p16(ka, q, s0, sc2, o);
+  } else {
+    if constexpr (P8) qk1_split_p8(ka, q, rope, s0, sc2, o);
+    else qk1_split_p16(ka, q, rope, s0, sc2, o);
+  }
+}
 
 // A stage's probabilities wait for their p.v in LDS, in the wave's output
 // staging area (unused until the piece ends): kept in registers they would be
@@ -735,21 +1254,17 @@ __device__ inline float max3(float a, float b, float c) {
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
-// Maximum of the lane's 32 scores: a three-way tree, 16 instructions deep 4.
-__device__ inline float row_max(const floatx16 &s0, const floatx16 &s1) {
-  float t[11];
-#pragma unroll
-  for (int i = 0; i < 5; ++i) t[i] = max3(s0[3 * i], s0[3 * i + 1], s0[3 * i + 2]);
-#pragma unroll
-  for (int i = 0; i < 5; ++i) t[5 + i] = max3(s1[3 * i], s1[3 * i + 1], s1[3 * i + 2]);
-  t[10] = max3(s0[15], s1[15], t[9]);
-  const float u0 = max3(t[0], t[1], t[2]), u1 = max3(t[3], t[4], t[5]), u2 = max3(t[6], t[7], t[8]);
-  return max3(max3(u0, u1, u2), t[10], t[10]);
+// Maximum of the lane's 16 scores of one tile half: a three-way tree.
+__device__ inline float half_max(const floatx16 &x) {
+  const float t0 = max3(x[0], x[1], x[2]), t1 = max3(x[3], x[4], x[5]), t2 = max3(x[6], x[7], x[8]);
+  const float t3 = max3(x[9], x[10], x[11]), t4 = max3(x[12], x[13], x[14]);
+  return __builtin_fmaxf(max3(t0, t1, t2), max3(t3, t4, x[15]));
 }
 
 // Group w (0..7) of the lane's 32 probabilities p' = 2^(score * sc2 - msub)
 // of one stage -- scores of tile half 0 in s0, half 1 in s1; masked scores
-// are -inf and give 0 -- packed as bytes w of the p.v B operand:
+// are -inf and give 0 -- packed as register w of the p.v B operand (groups
+// 0..3 run inside the second score block, with the same arithmetic):
 // hi = E4M3(p') (round to nearest even), lo = E5M2(p' - hi).  Adds the fp32
 // sum of p' to sf: the row sum that normalises the output and gives the LSE
 // is taken before the conversion, as in flash attention, so each output is
@@ -995,14 +1510,12 @@ attention_fp8_kernel(AttnArgs a) {
       // stage lies wholly inside every row window of the wave when
       // rlen - 64 s - 4h > 59 on all lanes.
       const int lim = rlen - s * kStage - 4 * hh;
-      // the score blocks also issue the next unit's tile loads
-      floatx16 s0, s1;
+      // the first score block also issues the next unit's tile loads
+      floatx16 s0;
       if (uu + 1 < hi) {
         const uint32_t nb = buf == kBufs - 1 ? 0 : buf + 1;
-        const uint8_t *nrow = stage_row(a, page, nx.s, nx.lmax, wave, &bad);
-        const uint32_t ndst = stage_dst(lds_base + nb * Tile8::kBytes, wave);
-        s0 = scores_dma<QF8, 0>(k_addr(tile), q, rope, nrow, ndst);
-        s1 = scores_dma<QF8, 1>(k_addr(tile + Tile8::kHalfBytes), q, rope, nrow, ndst);
+        s0 = scores_dma<QF8>(k_addr(tile), q, rope, stage_row(a, page, nx.s, nx.lmax, wave, &bad),
+                             stage_dst(lds_base + nb * Tile8::kBytes, wave));
         if (k == nst - 1) following = nx;
         if (uu + 2 < hi) {
           nx = wk.advance(nx, uu + 2);
@@ -1010,10 +1523,20 @@ attention_fp8_kernel(AttnArgs a) {
         }
       } else {
         s0 = scores<QF8>(k_addr(tile), q, rope);
-        s1 = scores<QF8>(k_addr(tile + Tile8::kHalfBytes), q, rope);
       }
+      const bool edge = !__all(lim > 59);   // some row's window ends inside this stage
+      if (edge) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s0[r] = 8 * (r >> 2) + (r & 3) < lim ? s0[r] : kNegInf;
+      }
+      // the second block: scores of half 1, and between its products the
+      // half-0 ceiling and probabilities (groups 0..3)
+      Half0<P8> h0;
+      h0.sf0 = 0.f;
+      qk1<QF8, P8>(k_addr(tile + Tile8::kHalfBytes), q, rope, s0, sc2, h0);
+      floatx16 s1 = h0.s1;
       // the pending stage's probabilities and first value blocks: their LDS
-      // latency runs under the masking and the row maximum
+      // latency runs under the half-1 maximum
       const uint32_t vt = prev_tile();
       const VOff vo = v_offsets(fresh_lane_id());
       POp<P8> pp;
@@ -1023,34 +1546,37 @@ attention_fp8_kernel(AttnArgs a) {
         va[0] = lds_v(vt, vo, 0);
         va[1] = lds_v(vt, vo, 1);
       }
-      if (!__all(lim > 59)) {
+      if (edge) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = 8 * (r >> 2) + (r & 3);
-          s0[r] = off < lim ? s0[r] : kNegInf;
-          s1[r] = off + 32 < lim ? s1[r] : kNegInf;
-        }
+        for (int r = 0; r < 16; ++r) s1[r] = 8 * (r >> 2) + (r & 3) + 32 < lim ? s1[r] : kNegInf;
       }
-      float mx = row_max(s0, s1);
-      mx = max3(mx, other_half(mx, hh), mx) * sc2;
-      // the stage ceiling; a row with nothing visible in the stage (all p'
-      // are 0) takes the reference, or 0 before the row has one
-      const bool vis = mx > kNegInf;
+      // half-1 ceiling; the reference starts only with a visible half
+      float m1 = half_max(s1);
+      m1 = __builtin_fmaxf(m1, other_half(m1, hh));
+      const float ms0 = h0.ms0;
+      const float ms1 = __builtin_fmaxf(__builtin_ceilf(m1 * sc2), kHidden);
+      const float msx = __builtin_fmaxf(ms0, ms1);
       const bool started = mref > kNegInf;
-      const float cm = __builtin_ceilf(mx);
-      const float ms = vis ? cm : (started ? mref : 0.f);
-      mref = started ? mref : (vis ? ms : kNegInf);   // nothing accumulated yet
-      const float delta = (started || vis) ? ms - mref : 0.f;
-      const float msub = ms - kPShift;
-      float sf = 0.f;
+      mref = started ? mref : (msx > kHidden ? msx : kNegInf);   // nothing accumulated yet
+      const bool ref = mref > kNegInf;
+      const float d0 = ref ? ms0 - mref : 0.f;
+      const float d1 = ref ? ms1 - mref : 0.f;
+      const float delta = __builtin_fmaxf(d0, d1);
+      const float msub1 = ms1 - kPShift;
+      float sf1 = 0.f;
       POp<P8> pc;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        pc.hi[g] = h0.hi[g];
+        if constexpr (!P8) pc.lo[g] = h0.lo[g];
+      }
       if constexpr (PREV) {
-        // the pending p.v with this stage's probabilities between its
-        // products: eight chunks of one group of four probabilities and two
-        // value blocks each, V read two blocks ahead
+        // the pending p.v in eight chunks of two value blocks, V read two
+        // blocks ahead; the odd chunks carry groups 4..7 of this stage's
+        // probabilities, the first the half-1 maximum above
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          p_group<P8>(s0, s1, c, sc2, msub, pc, sf);
+          if (c & 1) p_group<P8>(s0, s1, 4 + (c >> 1), sc2, msub1, pc, sf1);
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const int d = 2 * c + j;
@@ -1062,25 +1588,30 @@ attention_fp8_kernel(AttnArgs a) {
         }
       } else {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) p_group<P8>(s0, s1, c, sc2, msub, pc, sf);
+        for (int g = 4; g < 8; ++g) p_group<P8>(s0, s1, g, sc2, msub1, pc, sf1);
       }
       put_p<P8>(parea, pc);
-      // the stage sums join the row sums here, in the reference frame before
-      // any move; a row whose reference moves (the first stage of a piece
-      // never does: mref was -inf) redoes it below
+      // the stage sums join the row sums in the reference frame, each half
+      // with its own scale; a row whose reference moves (the first stage of a
+      // piece never does: mref was -inf) redoes it below.  The P operand's
+      // scale block 0 (lanes 0..31) covers half 0, block 1 (lanes 32..63)
+      // half 1.
       const float lf_old = lsum_f;
-      const int di = (int)__builtin_fmaxf(__builtin_fminf(delta, kMaxUp), -127.f);
-      epend = kScaleOne + di;
-      lsum_f += __builtin_ldexpf(sf, di);
+      const int di0 = (int)__builtin_fmaxf(__builtin_fminf(d0, kMaxUp), -127.f);
+      const int di1 = (int)__builtin_fmaxf(__builtin_fminf(d1, kMaxUp), -127.f);
+      epend = kScaleOne + (hh ? di1 : di0);
+      lsum_f += __builtin_ldexpf(h0.sf0, di0) + __builtin_ldexpf(sf1, di1);
       const bool move = PREV && delta > kMaxUp;
       if (PREV && __any(move)) {
         // exact power of two; the pending product is already in oacc
         const float alpha = move ? __builtin_ldexpf(1.0f, -(int)__builtin_fminf(delta, 1024.f)) : 1.0f;
         rescale_o(oacc, alpha);
         if (move) {
-          mref = ms;
-          epend = kScaleOne;
-          lsum_f = lf_old * alpha + sf;
+          mref = msx;
+          const int e0 = (int)__builtin_fmaxf(ms0 - msx, -127.f);
+          const int e1 = (int)__builtin_fmaxf(ms1 - msx, -127.f);
+          epend = kScaleOne + (hh ? e1 : e0);
+          lsum_f = lf_old * alpha + __builtin_ldexpf(h0.sf0, e0) + __builtin_ldexpf(sf1, e1);
         }
       }
       pin_agprs(oacc);

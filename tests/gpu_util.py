@@ -90,13 +90,14 @@ E4M3_SUB = 2.0 ** -17       # largest normalised weight error of one subnormal p
 
 def fp8_probability_bound(wabs, vsum):
     """Bound on the output change from rounding a row's probabilities to E4M3
-    against per-stage power-of-two scales (p_format "fp8"), given
+    against power-of-two scales (p_format "fp8"), given
     ``wabs = sum_t w_t |v_t|`` and ``vsum = sum_t |v_t|`` over the row's
     visible tokens.
 
-    A stage's probabilities are multiplied by 2^(8 - ms), 2^ms being a power of
-    two at least the stage's largest exp-score and below twice the row's
-    largest, then rounded; the sum that normalises the row is taken before
+    The probabilities of each 32-token block are multiplied by 2^(8 - ms),
+    2^ms a power of two at least the block's largest exp-score and below
+    twice the row's largest, then rounded; the sum that normalises the row is
+    taken before
     rounding.  A normal E4M3 value moves by at most 2^-4 of itself, so weight
     w_t by at most 2^-4 w_t; a subnormal one (below 2^-6) by at most
     min(p', 2^-10), which is min(w_t, 2^-17) after the scale and the

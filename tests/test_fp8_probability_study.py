@@ -1,8 +1,9 @@
 """FP8 probabilities for the p.v product: a float64 study of their error on
 rows shaped like the pages' decode and long-context runs.
 
-The FP8-probability variant (geometry p_format "fp8") forms each 64-token
-stage's probabilities against that stage's own ceiling ms = ceil(max s)
+The FP8-probability variant (geometry p_format "fp8") forms the
+probabilities of each 32-token half-stage (one score tile) against that
+half's own ceiling ms = ceil(max s)
 (scores s in base 2): p' = 2^(s - ms + 8) lies in (0, 256], inside E4M3's
 range, and is rounded to E4M3 (nearest, ties to even; below half the
 smallest subnormal it becomes 0).  The product applies 2^(ms - mref) as the
@@ -14,7 +15,7 @@ unrounded p' in fp32, so the output is
 This file emulates exactly that in float64 and compares it with exact
 attention over the same decoded cache ("Context Parallel Guide (PCP &
 DCP)", "How it works" item 4 runs attention with an FP8 KV cache; the bar
-on the output is max-abs 1.5e-2).  A stage with no visible token keeps
+on the output is max-abs 1.5e-2).  A half with no visible token keeps
 p' = 0.  Rows: the decode workload's rank shard (16,384 tokens) and a
 longer 65,536-token shard of the 1M-context run, query and latents N(0, 1)
 as BF16 and per-tensor-scaled E4M3, softmax scale 1/sqrt(192) as the
@@ -35,7 +36,7 @@ import pytest
 from oracle import formats, qsplit
 
 BAR = 1.5e-2
-STAGE = 64
+STAGE = 32   # tokens per probability scale (one score tile)
 SHIFT = 8
 
 
@@ -142,7 +143,7 @@ def test_short_row_bound(n_tok, spread, seed):
 
 
 def test_subnormal_term_is_needed():
-    # each stage leads with one token at the row maximum whose value is 0;
+    # each half-stage leads with one token at the row maximum whose value is 0;
     # the rest sit 16.6 lower (base 2), so their scaled probabilities are
     # 2^-8.6, subnormal in E4M3, and all round down to 2^-9 -- 24% of each
     # weight, past 2^-4 sum w|v| alone: the second term carries the

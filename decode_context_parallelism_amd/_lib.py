@@ -33,6 +33,7 @@ ERR_LOCAL_PAGES = 4
 ERR_BLOCK_ID = 8
 ERR_PAGE_RANGE = 16
 ERR_TOKEN = 32
+ERR_KERNARG = 64
 
 
 class Geom(ctypes.Structure):

@@ -164,7 +164,13 @@ attention_kernel(AttnArgs a) {
   const int l32 = lane & 31;
   const int h = lane >> 5;
   const int kslot = tok_slot(l32);   // LDS slot of the stage token in this lane's score row
-  if (blockIdx.x == 0 && threadIdx.x == 0) *a.ws_scale = a.out_scale;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *a.ws_scale = a.out_scale;
+    // fields read through kernarg_args() must be the by-value argument's
+    const KernargArgs ka = kernarg_args();
+    if (ka->M != a.M || ka->H != a.H || ka->err != a.err || ka->out_scale != a.out_scale)
+      atomicOr(a.err, DCPMLA_ERR_KERNARG);
+  }
   const int64_t U = a.work[0];
   if (U == 0) return;
   const Split sp = work_split(gridDim.x, U, a.n_mt, a.B, DCPMLA_KV_BF16);

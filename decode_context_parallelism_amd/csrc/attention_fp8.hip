@@ -1381,7 +1381,13 @@ attention_fp8_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int lane = tid & 63;
   const int h = lane >> 5;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *a.ws_scale = a.out_scale;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *a.ws_scale = a.out_scale;
+    // fields read through kernarg_args() must be the by-value argument's
+    const KernargArgs ka = kernarg_args();
+    if (ka->M != a.M || ka->H != a.H || ka->err != a.err || ka->out_scale != a.out_scale)
+      atomicOr(a.err, DCPMLA_ERR_KERNARG);
+  }
   const int64_t U = a.work[0];
   if (U == 0) return;
   const Split sp = work_split(gridDim.x, U, a.n_mt, a.B, DCPMLA_KV_FP8_E4M3);

@@ -116,7 +116,10 @@ enum {
   DCPMLA_ERR_LOCAL_PAGES = 4,    /* a row needs more subpages than max_local_pages: row clamped */
   DCPMLA_ERR_BLOCK_ID = 8,       /* a used block id lies outside [0, num_blocks): row cut there */
   DCPMLA_ERR_PAGE_RANGE = 16,    /* attention met a subpage outside the pool: tokens read as 0 */
-  DCPMLA_ERR_TOKEN = 32          /* KV write: bad sequence id / position: token dropped */
+  DCPMLA_ERR_TOKEN = 32,         /* KV write: bad sequence id / position: token dropped */
+  DCPMLA_ERR_KERNARG = 64        /* attention: the kernel argument block was not found at offset 0 of
+                                    the kernel-argument segment (a toolchain ABI change); the
+                                    launch's outputs are not valid */
 };
 
 /*

@@ -118,6 +118,25 @@ def test_partition_outside_lds(B, qlen, kv_format):
     _check_all(w, grp, _sample_rows(w, 48, 93), tag=f"B={B}")
 
 
+@pytest.mark.parametrize("world", [1, 2])
+@pytest.mark.parametrize("q_format,p_format", [("split", "split"), ("split", "fp8"), ("fp8", "split")])
+def test_windows_at_half_stage_edges(world, q_format, p_format):
+    # With an FP8 cache each 32-token tile half has its own probability scale;
+    # rows whose rank-local window ends just before, at and just after a
+    # 32-token boundary leave a half wholly or partly masked (qlen 3: row i
+    # of a sequence sees ctx - 2 + i tokens)
+    ctx = np.array([33, 34, 35, 65, 66, 67, 97, 98, 130, 200]) * world
+    w = make_workload(name="half_edges", world=world, interleave=1, batch=len(ctx), qlen=3, heads=16,
+                      block_size=16, kv_format="fp8_e4m3", ctx=ctx, table="random",
+                      max_local_pages=16, seed=99)
+    print(f"half-stage edges W={world} q {q_format} p {p_format}", flush=True)
+    for groups in (0, 5):
+        grp, _ = run_group(w, groups=groups, q_format=q_format, p_format=p_format)
+        assert grp.errors() == 0
+        _check_all(w, grp, _all_rows(w), q_format=q_format, p_bound=p_format == "fp8",
+                   tag=f"half edges W={world} q {q_format} p {p_format} groups {groups}")
+
+
 @pytest.mark.parametrize("block_size", [1, 48, 512])
 @pytest.mark.parametrize("kv_format", ["bf16", "fp8_e4m3"])
 def test_block_sizes(block_size, kv_format):

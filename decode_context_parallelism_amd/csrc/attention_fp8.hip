@@ -1505,30 +1505,33 @@ attention_fp8_kernel(AttnArgs a) {
       constexpr bool PREV = decltype(prev_tag)::value;
       const int s = P.st_begin + k;
       const int64_t uu = u + k;
+      // The stage's addresses first (the wait for this wave's loads and the
+      // barrier absorb them).  Online softmax in base 2 on this lane's 32
+      // tokens of head-row m: register r of half t holds token
+      // 64 s + 32 t + 4h + 8(r/4) + r%4, so a stage lies wholly inside every
+      // row window of the wave when rlen - 64 s - 4h > 59 on all lanes.
+      const uint32_t tile = lds_base + buf * Tile8::kBytes;
+      const int hh = fresh_lane_id() >> 5;
+      const int lim = rlen - s * kStage - 4 * hh;
+      const KAddr ka0 = k_addr(tile);
+      const bool more1 = uu + 1 < hi;
+      const uint8_t *nrow = more1 ? stage_row(a, page, nx.s, nx.lmax, wave, &bad) : a.zero_row;
       // tile uu has landed (this wave's share: the wait; every wave's: the
       // barrier), and every wave is done with the tile of unit uu - 2
       wait_direct_loads();
       __syncthreads();
-      const uint32_t tile = lds_base + buf * Tile8::kBytes;
-      const int hh = fresh_lane_id() >> 5;
-      // online softmax in base 2 on this lane's 32 tokens of head-row m.
-      // Register r of half t holds token 64 s + 32 t + 4h + 8(r/4) + r%4; a
-      // stage lies wholly inside every row window of the wave when
-      // rlen - 64 s - 4h > 59 on all lanes.
-      const int lim = rlen - s * kStage - 4 * hh;
       // the first score block also issues the next unit's tile loads
       floatx16 s0;
-      if (uu + 1 < hi) {
+      if (more1) {
         const uint32_t nb = buf == kBufs - 1 ? 0 : buf + 1;
-        s0 = scores_dma<QF8>(k_addr(tile), q, rope, stage_row(a, page, nx.s, nx.lmax, wave, &bad),
-                             stage_dst(lds_base + nb * Tile8::kBytes, wave));
+        s0 = scores_dma<QF8>(ka0, q, rope, nrow, stage_dst(lds_base + nb * Tile8::kBytes, wave));
         if (k == nst - 1) following = nx;
         if (uu + 2 < hi) {
           nx = wk.advance(nx, uu + 2);
           page = page_of(nx);
         }
       } else {
-        s0 = scores<QF8>(k_addr(tile), q, rope);
+        s0 = scores<QF8>(ka0, q, rope);
       }
       const bool edge = !__all(lim > 59);   // some row's window ends inside this stage
       if (edge) {

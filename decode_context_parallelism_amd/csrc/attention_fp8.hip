@@ -1210,6 +1210,871 @@ __device__ inline void qk1_fp8q_p8(KAddr ka, const QOp<true> &q,
         "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory");
 }
 
+// Both score blocks of a stage in one block, for the stages that need no
+// masking and load a next tile: tile half 0's products with the next tile's
+// nine direct loads between them, then tile half 1's with the half-0
+// softmax between them, the key reads running two steps ahead across the
+// halves.  The half-0 scores live in v206..v221 inside the block only.  The
+// loads take one address: the immediate offset 64 k moves the LDS
+// destination as well as the source, so M0 advances by 2048 - 64 per load.
+__device__ inline void qk01_split_p16(KAddr ka, const QOp<false> &q, const Rope &rope, const uint8_t *row,
+                                      uint32_t dst, float sc2, Half0<false> &o) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[m0s], m0\n\t"
+      "s_mov_b32 m0, %[dst]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:0\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:2048\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q0], 0\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q1], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q2], v[206:221]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q3], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:64\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q4], v[206:221]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q5], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:128\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q6], v[206:221]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q7], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:192\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q8], v[206:221]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q9], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:256\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q10], v[206:221]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q11], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:320\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q12], v[206:221]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q13], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:384\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q14], v[206:221]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q15], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:448\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:18432\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:18432\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q16], v[206:221]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q17], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:512\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:20480\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:20480\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[240:247], %[q0], 0\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[240:247], %[q1], %[s1]\n\t"
+      "v_max3_f32 v224, v206, v207, v208\n\t"
+      "v_max3_f32 v225, v209, v210, v211\n\t"
+      "v_max3_f32 v226, v212, v213, v214\n\t"
+      "v_max3_f32 v227, v215, v216, v217\n\t"
+      "v_max3_f32 v228, v218, v219, v220\n\t"
+      "v_max3_f32 v224, v224, v225, v226\n\t"
+      "v_max3_f32 v227, v227, v228, v221\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:22528\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:22528\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q2], %[s1]\n\t"
+      "v_max_f32 v224, v224, v227\n\t"
+      "v_mov_b32 v225, v224\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 v224, v225\n\t"
+      "v_max_f32 v224, v224, v225\n\t"
+      "v_mul_f32 v224, v224, %[sc2]\n\t"
+      "v_ceil_f32 v224, v224\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q3], %[s1]\n\t"
+      "v_max_f32 %[ms0], 0xce800000, v224\n\t"
+      "v_sub_f32 v222, 0x41000000, %[ms0]\n\t"
+      "v_fma_f32 v224, v206, %[sc2], v222\n\t"
+      "v_fma_f32 v225, v207, %[sc2], v222\n\t"
+      "v_fma_f32 v226, v208, %[sc2], v222\n\t"
+      "v_fma_f32 v227, v209, %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:24576\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:24576\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q4], %[s1]\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi0], v224, v225\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q5], %[s1]\n\t"
+      "v_cvt_pk_fp8_f32 %[hi0], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_cvt_pk_f32_fp8 v[228:229], %[hi0]\n\t"
+      "v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi0] src0_sel:WORD_1\n\t"
+      "v_sub_f32 v228, v224, v228\n\t"
+      "v_sub_f32 v229, v225, v229\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:26624\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:26624\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[240:247], %[q6], %[s1]\n\t"
+      "v_sub_f32 v230, v226, v230\n\t"
+      "v_sub_f32 v231, v227, v231\n\t"
+      "v_cvt_pk_bf8_f32 %[lo0], v228, v229\n\t"
+      "v_cvt_pk_bf8_f32 %[lo0], v230, v231 op_sel:[0,0,1]\n\t"
+      "v_fma_f32 v224, v210, %[sc2], v222\n\t"
+      "v_fma_f32 v225, v211, %[sc2], v222\n\t"
+      "v_fma_f32 v226, v212, %[sc2], v222\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[240:247], %[q7], %[s1]\n\t"
+      "v_fma_f32 v227, v213, %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:28672\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:28672\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q8], %[s1]\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi1], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi1], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_cvt_pk_f32_fp8 v[228:229], %[hi1]\n\t"
+      "v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi1] src0_sel:WORD_1\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q9], %[s1]\n\t"
+      "v_sub_f32 v228, v224, v228\n\t"
+      "v_sub_f32 v229, v225, v229\n\t"
+      "v_sub_f32 v230, v226, v230\n\t"
+      "v_sub_f32 v231, v227, v231\n\t"
+      "v_cvt_pk_bf8_f32 %[lo1], v228, v229\n\t"
+      "v_cvt_pk_bf8_f32 %[lo1], v230, v231 op_sel:[0,0,1]\n\t"
+      "v_fma_f32 v224, v214, %[sc2], v222\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:30720\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:30720\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q10], %[s1]\n\t"
+      "v_fma_f32 v225, v215, %[sc2], v222\n\t"
+      "v_fma_f32 v226, v216, %[sc2], v222\n\t"
+      "v_fma_f32 v227, v217, %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q11], %[s1]\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi2], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi2], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:32768\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:32768\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[240:247], %[q12], %[s1]\n\t"
+      "v_cvt_pk_f32_fp8 v[228:229], %[hi2]\n\t"
+      "v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi2] src0_sel:WORD_1\n\t"
+      "v_sub_f32 v228, v224, v228\n\t"
+      "v_sub_f32 v229, v225, v229\n\t"
+      "v_sub_f32 v230, v226, v230\n\t"
+      "v_sub_f32 v231, v227, v231\n\t"
+      "v_cvt_pk_bf8_f32 %[lo2], v228, v229\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[240:247], %[q13], %[s1]\n\t"
+      "v_cvt_pk_bf8_f32 %[lo2], v230, v231 op_sel:[0,0,1]\n\t"
+      "v_fma_f32 v224, v218, %[sc2], v222\n\t"
+      "v_fma_f32 v225, v219, %[sc2], v222\n\t"
+      "v_fma_f32 v226, v220, %[sc2], v222\n\t"
+      "v_fma_f32 v227, v221, %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:34816\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:34816\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q14], %[s1]\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi3], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi3], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q15], %[s1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_cvt_pk_f32_fp8 v[228:229], %[hi3]\n\t"
+      "v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi3] src0_sel:WORD_1\n\t"
+      "v_sub_f32 v228, v224, v228\n\t"
+      "v_sub_f32 v229, v225, v229\n\t"
+      "v_sub_f32 v230, v226, v230\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q16], %[s1]\n\t"
+      "v_sub_f32 v231, v227, v231\n\t"
+      "v_cvt_pk_bf8_f32 %[lo3], v228, v229\n\t"
+      "v_cvt_pk_bf8_f32 %[lo3], v230, v231 op_sel:[0,0,1]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q17], %[s1]\n\t"
+      "s_mov_b32 m0, %[m0s]\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3\n\t"
+      : [s1] "=&v"(o.s1), [ms0] "=&v"(o.ms0), [sf] "+v"(o.sf0), [hi0] "=&v"(o.hi[0]), [hi1] "=&v"(o.hi[1]),
+        [hi2] "=&v"(o.hi[2]), [hi3] "=&v"(o.hi[3]), [lo0] "=&v"(o.lo[0]), [lo1] "=&v"(o.lo[1]),
+        [lo2] "=&v"(o.lo[2]), [lo3] "=&v"(o.lo[3]), [m0s] "=&s"(saved)
+      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
+        [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
+        [q8] "v"(q.v[8]), [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]),
+        [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(rope.hi), [q17] "v"(rope.lo),
+        [row] "v"(row), [dst] "s"(dst), [sc2] "v"(sc2)
+      : "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218",
+        "v219", "v220", "v221", "v222", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232",
+        "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245",
+        "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "scc");
+}
+
+__device__ inline void qk01_split_p8(KAddr ka, const QOp<false> &q, const Rope &rope, const uint8_t *row,
+                                     uint32_t dst, float sc2, Half0<true> &o) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[m0s], m0\n\t"
+      "s_mov_b32 m0, %[dst]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:0\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:2048\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q0], 0\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q1], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q2], v[206:221]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q3], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:64\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q4], v[206:221]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q5], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:128\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q6], v[206:221]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q7], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:192\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q8], v[206:221]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q9], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:256\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q10], v[206:221]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q11], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:320\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q12], v[206:221]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q13], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:384\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q14], v[206:221]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q15], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:448\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:18432\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:18432\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q16], v[206:221]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q17], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:512\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:20480\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:20480\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[240:247], %[q0], 0\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[240:247], %[q1], %[s1]\n\t"
+      "v_max3_f32 v224, v206, v207, v208\n\t"
+      "v_max3_f32 v225, v209, v210, v211\n\t"
+      "v_max3_f32 v226, v212, v213, v214\n\t"
+      "v_max3_f32 v227, v215, v216, v217\n\t"
+      "v_max3_f32 v228, v218, v219, v220\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:22528\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:22528\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q2], %[s1]\n\t"
+      "v_max3_f32 v224, v224, v225, v226\n\t"
+      "v_max3_f32 v227, v227, v228, v221\n\t"
+      "v_max_f32 v224, v224, v227\n\t"
+      "v_mov_b32 v225, v224\n\t"
+      "s_nop 1\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q3], %[s1]\n\t"
+      "v_permlane32_swap_b32 v224, v225\n\t"
+      "v_max_f32 v224, v224, v225\n\t"
+      "v_mul_f32 v224, v224, %[sc2]\n\t"
+      "v_ceil_f32 v224, v224\n\t"
+      "v_max_f32 %[ms0], 0xce800000, v224\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:24576\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:24576\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q4], %[s1]\n\t"
+      "v_sub_f32 v222, 0x41000000, %[ms0]\n\t"
+      "v_fma_f32 v224, v206, %[sc2], v222\n\t"
+      "v_fma_f32 v225, v207, %[sc2], v222\n\t"
+      "v_fma_f32 v226, v208, %[sc2], v222\n\t"
+      "v_fma_f32 v227, v209, %[sc2], v222\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q5], %[s1]\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:26624\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:26624\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[240:247], %[q6], %[s1]\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi0], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi0], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[240:247], %[q7], %[s1]\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_fma_f32 v224, v210, %[sc2], v222\n\t"
+      "v_fma_f32 v225, v211, %[sc2], v222\n\t"
+      "v_fma_f32 v226, v212, %[sc2], v222\n\t"
+      "v_fma_f32 v227, v213, %[sc2], v222\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:28672\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:28672\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q8], %[s1]\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q9], %[s1]\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi1], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi1], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:30720\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:30720\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q10], %[s1]\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_fma_f32 v224, v214, %[sc2], v222\n\t"
+      "v_fma_f32 v225, v215, %[sc2], v222\n\t"
+      "v_fma_f32 v226, v216, %[sc2], v222\n\t"
+      "v_fma_f32 v227, v217, %[sc2], v222\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q11], %[s1]\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:32768\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:32768\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[240:247], %[q12], %[s1]\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi2], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi2], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[240:247], %[q13], %[s1]\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_fma_f32 v224, v218, %[sc2], v222\n\t"
+      "v_fma_f32 v225, v219, %[sc2], v222\n\t"
+      "v_fma_f32 v226, v220, %[sc2], v222\n\t"
+      "v_fma_f32 v227, v221, %[sc2], v222\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:34816\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:34816\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q14], %[s1]\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q15], %[s1]\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi3], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi3], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q16], %[s1]\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q17], %[s1]\n\t"
+      "s_mov_b32 m0, %[m0s]\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3\n\t"
+      : [s1] "=&v"(o.s1), [ms0] "=&v"(o.ms0), [sf] "+v"(o.sf0), [hi0] "=&v"(o.hi[0]), [hi1] "=&v"(o.hi[1]),
+        [hi2] "=&v"(o.hi[2]), [hi3] "=&v"(o.hi[3]), [m0s] "=&s"(saved)
+      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
+        [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
+        [q8] "v"(q.v[8]), [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]),
+        [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(rope.hi), [q17] "v"(rope.lo),
+        [row] "v"(row), [dst] "s"(dst), [sc2] "v"(sc2)
+      : "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218",
+        "v219", "v220", "v221", "v222", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232",
+        "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245",
+        "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "scc");
+}
+
+__device__ inline void qk01_fp8q_p16(KAddr ka, const QOp<true> &q, const uint8_t *row, uint32_t dst,
+                                     float sc2, Half0<false> &o) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[m0s], m0\n\t"
+      "s_mov_b32 m0, %[dst]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:0\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:2048\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q0], 0\n\t"
+      "global_load_lds_dwordx4 %[row], off\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q1], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:64\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q2], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:128\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q3], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:192\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q4], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:256\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q5], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:320\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q6], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:384\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q7], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:448\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:18432\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:18432\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q8], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:512\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:20480\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:20480\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[240:247], %[q0], 0\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:22528\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:22528\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q1], %[s1]\n\t"
+      "v_max3_f32 v224, v206, v207, v208\n\t"
+      "v_max3_f32 v225, v209, v210, v211\n\t"
+      "v_max3_f32 v226, v212, v213, v214\n\t"
+      "v_max3_f32 v227, v215, v216, v217\n\t"
+      "v_max3_f32 v228, v218, v219, v220\n\t"
+      "v_max3_f32 v224, v224, v225, v226\n\t"
+      "v_max3_f32 v227, v227, v228, v221\n\t"
+      "v_max_f32 v224, v224, v227\n\t"
+      "v_mov_b32 v225, v224\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 v224, v225\n\t"
+      "v_max_f32 v224, v224, v225\n\t"
+      "v_mul_f32 v224, v224, %[sc2]\n\t"
+      "v_ceil_f32 v224, v224\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:24576\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:24576\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q2], %[s1]\n\t"
+      "v_max_f32 %[ms0], 0xce800000, v224\n\t"
+      "v_sub_f32 v222, 0x41000000, %[ms0]\n\t"
+      "v_fma_f32 v224, v206, %[sc2], v222\n\t"
+      "v_fma_f32 v225, v207, %[sc2], v222\n\t"
+      "v_fma_f32 v226, v208, %[sc2], v222\n\t"
+      "v_fma_f32 v227, v209, %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi0], v224, v225\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:26624\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:26624\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[240:247], %[q3], %[s1]\n\t"
+      "v_cvt_pk_fp8_f32 %[hi0], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_cvt_pk_f32_fp8 v[228:229], %[hi0]\n\t"
+      "v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi0] src0_sel:WORD_1\n\t"
+      "v_sub_f32 v228, v224, v228\n\t"
+      "v_sub_f32 v229, v225, v229\n\t"
+      "v_sub_f32 v230, v226, v230\n\t"
+      "v_sub_f32 v231, v227, v231\n\t"
+      "v_cvt_pk_bf8_f32 %[lo0], v228, v229\n\t"
+      "v_cvt_pk_bf8_f32 %[lo0], v230, v231 op_sel:[0,0,1]\n\t"
+      "v_fma_f32 v224, v210, %[sc2], v222\n\t"
+      "v_fma_f32 v225, v211, %[sc2], v222\n\t"
+      "v_fma_f32 v226, v212, %[sc2], v222\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:28672\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:28672\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q4], %[s1]\n\t"
+      "v_fma_f32 v227, v213, %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi1], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi1], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_cvt_pk_f32_fp8 v[228:229], %[hi1]\n\t"
+      "v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi1] src0_sel:WORD_1\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:30720\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:30720\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q5], %[s1]\n\t"
+      "v_sub_f32 v228, v224, v228\n\t"
+      "v_sub_f32 v229, v225, v229\n\t"
+      "v_sub_f32 v230, v226, v230\n\t"
+      "v_sub_f32 v231, v227, v231\n\t"
+      "v_cvt_pk_bf8_f32 %[lo1], v228, v229\n\t"
+      "v_cvt_pk_bf8_f32 %[lo1], v230, v231 op_sel:[0,0,1]\n\t"
+      "v_fma_f32 v224, v214, %[sc2], v222\n\t"
+      "v_fma_f32 v225, v215, %[sc2], v222\n\t"
+      "v_fma_f32 v226, v216, %[sc2], v222\n\t"
+      "v_fma_f32 v227, v217, %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:32768\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:32768\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[240:247], %[q6], %[s1]\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi2], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi2], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_cvt_pk_f32_fp8 v[228:229], %[hi2]\n\t"
+      "v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi2] src0_sel:WORD_1\n\t"
+      "v_sub_f32 v228, v224, v228\n\t"
+      "v_sub_f32 v229, v225, v229\n\t"
+      "v_sub_f32 v230, v226, v230\n\t"
+      "v_sub_f32 v231, v227, v231\n\t"
+      "v_cvt_pk_bf8_f32 %[lo2], v228, v229\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:34816\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:34816\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q7], %[s1]\n\t"
+      "v_cvt_pk_bf8_f32 %[lo2], v230, v231 op_sel:[0,0,1]\n\t"
+      "v_fma_f32 v224, v218, %[sc2], v222\n\t"
+      "v_fma_f32 v225, v219, %[sc2], v222\n\t"
+      "v_fma_f32 v226, v220, %[sc2], v222\n\t"
+      "v_fma_f32 v227, v221, %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi3], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi3], v226, v227 op_sel:[0,0,1]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q8], %[s1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_cvt_pk_f32_fp8 v[228:229], %[hi3]\n\t"
+      "v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi3] src0_sel:WORD_1\n\t"
+      "v_sub_f32 v228, v224, v228\n\t"
+      "v_sub_f32 v229, v225, v229\n\t"
+      "v_sub_f32 v230, v226, v230\n\t"
+      "v_sub_f32 v231, v227, v231\n\t"
+      "v_cvt_pk_bf8_f32 %[lo3], v228, v229\n\t"
+      "v_cvt_pk_bf8_f32 %[lo3], v230, v231 op_sel:[0,0,1]\n\t"
+      "s_mov_b32 m0, %[m0s]\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3\n\t"
+      : [s1] "=&v"(o.s1), [ms0] "=&v"(o.ms0), [sf] "+v"(o.sf0), [hi0] "=&v"(o.hi[0]), [hi1] "=&v"(o.hi[1]),
+        [hi2] "=&v"(o.hi[2]), [hi3] "=&v"(o.hi[3]), [lo0] "=&v"(o.lo[0]), [lo1] "=&v"(o.lo[1]),
+        [lo2] "=&v"(o.lo[2]), [lo3] "=&v"(o.lo[3]), [m0s] "=&s"(saved)
+      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
+        [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
+        [q8] "v"(q.v[8]), [row] "v"(row), [dst] "s"(dst), [sc2] "v"(sc2)
+      : "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218",
+        "v219", "v220", "v221", "v222", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232",
+        "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245",
+        "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "scc");
+}
+
+__device__ inline void qk01_fp8q_p8(KAddr ka, const QOp<true> &q, const uint8_t *row, uint32_t dst,
+                                    float sc2, Half0<true> &o) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[m0s], m0\n\t"
+      "s_mov_b32 m0, %[dst]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:0\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:2048\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q0], 0\n\t"
+      "global_load_lds_dwordx4 %[row], off\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q1], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:64\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q2], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:128\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q3], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:192\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q4], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:256\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q5], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:320\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q6], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:384\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q7], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:448\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:18432\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:18432\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q8], v[206:221]\n\t"
+      "global_load_lds_dwordx4 %[row], off offset:512\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:20480\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:20480\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[240:247], %[q0], 0\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:22528\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:22528\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q1], %[s1]\n\t"
+      "v_max3_f32 v224, v206, v207, v208\n\t"
+      "v_max3_f32 v225, v209, v210, v211\n\t"
+      "v_max3_f32 v226, v212, v213, v214\n\t"
+      "v_max3_f32 v227, v215, v216, v217\n\t"
+      "v_max3_f32 v228, v218, v219, v220\n\t"
+      "v_max3_f32 v224, v224, v225, v226\n\t"
+      "v_max3_f32 v227, v227, v228, v221\n\t"
+      "v_max_f32 v224, v224, v227\n\t"
+      "v_mov_b32 v225, v224\n\t"
+      "s_nop 1\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:24576\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:24576\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q2], %[s1]\n\t"
+      "v_permlane32_swap_b32 v224, v225\n\t"
+      "v_max_f32 v224, v224, v225\n\t"
+      "v_mul_f32 v224, v224, %[sc2]\n\t"
+      "v_ceil_f32 v224, v224\n\t"
+      "v_max_f32 %[ms0], 0xce800000, v224\n\t"
+      "v_sub_f32 v222, 0x41000000, %[ms0]\n\t"
+      "v_fma_f32 v224, v206, %[sc2], v222\n\t"
+      "v_fma_f32 v225, v207, %[sc2], v222\n\t"
+      "v_fma_f32 v226, v208, %[sc2], v222\n\t"
+      "v_fma_f32 v227, v209, %[sc2], v222\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:26624\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:26624\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[240:247], %[q3], %[s1]\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi0], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi0], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:28672\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:28672\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q4], %[s1]\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_fma_f32 v224, v210, %[sc2], v222\n\t"
+      "v_fma_f32 v225, v211, %[sc2], v222\n\t"
+      "v_fma_f32 v226, v212, %[sc2], v222\n\t"
+      "v_fma_f32 v227, v213, %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "ds_read_b128 v[240:243], %[a0] offset:30720\n\t"
+      "ds_read_b128 v[244:247], %[a1] offset:30720\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q5], %[s1]\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi1], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi1], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_fma_f32 v224, v214, %[sc2], v222\n\t"
+      "v_fma_f32 v225, v215, %[sc2], v222\n\t"
+      "v_fma_f32 v226, v216, %[sc2], v222\n\t"
+      "v_fma_f32 v227, v217, %[sc2], v222\n\t"
+      "ds_read_b128 v[248:251], %[a0] offset:32768\n\t"
+      "ds_read_b128 v[252:255], %[a1] offset:32768\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[240:247], %[q6], %[s1]\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi2], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi2], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "ds_read_b128 v[232:235], %[a0] offset:34816\n\t"
+      "ds_read_b128 v[236:239], %[a1] offset:34816\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q7], %[s1]\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "v_fma_f32 v224, v218, %[sc2], v222\n\t"
+      "v_fma_f32 v225, v219, %[sc2], v222\n\t"
+      "v_fma_f32 v226, v220, %[sc2], v222\n\t"
+      "v_fma_f32 v227, v221, %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q8], %[s1]\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi3], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi3], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf], %[sf], v228\n\t"
+      "s_mov_b32 m0, %[m0s]\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3\n\t"
+      : [s1] "=&v"(o.s1), [ms0] "=&v"(o.ms0), [sf] "+v"(o.sf0), [hi0] "=&v"(o.hi[0]), [hi1] "=&v"(o.hi[1]),
+        [hi2] "=&v"(o.hi[2]), [hi3] "=&v"(o.hi[3]), [m0s] "=&s"(saved)
+      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
+        [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
+        [q8] "v"(q.v[8]), [row] "v"(row), [dst] "s"(dst), [sc2] "v"(sc2)
+      : "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218",
+        "v219", "v220", "v221", "v222", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232",
+        "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245",
+        "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "scc");
+}
+
 template <bool QF8, bool P8>
 __device__ inline void qk1(KAddr ka, const QOp<QF8> &q, const Rope &rope, const floatx16 &s0, float sc2,
                            Half0<P8> &o) {
@@ -1219,6 +2084,17 @@ __device__ inline void qk1(KAddr ka, const QOp<QF8> &q, const Rope &rope, const 
   } else {
     if constexpr (P8) qk1_split_p8(ka, q, rope, s0, sc2, o);
     else qk1_split_p16(ka, q, rope, s0, sc2, o);
+  }
+}
+template <bool QF8, bool P8>
+__device__ inline void qk01(KAddr ka, const QOp<QF8> &q, const Rope &rope, const uint8_t *row, uint32_t dst,
+                            float sc2, Half0<P8> &o) {
+  if constexpr (QF8) {
+    if constexpr (P8) qk01_fp8q_p8(ka, q, row, dst, sc2, o);
+    else qk01_fp8q_p16(ka, q, row, dst, sc2, o);
+  } else {
+    if constexpr (P8) qk01_split_p8(ka, q, rope, row, dst, sc2, o);
+    else qk01_split_p16(ka, q, rope, row, dst, sc2, o);
   }
 }
 
@@ -1520,29 +2396,31 @@ attention_fp8_kernel(AttnArgs a) {
       // barrier), and every wave is done with the tile of unit uu - 2
       wait_direct_loads();
       __syncthreads();
-      // the first score block also issues the next unit's tile loads
-      floatx16 s0;
+      // the scores of both tile halves, the next unit's tile loads and the
+      // half-0 ceiling and probabilities (groups 0..3): one block when no
+      // row's window ends inside the stage and a next tile is loaded; else
+      // two, with the half-0 scores masked between them
+      const bool edge = !__all(lim > 59);
+      const uint32_t ndst = stage_dst(lds_base + (buf == kBufs - 1 ? 0 : buf + 1) * Tile8::kBytes, wave);
+      Half0<P8> h0;
+      h0.sf0 = 0.f;
+      if (more1 && !edge) {
+        qk01<QF8, P8>(ka0, q, rope, nrow, ndst, sc2, h0);
+      } else {
+        floatx16 s0 = more1 ? scores_dma<QF8>(ka0, q, rope, nrow, ndst) : scores<QF8>(ka0, q, rope);
+        if (edge) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s0[r] = 8 * (r >> 2) + (r & 3) < lim ? s0[r] : kNegInf;
+        }
+        qk1<QF8, P8>(k_addr(tile + Tile8::kHalfBytes), q, rope, s0, sc2, h0);
+      }
       if (more1) {
-        const uint32_t nb = buf == kBufs - 1 ? 0 : buf + 1;
-        s0 = scores_dma<QF8>(ka0, q, rope, nrow, stage_dst(lds_base + nb * Tile8::kBytes, wave));
         if (k == nst - 1) following = nx;
         if (uu + 2 < hi) {
           nx = wk.advance(nx, uu + 2);
           page = page_of(nx);
         }
-      } else {
-        s0 = scores<QF8>(ka0, q, rope);
       }
-      const bool edge = !__all(lim > 59);   // some row's window ends inside this stage
-      if (edge) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s0[r] = 8 * (r >> 2) + (r & 3) < lim ? s0[r] : kNegInf;
-      }
-      // the second block: scores of half 1, and between its products the
-      // half-0 ceiling and probabilities (groups 0..3)
-      Half0<P8> h0;
-      h0.sf0 = 0.f;
-      qk1<QF8, P8>(k_addr(tile + Tile8::kHalfBytes), q, rope, s0, sc2, h0);
       floatx16 s1 = h0.s1;
       // the pending stage's probabilities and first value blocks: their LDS
       // latency runs under the half-1 maximum
@@ -1585,7 +2463,7 @@ attention_fp8_kernel(AttnArgs a) {
         // probabilities, the first the half-1 maximum above
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          if (c & 1) p_group<P8>(s0, s1, 4 + (c >> 1), sc2, msub1, pc, sf1);
+          if (c & 1) p_group<P8>(s1, s1, 4 + (c >> 1), sc2, msub1, pc, sf1);
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const int d = 2 * c + j;
@@ -1597,7 +2475,7 @@ attention_fp8_kernel(AttnArgs a) {
         }
       } else {
 #pragma unroll
-        for (int g = 4; g < 8; ++g) p_group<P8>(s0, s1, g, sc2, msub1, pc, sf1);
+        for (int g = 4; g < 8; ++g) p_group<P8>(s1, s1, g, sc2, msub1, pc, sf1);
       }
       put_p<P8>(parea, pc);
       // the stage sums join the row sums in the reference frame, each half

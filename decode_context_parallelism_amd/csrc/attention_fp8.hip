@@ -275,6 +275,9 @@ __device__ inline KAddr k_addr(uint32_t half_base) {
   return k;
 }
 
+// The asm score blocks below (scores_*, qk1_*, qk01_*) are written by
+// gen_score_blocks.py beside this file; edit the generator, not the blocks.
+//
 // S^T for one 32-token half of a tile: the nine 64-dim steps' hi (and lo)
 // products in one asm block.  Per step two 16-byte tile reads (blocks
 // 4 st + 2h and 4 st + 2h + 1: 32 dims of this lane's token row) feed the
@@ -335,14 +338,12 @@ __device__ inline floatx16 scores_split(KAddr ka, const QOp<false> &q, const Rop
       "s_nop 15\n\t"
       "s_nop 3\n\t"
       : [acc] "=&v"(acc)
-      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]), [q3] "v"(q.v[3]),
-        [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]), [q8] "v"(q.v[8]),
-        [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]),
-        [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(rope.hi),
-        [q17] "v"(rope.lo)
-      : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242",
-        "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253",
-        "v254", "v255", "memory");
+      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
+        [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
+        [q8] "v"(q.v[8]), [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]),
+        [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(rope.hi), [q17] "v"(rope.lo)
+      : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244",
+        "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory");
   return acc;
 }
 
@@ -390,11 +391,11 @@ __device__ inline floatx16 scores_fp8q(KAddr ka, const QOp<true> &q) {
       "s_nop 15\n\t"
       "s_nop 3\n\t"
       : [acc] "=&v"(acc)
-      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]), [q3] "v"(q.v[3]),
-        [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]), [q8] "v"(q.v[8])
-      : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242",
-        "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253",
-        "v254", "v255", "memory");
+      : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
+        [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
+        [q8] "v"(q.v[8])
+      : "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244",
+        "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory");
   return acc;
 }
 
@@ -598,8 +599,8 @@ template <> struct Half0<true> { floatx16 s1; float ms0, sf0; int hi[4]; };
 // with the wait states an XDL result needs before a VALU reads it).  The
 // VALU work uses v222 and v224..v231 as scratch; besides the exponentials'
 // one wait state, it touches no register the products read or write.
-__device__ inline void qk1_split_p16(KAddr ka, const QOp<false> &q, const Rope &rope,
-                                     const floatx16 &s0, float sc2, Half0<false> &o) {
+__device__ inline void qk1_split_p16(KAddr ka, const QOp<false> &q, const Rope &rope, const floatx16 &s0,
+                                     float sc2, Half0<false> &o) {
   asm volatile(
       "s_waitcnt lgkmcnt(0)\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
@@ -773,8 +774,8 @@ __device__ inline void qk1_split_p16(KAddr ka, const QOp<false> &q, const Rope &
         "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory");
 }
 
-__device__ inline void qk1_split_p8(KAddr ka, const QOp<false> &q, const Rope &rope,
-                                    const floatx16 &s0, float sc2, Half0<true> &o) {
+__device__ inline void qk1_split_p8(KAddr ka, const QOp<false> &q, const Rope &rope, const floatx16 &s0,
+                                    float sc2, Half0<true> &o) {
   asm volatile(
       "s_waitcnt lgkmcnt(0)\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
@@ -915,8 +916,8 @@ __device__ inline void qk1_split_p8(KAddr ka, const QOp<false> &q, const Rope &r
         "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory");
 }
 
-__device__ inline void qk1_fp8q_p16(KAddr ka, const QOp<true> &q,
-                                    const floatx16 &s0, float sc2, Half0<false> &o) {
+__device__ inline void qk1_fp8q_p16(KAddr ka, const QOp<true> &q, const floatx16 &s0, float sc2,
+                                    Half0<false> &o) {
   asm volatile(
       "s_waitcnt lgkmcnt(0)\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:0\n\t"
@@ -1079,8 +1080,8 @@ __device__ inline void qk1_fp8q_p16(KAddr ka, const QOp<true> &q,
         "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory");
 }
 
-__device__ inline void qk1_fp8q_p8(KAddr ka, const QOp<true> &q,
-                                   const floatx16 &s0, float sc2, Half0<true> &o) {
+__device__ inline void qk1_fp8q_p8(KAddr ka, const QOp<true> &q, const floatx16 &s0, float sc2,
+                                   Half0<true> &o) {
   asm volatile(
       "s_waitcnt lgkmcnt(0)\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:0\n\t"

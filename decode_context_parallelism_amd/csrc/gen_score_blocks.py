@@ -1,0 +1,304 @@
+"""Generator of the inline-asm score blocks of attention_fp8.hip.
+
+The FP8-cache attention kernel runs its score products as asm blocks with fixed
+register tuples (the compiler, left to schedule them, moved the output
+accumulator out of its AGPRs to hold the scores and waited for each step's
+reads before its products).  The blocks follow a few regular patterns, so they
+are written by this script rather than by hand:
+
+  scores_{split,fp8q}       nine 64-dim steps of one tile half: per step two
+                            16-byte key reads (two steps ahead, three tuples
+                            v[232:255]) and the query terms' products;
+  scores_{split,fp8q}_dma   the same with the next tile's nine direct loads,
+                            one after each step's products;
+  qk1_{split,fp8q}_{p16,p8} tile half 1's products with the half-0 softmax
+                            between them (row maximum over the lane and its
+                            partner lane, ceiling, probability groups 0..3
+                            with their fp32 sum; p16 also the E5M2 remainder);
+  qk01_{split,fp8q}_{p16,p8} both halves in one block: half 0 with the loads,
+                            half 1 with the half-0 softmax, the key reads two
+                            steps ahead across the halves; the half-0 scores
+                            stay in v[206:221].
+
+python gen_score_blocks.py --write   rewrite those functions in attention_fp8.hip
+python gen_score_blocks.py --check   exit 1 if the source differs from the generator
+"""
+import os
+import re
+import sys
+
+SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "attention_fp8.hip")
+
+T = ["v[240:247]", "v[248:255]", "v[232:239]"]          # key operand tuples, step % 3
+R = [("v[240:243]", "v[244:247]"), ("v[248:251]", "v[252:255]"), ("v[232:235]", "v[236:239]")]
+HALF = 18432        # bytes of a tile half
+STEP = 2048         # bytes of a 64-dim step of a tile half
+S0 = 206            # the merged block's half-0 accumulator v[206:221]
+NEG_2_30 = "0xce800000"
+
+
+def wrap(items, width=104):
+    out, line = [], ""
+    for i, it in enumerate(items):
+        piece = it + (", " if i + 1 < len(items) else "")
+        if len(line) + len(piece.rstrip()) > width and line.strip():
+            out.append(line.rstrip())
+            line = ""
+        line += piece
+    out.append(line.rstrip())
+    return "\n        ".join(out)
+
+
+def q_inputs(split):
+    if split:
+        return [f'[q{i}] "v"(q.v[{i}])' for i in range(16)] + ['[q16] "v"(rope.hi)', '[q17] "v"(rope.lo)']
+    return [f'[q{i}] "v"(q.v[{i}])' for i in range(9)]
+
+
+def signature(head, parts):
+    lines, cur = [], head
+    for i, p in enumerate(parts):
+        piece = p + ("," if i + 1 < len(parts) else ") {")
+        if len(cur) + len(piece) + 1 > 110 and cur.strip() != head.strip():
+            lines.append(cur.rstrip())
+            cur = " " * len(head)
+        cur += piece + " "
+    lines.append(cur.rstrip())
+    return "\n".join(lines) + "\n"
+
+
+def softmax_ops(p8, s=lambda i: f"%[s{i}]"):
+    """Half-0 softmax: row maximum with the partner lane, ceiling ms0 (-2^30 if
+    nothing is visible), then groups 0..3 of p' = 2^(s * sc2 - ms0 + 8)."""
+    ops = [
+        f"v_max3_f32 v224, {s(0)}, {s(1)}, {s(2)}",
+        f"v_max3_f32 v225, {s(3)}, {s(4)}, {s(5)}",
+        f"v_max3_f32 v226, {s(6)}, {s(7)}, {s(8)}",
+        f"v_max3_f32 v227, {s(9)}, {s(10)}, {s(11)}",
+        f"v_max3_f32 v228, {s(12)}, {s(13)}, {s(14)}",
+        "v_max3_f32 v224, v224, v225, v226",
+        f"v_max3_f32 v227, v227, v228, {s(15)}",
+        "v_max_f32 v224, v224, v227",
+        "v_mov_b32 v225, v224",
+        "s_nop 1",                                   # VALU write -> permlane read
+        "v_permlane32_swap_b32 v224, v225",          # one of the two now holds the partner's
+        "v_max_f32 v224, v224, v225",
+        "v_mul_f32 v224, v224, %[sc2]",
+        "v_ceil_f32 v224, v224",
+        f"v_max_f32 %[ms0], {NEG_2_30}, v224",
+        "v_sub_f32 v222, 0x41000000, %[ms0]",        # 8 - ms0
+    ]
+    for g in range(4):
+        for i in range(4):
+            ops.append(f"v_fma_f32 v{224 + i}, {s(4 * g + i)}, %[sc2], v222")
+        for i in range(4):
+            ops.append(f"v_exp_f32 v{224 + i}, v{224 + i}")
+        ops += ["s_nop 0",                           # exponential -> VALU read
+                "v_add_f32 v228, v224, v225",
+                "v_add_f32 v229, v226, v227",
+                f"v_cvt_pk_fp8_f32 %[hi{g}], v224, v225",
+                f"v_cvt_pk_fp8_f32 %[hi{g}], v226, v227 op_sel:[0,0,1]",
+                "v_add_f32 v228, v228, v229",
+                "v_add_f32 %[sf], %[sf], v228"]
+        if not p8:
+            ops += [f"v_cvt_pk_f32_fp8 v[228:229], %[hi{g}]",
+                    f"v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi{g}] src0_sel:WORD_1",
+                    "v_sub_f32 v228, v224, v228",
+                    "v_sub_f32 v229, v225, v229",
+                    "v_sub_f32 v230, v226, v230",
+                    "v_sub_f32 v231, v227, v231",
+                    f"v_cvt_pk_bf8_f32 %[lo{g}], v228, v229",
+                    f"v_cvt_pk_bf8_f32 %[lo{g}], v230, v231 op_sel:[0,0,1]"]
+    return ops
+
+
+def q(line):
+    return f'"{line}\\n\\t"'
+
+
+def one_half(terms, dma_steps=(), softmax=None):
+    """Body of a one-half block.  dma_steps: steps after whose products a load
+    is issued (load operands g0..); softmax: VALU ops spread over the products."""
+    out = []
+    e = out.append
+    ops = list(softmax or [])
+    per = -(-len(ops) // (9 * terms)) if ops else 0
+    if dma_steps:
+        e(q("s_mov_b32 %[m0s], m0"))
+        e(q("s_mov_b32 m0, %[dst]"))
+    e(q("s_waitcnt lgkmcnt(0)"))
+
+    def reads(st):
+        a, b = R[st % 3]
+        e(q(f"ds_read_b128 {a}, %[a0] offset:{STEP * st}"))
+        e(q(f"ds_read_b128 {b}, %[a1] offset:{STEP * st}"))
+    reads(0)
+    reads(1)
+    g, k = 0, 0
+    for st in range(9):
+        e(q("s_waitcnt lgkmcnt(2)") if st < 8 else q("s_waitcnt lgkmcnt(0)"))
+        for tm in range(terms):
+            src = "0" if (st == 0 and tm == 0) else "%[acc]"
+            e(q(f"v_mfma_f32_32x32x64_f8f6f4 %[acc], {T[st % 3]}, %[q{terms * st + tm}], {src}"))
+            n = len(ops) - k if (st == 8 and tm == terms - 1) else per
+            for _ in range(n):
+                if k < len(ops):
+                    e(q(ops[k]))
+                    k += 1
+        if st in dma_steps:
+            e(q(f"global_load_lds_dwordx4 %[g{g}], off"))
+            g += 1
+            if g < len(dma_steps):
+                e(q("s_add_u32 m0, m0, 2048"))
+        if st + 2 < 9:
+            reads(st + 2)
+    if dma_steps:
+        e(q("s_mov_b32 m0, %[m0s]"))
+    e(q("s_nop 15"))          # XDL result -> VALU read
+    e(q("s_nop 3"))
+    return out
+
+
+def both_halves(terms, p8):
+    out = []
+    e = out.append
+    ops = softmax_ops(p8, lambda i: f"v{S0 + i}")
+    per = -(-len(ops) // (9 * terms - 1))
+    e(q("s_mov_b32 %[m0s], m0"))
+    e(q("s_mov_b32 m0, %[dst]"))
+    e(q("s_waitcnt lgkmcnt(0)"))
+
+    def reads(gs):
+        a, b = R[gs % 3]
+        off = (gs // 9) * HALF + (gs % 9) * STEP
+        e(q(f"ds_read_b128 {a}, %[a0] offset:{off}"))
+        e(q(f"ds_read_b128 {b}, %[a1] offset:{off}"))
+    reads(0)
+    reads(1)
+    k = 0
+    for gs in range(18):
+        half, st = divmod(gs, 9)
+        acc = f"v[{S0}:{S0 + 15}]" if half == 0 else "%[s1]"
+        e(q("s_waitcnt lgkmcnt(2)") if gs < 17 else q("s_waitcnt lgkmcnt(0)"))
+        for tm in range(terms):
+            src = "0" if (st == 0 and tm == 0) else acc
+            e(q(f"v_mfma_f32_32x32x64_f8f6f4 {acc}, {T[gs % 3]}, %[q{terms * st + tm}], {src}"))
+            if half == 1:
+                if gs == 9 and tm == 0:
+                    e(q("s_nop 15"))      # XDL result -> VALU read of the half-0 scores
+                    e(q("s_nop 3"))
+                    continue
+                n = len(ops) - k if (st == 8 and tm == terms - 1) else per
+                for _ in range(n):
+                    if k < len(ops):
+                        e(q(ops[k]))
+                        k += 1
+        if half == 0:
+            # load st: row bytes 64 st on; the offset also moves the LDS
+            # destination, so M0 steps by 2048 - 64
+            e(q("global_load_lds_dwordx4 %[row], off" + (f" offset:{64 * st}" if st else "")))
+            if st < 8:
+                e(q(f"s_add_u32 m0, m0, {STEP - 64}"))
+        if gs + 2 < 18:
+            reads(gs + 2)
+    assert k == len(ops)
+    e(q("s_mov_b32 m0, %[m0s]"))
+    e(q("s_nop 15"))
+    e(q("s_nop 3"))
+    return out
+
+
+def function(kind, split, p8=False):
+    terms = 2 if split else 1
+    qname = "split" if split else "fp8q"
+    base = ["KAddr ka", "const QOp<false> &q", "const Rope &rope"] if split else ["KAddr ka", "const QOp<true> &q"]
+    ins = ['[a0] "v"(ka.a0)', '[a1] "v"(ka.a1)'] + q_inputs(split)
+    clob_regs = list(range(232, 256))
+    flags = ['"memory"']
+    if kind == "scores":
+        name, ret = f"scores_{qname}", "floatx16"
+        parts, outs, body = base, ['[acc] "=&v"(acc)'], one_half(terms)
+    elif kind == "scores_dma":
+        name, ret = f"scores_{qname}_dma", "floatx16"
+        parts = base + ["const uint8_t *row", "uint32_t dst"]
+        outs = ['[acc] "=&v"(acc)', '[m0s] "=&s"(saved)']
+        ins += [f'[g{k}] "v"(row + {64 * k})' for k in range(9)] + ['[dst] "s"(dst)']
+        body = one_half(terms, dma_steps=tuple(range(9)))
+        flags.append('"scc"')
+    elif kind == "qk1":
+        name, ret = f"qk1_{qname}_{'p8' if p8 else 'p16'}", "void"
+        parts = base + ["const floatx16 &s0", "float sc2", f"Half0<{'true' if p8 else 'false'}> &o"]
+        outs = ['[acc] "=&v"(o.s1)', '[ms0] "=&v"(o.ms0)', '[sf] "+v"(o.sf0)']
+        outs += [f'[hi{g}] "=&v"(o.hi[{g}])' for g in range(4)]
+        if not p8:
+            outs += [f'[lo{g}] "=&v"(o.lo[{g}])' for g in range(4)]
+        ins += [f'[s{i}] "v"(s0[{i}])' for i in range(16)] + ['[sc2] "v"(sc2)']
+        body = one_half(terms, softmax=softmax_ops(p8))
+        clob_regs = [222] + list(range(224, 256))
+    else:   # qk01
+        name, ret = f"qk01_{qname}_{'p8' if p8 else 'p16'}", "void"
+        parts = base + ["const uint8_t *row", "uint32_t dst", "float sc2", f"Half0<{'true' if p8 else 'false'}> &o"]
+        outs = ['[s1] "=&v"(o.s1)', '[ms0] "=&v"(o.ms0)', '[sf] "+v"(o.sf0)']
+        outs += [f'[hi{g}] "=&v"(o.hi[{g}])' for g in range(4)]
+        if not p8:
+            outs += [f'[lo{g}] "=&v"(o.lo[{g}])' for g in range(4)]
+        outs.append('[m0s] "=&s"(saved)')
+        ins += ['[row] "v"(row)', '[dst] "s"(dst)', '[sc2] "v"(sc2)']
+        body = both_halves(terms, p8)
+        clob_regs = list(range(S0, S0 + 16)) + [222] + list(range(224, 256))
+        flags.append('"scc"')
+    clob = [f'"v{r}"' for r in clob_regs] + flags
+    s = signature(f"__device__ inline {ret} {name}(", parts)
+    if ret == "floatx16":
+        s += "  floatx16 acc;\n"
+    if kind in ("scores_dma", "qk01"):
+        s += "  uint32_t saved;\n"
+    s += "  asm volatile(\n" + "\n".join("      " + l for l in body) + "\n"
+    s += "      : " + wrap(outs) + "\n"
+    s += "      : " + wrap(ins) + "\n"
+    s += "      : " + wrap(clob) + ");\n"
+    if ret == "floatx16":
+        s += "  return acc;\n"
+    s += "}\n"
+    return name, s
+
+
+def all_functions():
+    out = []
+    for split in (True, False):
+        out.append(function("scores", split))
+        out.append(function("scores_dma", split))
+        for p8 in (False, True):
+            out.append(function("qk1", split, p8))
+            out.append(function("qk01", split, p8))
+    return out
+
+
+def locate(src, name):
+    m = re.search(r"^__device__ inline (?:floatx16|void) " + re.escape(name) + r"\(", src, re.M)
+    if not m:
+        raise KeyError(name)
+    end = src.index("\n}\n", m.start()) + 3
+    return m.start(), end
+
+
+def main():
+    src = open(SRC).read()
+    new = src
+    for name, text in all_functions():
+        i, j = locate(new, name)
+        new = new[:i] + text + new[j:]
+    if "--write" in sys.argv:
+        if new != src:
+            open(SRC, "w").write(new)
+        print("written" if new != src else "unchanged")
+        return 0
+    if new != src:
+        print("attention_fp8.hip differs from gen_score_blocks.py; run it with --write")
+        return 1
+    print("attention_fp8.hip matches gen_score_blocks.py")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -84,3 +84,12 @@ def test_loop_keeps_output_accumulator_in_agprs(fp8_asm):
         reads = sum(1 for l in loop if "v_accvgpr_read_b32" in l)
         # only the rare rescale path reads them (256 reads, once)
         assert reads <= 256, (name, reads)
+
+
+def test_score_blocks_match_their_generator():
+    # the asm score blocks are written by gen_score_blocks.py; the source must
+    # be what the generator writes
+    import sys
+    gen = os.path.join(CSRC, "gen_score_blocks.py")
+    res = subprocess.run([sys.executable, gen, "--check"], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stdout + res.stderr

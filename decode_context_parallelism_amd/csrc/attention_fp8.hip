@@ -2417,13 +2417,19 @@ attention_fp8_kernel(AttnArgs a) {
         }
         qk1<QF8, P8>(k_addr(tile + Tile8::kHalfBytes), q, rope, s0, sc2, h0);
       }
-      if (more1) {
-        if (k == nst - 1) following = nx;
-        if (uu + 2 < hi) {
-          nx = wk.advance(nx, uu + 2);
-          page = page_of(nx);
+      // the cursor of the unit two ahead and its page id (loaded now, used by
+      // the next stage's row address): in the p.v phase after its first chunk
+      // when there is one, where its issue overlaps the products
+      auto advance_next = [&]() __attribute__((always_inline)) {
+        if (more1) {
+          if (k == nst - 1) following = nx;
+          if (uu + 2 < hi) {
+            nx = wk.advance(nx, uu + 2);
+            page = page_of(nx);
+          }
         }
-      }
+      };
+      if constexpr (!PREV) advance_next();
       floatx16 s1 = h0.s1;
       // the pending stage's probabilities and first value blocks: their LDS
       // latency runs under the half-1 maximum
@@ -2475,6 +2481,7 @@ attention_fp8_kernel(AttnArgs a) {
             if constexpr (!P8) oacc[d] = mma_pv_lo(va[d % 3], pp.lo, oacc[d], epend);
           }
           chunk_order<P8>();
+          if (c == 0) advance_next();
         }
       } else {
 #pragma unroll

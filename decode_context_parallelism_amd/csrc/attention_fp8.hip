@@ -586,10 +586,24 @@ template <> struct POp<true> { int8v hi; };
 // What the second score block hands back besides the half-1 scores s1: the
 // half-0 ceiling ms0 (-2^30 when the row sees nothing in that half), the
 // probabilities of groups 0..3 (registers 0..3 of the P operand) and their
-// fp32 sum.
+// fp32 sum; the one-block form also the lanes whose next-tile page was
+// outside the pool (badm).
 template <bool P8> struct Half0;
-template <> struct Half0<false> { floatx16 s1; float ms0, sf0; int hi[4], lo[4]; };
-template <> struct Half0<true> { floatx16 s1; float ms0, sf0; int hi[4]; };
+template <> struct Half0<false> { floatx16 s1; float ms0, sf0; int hi[4], lo[4]; uint64_t badm; };
+template <> struct Half0<true> { floatx16 s1; float ms0, sf0; int hi[4]; uint64_t badm; };
+
+// The one-block score phase computes the next tile's row addresses itself
+// (the same token, page and zero-row rules as stage_row), while its first
+// key reads are in flight: this lane's page id of the next unit and the
+// wave-uniform rest.  Row indices are 32-bit: a pool of 2^32 rows would be
+// 2.4 TB.
+struct NextRow {
+  int32_t page;            // this lane's page id (vector)
+  int ts;                  // 64 s + 32 (wave's half) + 16 (wave & 1): the lane's token less its slot part
+  int lmax, mask, shift;   // the unit's row length; page size - 1 and its log2
+  int np;                  // pages in the pool, at most 2^31 - 1
+  const uint8_t *pool, *zero;
+};
 
 // The scores of tile half 1, with the half-0 softmax between the products:
 // the row maximum of s0 over this lane and its partner lane (l ^ 32), the
@@ -1218,9 +1232,10 @@ __device__ inline void qk1_fp8q_p8(KAddr ka, const QOp<true> &q, const floatx16 
 // halves.  The half-0 scores live in v206..v221 inside the block only.  The
 // loads take one address: the immediate offset 64 k moves the LDS
 // destination as well as the source, so M0 advances by 2048 - 64 per load.
-__device__ inline void qk01_split_p16(KAddr ka, const QOp<false> &q, const Rope &rope, const uint8_t *row,
+__device__ inline void qk01_split_p16(KAddr ka, const QOp<false> &q, const Rope &rope, const NextRow &nr,
                                       uint32_t dst, float sc2, Half0<false> &o) {
   uint32_t saved;
+  uint64_t inm;
   asm volatile(
       "s_mov_b32 %[m0s], m0\n\t"
       "s_mov_b32 m0, %[dst]\n\t"
@@ -1231,64 +1246,90 @@ __device__ inline void qk01_split_p16(KAddr ka, const QOp<false> &q, const Rope 
       "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q0], 0\n\t"
+      "v_mbcnt_lo_u32_b32 v224, -1, 0\n\t"
+      "v_mbcnt_hi_u32_b32 v224, -1, v224\n\t"
+      "v_lshrrev_b32 v225, 1, v224\n\t"
+      "v_and_b32 v225, 8, v225\n\t"
+      "v_and_b32 v226, 15, v224\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q1], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off\n\t"
-      "s_add_u32 m0, m0, 1984\n\t"
+      "v_xor_b32 v225, v225, v226\n\t"
+      "v_lshrrev_b32 v226, 1, v225\n\t"
+      "v_xor_b32 v226, v226, v225\n\t"
+      "v_and_b32 v226, 4, v226\n\t"
+      "v_mul_u32_u24 v226, 3, v226\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q2], v[206:221]\n\t"
+      "v_xor_b32 v225, v225, v226\n\t"
+      "v_add_u32 v225, %[ts], v225\n\t"
+      "v_cmp_gt_i32 %[inm], %[lmax], v225\n\t"
+      "v_and_b32 v226, %[mask], v225\n\t"
+      "v_lshl_add_u32 v227, %[page], %[shift], v226\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q3], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:64\n\t"
-      "s_add_u32 m0, m0, 1984\n\t"
+      "v_and_b32 v224, 0x30, v224\n\t"
+      "v_mov_b32 v225, 0\n\t"
+      "v_lshl_add_u64 v[228:229], v[224:225], 0, %[pool]\n\t"
+      "v_mov_b32 v226, 0x240\n\t"
+      "v_mad_u64_u32 v[230:231], vcc, v227, v226, v[228:229]\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q4], v[206:221]\n\t"
+      "v_lshl_add_u64 v[228:229], v[224:225], 0, %[zero]\n\t"
+      "v_cmp_gt_u32 vcc, %[np], %[page]\n\t"
+      "s_andn2_b64 %[badm], %[inm], vcc\n\t"
+      "s_and_b64 vcc, %[inm], vcc\n\t"
+      "v_cndmask_b32 v230, v228, v230, vcc\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q5], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:128\n\t"
-      "s_add_u32 m0, m0, 1984\n\t"
+      "v_cndmask_b32 v231, v229, v231, vcc\n\t"
       "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
       "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q6], v[206:221]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q7], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:192\n\t"
+      "global_load_lds_dwordx4 v[230:231], off\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:64\n\t"
       "s_add_u32 m0, m0, 1984\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q8], v[206:221]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q9], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:256\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:128\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:192\n\t"
       "s_add_u32 m0, m0, 1984\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q10], v[206:221]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q11], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:320\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:256\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:320\n\t"
       "s_add_u32 m0, m0, 1984\n\t"
       "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
       "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q12], v[206:221]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q13], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:384\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:384\n\t"
       "s_add_u32 m0, m0, 1984\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q14], v[206:221]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q15], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:448\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:448\n\t"
       "s_add_u32 m0, m0, 1984\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:18432\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:18432\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q16], v[206:221]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q17], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:512\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:512\n\t"
       "ds_read_b128 v[248:251], %[a0] offset:20480\n\t"
       "ds_read_b128 v[252:255], %[a1] offset:20480\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
@@ -1447,21 +1488,23 @@ __device__ inline void qk01_split_p16(KAddr ka, const QOp<false> &q, const Rope 
       "s_nop 3\n\t"
       : [s1] "=&v"(o.s1), [ms0] "=&v"(o.ms0), [sf] "+v"(o.sf0), [hi0] "=&v"(o.hi[0]), [hi1] "=&v"(o.hi[1]),
         [hi2] "=&v"(o.hi[2]), [hi3] "=&v"(o.hi[3]), [lo0] "=&v"(o.lo[0]), [lo1] "=&v"(o.lo[1]),
-        [lo2] "=&v"(o.lo[2]), [lo3] "=&v"(o.lo[3]), [m0s] "=&s"(saved)
+        [lo2] "=&v"(o.lo[2]), [lo3] "=&v"(o.lo[3]), [m0s] "=&s"(saved), [inm] "=&s"(inm), [badm] "=&s"(o.badm)
       : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
         [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
         [q8] "v"(q.v[8]), [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]),
         [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(rope.hi), [q17] "v"(rope.lo),
-        [row] "v"(row), [dst] "s"(dst), [sc2] "v"(sc2)
+        [page] "v"(nr.page), [ts] "s"(nr.ts), [lmax] "s"(nr.lmax), [mask] "s"(nr.mask), [shift] "s"(nr.shift),
+        [np] "s"(nr.np), [pool] "s"(nr.pool), [zero] "s"(nr.zero), [dst] "s"(dst), [sc2] "v"(sc2)
       : "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218",
         "v219", "v220", "v221", "v222", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232",
         "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245",
-        "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "scc");
+        "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "scc", "vcc");
 }
 
-__device__ inline void qk01_split_p8(KAddr ka, const QOp<false> &q, const Rope &rope, const uint8_t *row,
+__device__ inline void qk01_split_p8(KAddr ka, const QOp<false> &q, const Rope &rope, const NextRow &nr,
                                      uint32_t dst, float sc2, Half0<true> &o) {
   uint32_t saved;
+  uint64_t inm;
   asm volatile(
       "s_mov_b32 %[m0s], m0\n\t"
       "s_mov_b32 m0, %[dst]\n\t"
@@ -1472,64 +1515,90 @@ __device__ inline void qk01_split_p8(KAddr ka, const QOp<false> &q, const Rope &
       "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q0], 0\n\t"
+      "v_mbcnt_lo_u32_b32 v224, -1, 0\n\t"
+      "v_mbcnt_hi_u32_b32 v224, -1, v224\n\t"
+      "v_lshrrev_b32 v225, 1, v224\n\t"
+      "v_and_b32 v225, 8, v225\n\t"
+      "v_and_b32 v226, 15, v224\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q1], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off\n\t"
-      "s_add_u32 m0, m0, 1984\n\t"
+      "v_xor_b32 v225, v225, v226\n\t"
+      "v_lshrrev_b32 v226, 1, v225\n\t"
+      "v_xor_b32 v226, v226, v225\n\t"
+      "v_and_b32 v226, 4, v226\n\t"
+      "v_mul_u32_u24 v226, 3, v226\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q2], v[206:221]\n\t"
+      "v_xor_b32 v225, v225, v226\n\t"
+      "v_add_u32 v225, %[ts], v225\n\t"
+      "v_cmp_gt_i32 %[inm], %[lmax], v225\n\t"
+      "v_and_b32 v226, %[mask], v225\n\t"
+      "v_lshl_add_u32 v227, %[page], %[shift], v226\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q3], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:64\n\t"
-      "s_add_u32 m0, m0, 1984\n\t"
+      "v_and_b32 v224, 0x30, v224\n\t"
+      "v_mov_b32 v225, 0\n\t"
+      "v_lshl_add_u64 v[228:229], v[224:225], 0, %[pool]\n\t"
+      "v_mov_b32 v226, 0x240\n\t"
+      "v_mad_u64_u32 v[230:231], vcc, v227, v226, v[228:229]\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q4], v[206:221]\n\t"
+      "v_lshl_add_u64 v[228:229], v[224:225], 0, %[zero]\n\t"
+      "v_cmp_gt_u32 vcc, %[np], %[page]\n\t"
+      "s_andn2_b64 %[badm], %[inm], vcc\n\t"
+      "s_and_b64 vcc, %[inm], vcc\n\t"
+      "v_cndmask_b32 v230, v228, v230, vcc\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q5], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:128\n\t"
-      "s_add_u32 m0, m0, 1984\n\t"
+      "v_cndmask_b32 v231, v229, v231, vcc\n\t"
       "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
       "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q6], v[206:221]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q7], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:192\n\t"
+      "global_load_lds_dwordx4 v[230:231], off\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:64\n\t"
       "s_add_u32 m0, m0, 1984\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q8], v[206:221]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q9], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:256\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:128\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:192\n\t"
       "s_add_u32 m0, m0, 1984\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q10], v[206:221]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q11], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:320\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:256\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:320\n\t"
       "s_add_u32 m0, m0, 1984\n\t"
       "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
       "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q12], v[206:221]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q13], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:384\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:384\n\t"
       "s_add_u32 m0, m0, 1984\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q14], v[206:221]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q15], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:448\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:448\n\t"
       "s_add_u32 m0, m0, 1984\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:18432\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:18432\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q16], v[206:221]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q17], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:512\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:512\n\t"
       "ds_read_b128 v[248:251], %[a0] offset:20480\n\t"
       "ds_read_b128 v[252:255], %[a1] offset:20480\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
@@ -1655,21 +1724,23 @@ __device__ inline void qk01_split_p8(KAddr ka, const QOp<false> &q, const Rope &
       "s_nop 15\n\t"
       "s_nop 3\n\t"
       : [s1] "=&v"(o.s1), [ms0] "=&v"(o.ms0), [sf] "+v"(o.sf0), [hi0] "=&v"(o.hi[0]), [hi1] "=&v"(o.hi[1]),
-        [hi2] "=&v"(o.hi[2]), [hi3] "=&v"(o.hi[3]), [m0s] "=&s"(saved)
+        [hi2] "=&v"(o.hi[2]), [hi3] "=&v"(o.hi[3]), [m0s] "=&s"(saved), [inm] "=&s"(inm), [badm] "=&s"(o.badm)
       : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
         [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
         [q8] "v"(q.v[8]), [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]),
         [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(rope.hi), [q17] "v"(rope.lo),
-        [row] "v"(row), [dst] "s"(dst), [sc2] "v"(sc2)
+        [page] "v"(nr.page), [ts] "s"(nr.ts), [lmax] "s"(nr.lmax), [mask] "s"(nr.mask), [shift] "s"(nr.shift),
+        [np] "s"(nr.np), [pool] "s"(nr.pool), [zero] "s"(nr.zero), [dst] "s"(dst), [sc2] "v"(sc2)
       : "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218",
         "v219", "v220", "v221", "v222", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232",
         "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245",
-        "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "scc");
+        "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "scc", "vcc");
 }
 
-__device__ inline void qk01_fp8q_p16(KAddr ka, const QOp<true> &q, const uint8_t *row, uint32_t dst,
+__device__ inline void qk01_fp8q_p16(KAddr ka, const QOp<true> &q, const NextRow &nr, uint32_t dst,
                                      float sc2, Half0<false> &o) {
   uint32_t saved;
+  uint64_t inm;
   asm volatile(
       "s_mov_b32 %[m0s], m0\n\t"
       "s_mov_b32 m0, %[dst]\n\t"
@@ -1680,55 +1751,81 @@ __device__ inline void qk01_fp8q_p16(KAddr ka, const QOp<true> &q, const uint8_t
       "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q0], 0\n\t"
-      "global_load_lds_dwordx4 %[row], off\n\t"
-      "s_add_u32 m0, m0, 1984\n\t"
+      "v_mbcnt_lo_u32_b32 v224, -1, 0\n\t"
+      "v_mbcnt_hi_u32_b32 v224, -1, v224\n\t"
+      "v_lshrrev_b32 v225, 1, v224\n\t"
+      "v_and_b32 v225, 8, v225\n\t"
+      "v_and_b32 v226, 15, v224\n\t"
+      "v_xor_b32 v225, v225, v226\n\t"
+      "v_lshrrev_b32 v226, 1, v225\n\t"
+      "v_xor_b32 v226, v226, v225\n\t"
+      "v_and_b32 v226, 4, v226\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q1], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:64\n\t"
-      "s_add_u32 m0, m0, 1984\n\t"
+      "v_mul_u32_u24 v226, 3, v226\n\t"
+      "v_xor_b32 v225, v225, v226\n\t"
+      "v_add_u32 v225, %[ts], v225\n\t"
+      "v_cmp_gt_i32 %[inm], %[lmax], v225\n\t"
+      "v_and_b32 v226, %[mask], v225\n\t"
+      "v_lshl_add_u32 v227, %[page], %[shift], v226\n\t"
+      "v_and_b32 v224, 0x30, v224\n\t"
+      "v_mov_b32 v225, 0\n\t"
+      "v_lshl_add_u64 v[228:229], v[224:225], 0, %[pool]\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q2], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:128\n\t"
-      "s_add_u32 m0, m0, 1984\n\t"
+      "v_mov_b32 v226, 0x240\n\t"
+      "v_mad_u64_u32 v[230:231], vcc, v227, v226, v[228:229]\n\t"
+      "v_lshl_add_u64 v[228:229], v[224:225], 0, %[zero]\n\t"
+      "v_cmp_gt_u32 vcc, %[np], %[page]\n\t"
+      "s_andn2_b64 %[badm], %[inm], vcc\n\t"
+      "s_and_b64 vcc, %[inm], vcc\n\t"
+      "v_cndmask_b32 v230, v228, v230, vcc\n\t"
+      "v_cndmask_b32 v231, v229, v231, vcc\n\t"
       "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
       "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q3], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:192\n\t"
+      "global_load_lds_dwordx4 v[230:231], off\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:64\n\t"
       "s_add_u32 m0, m0, 1984\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q4], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:256\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:128\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:192\n\t"
       "s_add_u32 m0, m0, 1984\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q5], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:320\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:256\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:320\n\t"
       "s_add_u32 m0, m0, 1984\n\t"
       "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
       "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q6], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:384\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:384\n\t"
       "s_add_u32 m0, m0, 1984\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q7], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:448\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:448\n\t"
       "s_add_u32 m0, m0, 1984\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:18432\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:18432\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q8], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:512\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:512\n\t"
       "ds_read_b128 v[248:251], %[a0] offset:20480\n\t"
       "ds_read_b128 v[252:255], %[a1] offset:20480\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
@@ -1878,19 +1975,22 @@ __device__ inline void qk01_fp8q_p16(KAddr ka, const QOp<true> &q, const uint8_t
       "s_nop 3\n\t"
       : [s1] "=&v"(o.s1), [ms0] "=&v"(o.ms0), [sf] "+v"(o.sf0), [hi0] "=&v"(o.hi[0]), [hi1] "=&v"(o.hi[1]),
         [hi2] "=&v"(o.hi[2]), [hi3] "=&v"(o.hi[3]), [lo0] "=&v"(o.lo[0]), [lo1] "=&v"(o.lo[1]),
-        [lo2] "=&v"(o.lo[2]), [lo3] "=&v"(o.lo[3]), [m0s] "=&s"(saved)
+        [lo2] "=&v"(o.lo[2]), [lo3] "=&v"(o.lo[3]), [m0s] "=&s"(saved), [inm] "=&s"(inm), [badm] "=&s"(o.badm)
       : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
         [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
-        [q8] "v"(q.v[8]), [row] "v"(row), [dst] "s"(dst), [sc2] "v"(sc2)
+        [q8] "v"(q.v[8]), [page] "v"(nr.page), [ts] "s"(nr.ts), [lmax] "s"(nr.lmax), [mask] "s"(nr.mask),
+        [shift] "s"(nr.shift), [np] "s"(nr.np), [pool] "s"(nr.pool), [zero] "s"(nr.zero), [dst] "s"(dst),
+        [sc2] "v"(sc2)
       : "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218",
         "v219", "v220", "v221", "v222", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232",
         "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245",
-        "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "scc");
+        "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "scc", "vcc");
 }
 
-__device__ inline void qk01_fp8q_p8(KAddr ka, const QOp<true> &q, const uint8_t *row, uint32_t dst,
-                                    float sc2, Half0<true> &o) {
+__device__ inline void qk01_fp8q_p8(KAddr ka, const QOp<true> &q, const NextRow &nr, uint32_t dst, float sc2,
+                                    Half0<true> &o) {
   uint32_t saved;
+  uint64_t inm;
   asm volatile(
       "s_mov_b32 %[m0s], m0\n\t"
       "s_mov_b32 m0, %[dst]\n\t"
@@ -1901,55 +2001,81 @@ __device__ inline void qk01_fp8q_p8(KAddr ka, const QOp<true> &q, const uint8_t 
       "ds_read_b128 v[252:255], %[a1] offset:2048\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q0], 0\n\t"
-      "global_load_lds_dwordx4 %[row], off\n\t"
-      "s_add_u32 m0, m0, 1984\n\t"
+      "v_mbcnt_lo_u32_b32 v224, -1, 0\n\t"
+      "v_mbcnt_hi_u32_b32 v224, -1, v224\n\t"
+      "v_lshrrev_b32 v225, 1, v224\n\t"
+      "v_and_b32 v225, 8, v225\n\t"
+      "v_and_b32 v226, 15, v224\n\t"
+      "v_xor_b32 v225, v225, v226\n\t"
+      "v_lshrrev_b32 v226, 1, v225\n\t"
+      "v_xor_b32 v226, v226, v225\n\t"
+      "v_and_b32 v226, 4, v226\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q1], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:64\n\t"
-      "s_add_u32 m0, m0, 1984\n\t"
+      "v_mul_u32_u24 v226, 3, v226\n\t"
+      "v_xor_b32 v225, v225, v226\n\t"
+      "v_add_u32 v225, %[ts], v225\n\t"
+      "v_cmp_gt_i32 %[inm], %[lmax], v225\n\t"
+      "v_and_b32 v226, %[mask], v225\n\t"
+      "v_lshl_add_u32 v227, %[page], %[shift], v226\n\t"
+      "v_and_b32 v224, 0x30, v224\n\t"
+      "v_mov_b32 v225, 0\n\t"
+      "v_lshl_add_u64 v[228:229], v[224:225], 0, %[pool]\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q2], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:128\n\t"
-      "s_add_u32 m0, m0, 1984\n\t"
+      "v_mov_b32 v226, 0x240\n\t"
+      "v_mad_u64_u32 v[230:231], vcc, v227, v226, v[228:229]\n\t"
+      "v_lshl_add_u64 v[228:229], v[224:225], 0, %[zero]\n\t"
+      "v_cmp_gt_u32 vcc, %[np], %[page]\n\t"
+      "s_andn2_b64 %[badm], %[inm], vcc\n\t"
+      "s_and_b64 vcc, %[inm], vcc\n\t"
+      "v_cndmask_b32 v230, v228, v230, vcc\n\t"
+      "v_cndmask_b32 v231, v229, v231, vcc\n\t"
       "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
       "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q3], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:192\n\t"
+      "global_load_lds_dwordx4 v[230:231], off\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:64\n\t"
       "s_add_u32 m0, m0, 1984\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:10240\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:10240\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q4], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:256\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:128\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:192\n\t"
       "s_add_u32 m0, m0, 1984\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:12288\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:12288\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q5], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:320\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:256\n\t"
+      "s_add_u32 m0, m0, 1984\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:320\n\t"
       "s_add_u32 m0, m0, 1984\n\t"
       "ds_read_b128 v[248:251], %[a0] offset:14336\n\t"
       "ds_read_b128 v[252:255], %[a1] offset:14336\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q6], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:384\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:384\n\t"
       "s_add_u32 m0, m0, 1984\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:16384\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:16384\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q7], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:448\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:448\n\t"
       "s_add_u32 m0, m0, 1984\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:18432\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:18432\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q8], v[206:221]\n\t"
-      "global_load_lds_dwordx4 %[row], off offset:512\n\t"
+      "global_load_lds_dwordx4 v[230:231], off offset:512\n\t"
       "ds_read_b128 v[248:251], %[a0] offset:20480\n\t"
       "ds_read_b128 v[252:255], %[a1] offset:20480\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
@@ -2066,14 +2192,16 @@ __device__ inline void qk01_fp8q_p8(KAddr ka, const QOp<true> &q, const uint8_t 
       "s_nop 15\n\t"
       "s_nop 3\n\t"
       : [s1] "=&v"(o.s1), [ms0] "=&v"(o.ms0), [sf] "+v"(o.sf0), [hi0] "=&v"(o.hi[0]), [hi1] "=&v"(o.hi[1]),
-        [hi2] "=&v"(o.hi[2]), [hi3] "=&v"(o.hi[3]), [m0s] "=&s"(saved)
+        [hi2] "=&v"(o.hi[2]), [hi3] "=&v"(o.hi[3]), [m0s] "=&s"(saved), [inm] "=&s"(inm), [badm] "=&s"(o.badm)
       : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
         [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
-        [q8] "v"(q.v[8]), [row] "v"(row), [dst] "s"(dst), [sc2] "v"(sc2)
+        [q8] "v"(q.v[8]), [page] "v"(nr.page), [ts] "s"(nr.ts), [lmax] "s"(nr.lmax), [mask] "s"(nr.mask),
+        [shift] "s"(nr.shift), [np] "s"(nr.np), [pool] "s"(nr.pool), [zero] "s"(nr.zero), [dst] "s"(dst),
+        [sc2] "v"(sc2)
       : "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218",
         "v219", "v220", "v221", "v222", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232",
         "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245",
-        "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "scc");
+        "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "scc", "vcc");
 }
 
 template <bool QF8, bool P8>
@@ -2088,14 +2216,14 @@ __device__ inline void qk1(KAddr ka, const QOp<QF8> &q, const Rope &rope, const 
   }
 }
 template <bool QF8, bool P8>
-__device__ inline void qk01(KAddr ka, const QOp<QF8> &q, const Rope &rope, const uint8_t *row, uint32_t dst,
+__device__ inline void qk01(KAddr ka, const QOp<QF8> &q, const Rope &rope, const NextRow &nr, uint32_t dst,
                             float sc2, Half0<P8> &o) {
   if constexpr (QF8) {
-    if constexpr (P8) qk01_fp8q_p8(ka, q, row, dst, sc2, o);
-    else qk01_fp8q_p16(ka, q, row, dst, sc2, o);
+    if constexpr (P8) qk01_fp8q_p8(ka, q, nr, dst, sc2, o);
+    else qk01_fp8q_p16(ka, q, nr, dst, sc2, o);
   } else {
-    if constexpr (P8) qk01_split_p8(ka, q, rope, row, dst, sc2, o);
-    else qk01_split_p16(ka, q, rope, row, dst, sc2, o);
+    if constexpr (P8) qk01_split_p8(ka, q, rope, nr, dst, sc2, o);
+    else qk01_split_p16(ka, q, rope, nr, dst, sc2, o);
   }
 }
 
@@ -2303,6 +2431,7 @@ attention_fp8_kernel(AttnArgs a) {
 
   auto pt_of = [&](const Cursor &c) { return a.page_table + (int64_t)c.lrow * a.max_local_pages; };
   auto page_of = [&](const Cursor &c) { return fetch_page(a, pt_of(c), c.s, c.lmax, wave); };
+  const int npages = (int)min(a.num_pages, (int64_t)0x7FFFFFFF);
   auto load_stage = [&](const Cursor &c, int32_t page, int buf) {
     issue_stage(lds_base + buf * Tile8::kBytes, stage_row(a, page, c.s, c.lmax, wave, &bad), wave);
   };
@@ -2394,7 +2523,6 @@ attention_fp8_kernel(AttnArgs a) {
       const int lim = rlen - s * kStage - 4 * hh;
       const KAddr ka0 = k_addr(tile);
       const bool more1 = uu + 1 < hi;
-      const uint8_t *nrow = more1 ? stage_row(a, page, nx.s, nx.lmax, wave, &bad) : a.zero_row;
       // tile uu has landed (this wave's share: the wait; every wave's: the
       // barrier), and every wave is done with the tile of unit uu - 2
       wait_direct_loads();
@@ -2408,8 +2536,19 @@ attention_fp8_kernel(AttnArgs a) {
       Half0<P8> h0;
       h0.sf0 = 0.f;
       if (more1 && !edge) {
-        qk01<QF8, P8>(ka0, q, rope, nrow, ndst, sc2, h0);
+        NextRow nr;
+        nr.page = page;
+        nr.ts = nx.s * kStage + 32 * load_half(wave) + 16 * (wave & 1);
+        nr.lmax = nx.lmax;
+        nr.mask = (1 << a.page_shift) - 1;
+        nr.shift = a.page_shift;
+        nr.np = npages;
+        nr.pool = a.pool;
+        nr.zero = a.zero_row;
+        qk01<QF8, P8>(ka0, q, rope, nr, ndst, sc2, h0);
+        bad = bad || h0.badm != 0;
       } else {
+        const uint8_t *nrow = more1 ? stage_row(a, page, nx.s, nx.lmax, wave, &bad) : a.zero_row;
         floatx16 s0 = more1 ? scores_dma<QF8>(ka0, q, rope, nrow, ndst) : scores<QF8>(ka0, q, rope);
         if (edge) {
 #pragma unroll

@@ -15,10 +15,12 @@ are written by this script rather than by hand:
                             between them (row maximum over the lane and its
                             partner lane, ceiling, probability groups 0..3
                             with their fp32 sum; p16 also the E5M2 remainder);
-  qk01_{split,fp8q}_{p16,p8} both halves in one block: half 0 with the loads,
-                            half 1 with the half-0 softmax, the key reads two
-                            steps ahead across the halves; the half-0 scores
-                            stay in v[206:221].
+  qk01_{split,fp8q}_{p16,p8} both halves in one block: half 0 with the next
+                            tile's row address (under the first three steps'
+                            products) and then its loads, half 1 with the
+                            half-0 softmax, the key reads two steps ahead
+                            across the halves; the half-0 scores stay in
+                            v[206:221].
 
 python gen_score_blocks.py --write   rewrite those functions in attention_fp8.hip
 python gen_score_blocks.py --check   exit 1 if the source differs from the generator
@@ -35,6 +37,7 @@ HALF = 18432        # bytes of a tile half
 STEP = 2048         # bytes of a 64-dim step of a tile half
 S0 = 206            # the merged block's half-0 accumulator v[206:221]
 NEG_2_30 = "0xce800000"
+ROW_STEPS = 3       # merged block: steps whose products cover the row address
 
 
 def wrap(items, width=104):
@@ -159,6 +162,45 @@ def one_half(terms, dma_steps=(), softmax=None):
     return out
 
 
+def row_ops():
+    """The next tile's row address for this lane's loads, into v[230:231],
+    spread over the first steps' products (v224..v231 are free until the
+    half-0 softmax).  The lane loads token t = ts + tok_slot(slot) of the next
+    unit, slot = (l & 15) ^ 8 l4 (ts: that unit's stage start plus the wave's
+    half and slot-block offset), 16 bytes at 16 (l >> 4) of its row: page
+    (page << shift) + (t & mask) of the pool, or the zero row when t is past
+    the row length (lmax) or the page is outside the pool (also reported in
+    badm)."""
+    return [
+        "v_mbcnt_lo_u32_b32 v224, -1, 0",
+        "v_mbcnt_hi_u32_b32 v224, -1, v224",
+        "v_lshrrev_b32 v225, 1, v224",
+        "v_and_b32 v225, 8, v225",
+        "v_and_b32 v226, 15, v224",
+        "v_xor_b32 v225, v225, v226",             # slot
+        "v_lshrrev_b32 v226, 1, v225",            # tok_slot: swap slot bits 2 and 3
+        "v_xor_b32 v226, v226, v225",
+        "v_and_b32 v226, 4, v226",
+        "v_mul_u32_u24 v226, 3, v226",
+        "v_xor_b32 v225, v225, v226",
+        "v_add_u32 v225, %[ts], v225",            # t
+        "v_cmp_gt_i32 %[inm], %[lmax], v225",     # t < lmax
+        "v_and_b32 v226, %[mask], v225",
+        "v_lshl_add_u32 v227, %[page], %[shift], v226",
+        "v_and_b32 v224, 0x30, v224",             # 16 (l >> 4)
+        "v_mov_b32 v225, 0",
+        "v_lshl_add_u64 v[228:229], v[224:225], 0, %[pool]",
+        "v_mov_b32 v226, 0x240",                  # 576 bytes a row
+        "v_mad_u64_u32 v[230:231], vcc, v227, v226, v[228:229]",
+        "v_lshl_add_u64 v[228:229], v[224:225], 0, %[zero]",
+        "v_cmp_gt_u32 vcc, %[np], %[page]",       # page inside the pool
+        "s_andn2_b64 %[badm], %[inm], vcc",
+        "s_and_b64 vcc, %[inm], vcc",
+        "v_cndmask_b32 v230, v228, v230, vcc",
+        "v_cndmask_b32 v231, v229, v231, vcc",
+    ]
+
+
 def both_halves(terms, p8):
     out = []
     e = out.append
@@ -175,6 +217,14 @@ def both_halves(terms, p8):
         e(q(f"ds_read_b128 {b}, %[a1] offset:{off}"))
     reads(0)
     reads(1)
+    # the row address under the first ROW_STEPS steps' products, then the nine
+    # loads over the remaining half-0 steps
+    rops = row_ops()
+    rper = -(-len(rops) // (ROW_STEPS * terms))
+    nload = 9 - ROW_STEPS
+    per_step = [9 // nload + (1 if i < 9 % nload else 0) for i in range(nload)]
+    load_at = {ROW_STEPS + i: n for i, n in enumerate(per_step)}
+    ld = 0
     k = 0
     for gs in range(18):
         half, st = divmod(gs, 9)
@@ -183,6 +233,10 @@ def both_halves(terms, p8):
         for tm in range(terms):
             src = "0" if (st == 0 and tm == 0) else acc
             e(q(f"v_mfma_f32_32x32x64_f8f6f4 {acc}, {T[gs % 3]}, %[q{terms * st + tm}], {src}"))
+            if gs < ROW_STEPS:
+                for op in rops[:rper]:
+                    e(q(op))
+                rops = rops[rper:]
             if half == 1:
                 if gs == 9 and tm == 0:
                     e(q("s_nop 15"))      # XDL result -> VALU read of the half-0 scores
@@ -193,15 +247,16 @@ def both_halves(terms, p8):
                     if k < len(ops):
                         e(q(ops[k]))
                         k += 1
-        if half == 0:
-            # load st: row bytes 64 st on; the offset also moves the LDS
+        for _ in range(load_at.get(gs, 0)):
+            # load ld: row bytes 64 ld on; the offset also moves the LDS
             # destination, so M0 steps by 2048 - 64
-            e(q("global_load_lds_dwordx4 %[row], off" + (f" offset:{64 * st}" if st else "")))
-            if st < 8:
+            e(q("global_load_lds_dwordx4 v[230:231], off" + (f" offset:{64 * ld}" if ld else "")))
+            if ld < 8:
                 e(q(f"s_add_u32 m0, m0, {STEP - 64}"))
+            ld += 1
         if gs + 2 < 18:
             reads(gs + 2)
-    assert k == len(ops)
+    assert k == len(ops) and ld == 9 and not rops
     e(q("s_mov_b32 m0, %[m0s]"))
     e(q("s_nop 15"))
     e(q("s_nop 3"))
@@ -237,22 +292,27 @@ def function(kind, split, p8=False):
         clob_regs = [222] + list(range(224, 256))
     else:   # qk01
         name, ret = f"qk01_{qname}_{'p8' if p8 else 'p16'}", "void"
-        parts = base + ["const uint8_t *row", "uint32_t dst", "float sc2", f"Half0<{'true' if p8 else 'false'}> &o"]
+        parts = base + ["const NextRow &nr", "uint32_t dst", "float sc2", f"Half0<{'true' if p8 else 'false'}> &o"]
         outs = ['[s1] "=&v"(o.s1)', '[ms0] "=&v"(o.ms0)', '[sf] "+v"(o.sf0)']
         outs += [f'[hi{g}] "=&v"(o.hi[{g}])' for g in range(4)]
         if not p8:
             outs += [f'[lo{g}] "=&v"(o.lo[{g}])' for g in range(4)]
-        outs.append('[m0s] "=&s"(saved)')
-        ins += ['[row] "v"(row)', '[dst] "s"(dst)', '[sc2] "v"(sc2)']
+        outs += ['[m0s] "=&s"(saved)', '[inm] "=&s"(inm)', '[badm] "=&s"(o.badm)']
+        ins += ['[page] "v"(nr.page)', '[ts] "s"(nr.ts)', '[lmax] "s"(nr.lmax)', '[mask] "s"(nr.mask)',
+                '[shift] "s"(nr.shift)', '[np] "s"(nr.np)', '[pool] "s"(nr.pool)', '[zero] "s"(nr.zero)',
+                '[dst] "s"(dst)', '[sc2] "v"(sc2)']
         body = both_halves(terms, p8)
         clob_regs = list(range(S0, S0 + 16)) + [222] + list(range(224, 256))
         flags.append('"scc"')
+        flags.append('"vcc"')
     clob = [f'"v{r}"' for r in clob_regs] + flags
     s = signature(f"__device__ inline {ret} {name}(", parts)
     if ret == "floatx16":
         s += "  floatx16 acc;\n"
     if kind in ("scores_dma", "qk01"):
         s += "  uint32_t saved;\n"
+    if kind == "qk01":
+        s += "  uint64_t inm;\n"
     s += "  asm volatile(\n" + "\n".join("      " + l for l in body) + "\n"
     s += "      : " + wrap(outs) + "\n"
     s += "      : " + wrap(ins) + "\n"

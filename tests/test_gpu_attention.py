@@ -188,6 +188,40 @@ def test_all_ranks_but_one_empty():
     _check_all(w, grp, _all_rows(w), ranks=[0], tag="rank 0 only")
 
 
+@pytest.mark.parametrize("where,bad_page", [("interior", 1 << 30), ("interior", -5), ("last", 1 << 30)])
+def test_page_outside_pool(where, bad_page):
+    # a page id of a sequence's longest verify row points outside the pool:
+    # its tokens read as the zero row (no read outside the pool), the kernel
+    # raises the page-range bit, and no other sequence's output or LSE moves
+    # (the rows of one sequence share the tiles that row's table loads).  An
+    # interior page sits in a stage the one-block score phase loads; the last
+    # page in the row's last stage.
+    from decode_context_parallelism_amd import _lib, ops
+    w = make_config(2)
+    grp, _ = run_group(w)
+    r = 0
+    meta = grp.meta[r]
+    P = ops.subpage_size(w.block_size)
+    lens = meta.row_local_len.cpu().numpy()
+    row = int(np.argmax(lens))
+    npg = (int(lens[row]) + P - 1) // P
+    assert npg >= 8
+    idx = npg // 2 if where == "interior" else npg - 1
+    out0, lse0 = grp.out_ranks[r].clone(), grp.lse_ranks[r].clone()
+    assert int(meta.err.item()) == 0
+    b = row // w.qlen
+    meta.page_table[b * w.qlen:(b + 1) * w.qlen, idx] = bad_page   # whichever row's table loads
+    grp.rank_attention_split(r, w.kv_scale, w.softmax_scale)
+    torch.cuda.synchronize()
+    assert int(meta.err.item()) & _lib.ERR_PAGE_RANGE
+    out1, lse1 = grp.out_ranks[r], grp.lse_ranks[r]
+    assert torch.isfinite(out1[b].float()).all() and torch.isfinite(lse1[b]).all()
+    keep = torch.ones(w.batch, dtype=torch.bool, device=out1.device)
+    keep[b] = False
+    assert torch.equal(out1[keep], out0[keep])
+    assert torch.equal(lse1[keep], lse0[keep])
+
+
 @pytest.mark.parametrize("k", [1, 2, 4])
 def test_negative_control_boundary(k):
     # "[ROCm][MLA][DCP] Support causal multi-token verification", "Validation":

@@ -587,10 +587,10 @@ template <> struct POp<true> { int8v hi; };
 // half-0 ceiling ms0 (-2^30 when the row sees nothing in that half), the
 // probabilities of groups 0..3 (registers 0..3 of the P operand) and their
 // fp32 sum; the one-block form also the lanes whose next-tile page was
-// outside the pool (badm).
+// outside the pool (badm) and this lane's page id of the unit after next.
 template <bool P8> struct Half0;
-template <> struct Half0<false> { floatx16 s1; float ms0, sf0; int hi[4], lo[4]; uint64_t badm; };
-template <> struct Half0<true> { floatx16 s1; float ms0, sf0; int hi[4]; uint64_t badm; };
+template <> struct Half0<false> { floatx16 s1; float ms0, sf0; int hi[4], lo[4]; uint64_t badm; int32_t pnext; };
+template <> struct Half0<true> { floatx16 s1; float ms0, sf0; int hi[4]; uint64_t badm; int32_t pnext; };
 
 // The one-block score phase computes the next tile's row addresses itself
 // (the same token, page and zero-row rules as stage_row), while its first
@@ -603,6 +603,8 @@ struct NextRow {
   int lmax, mask, shift;   // the unit's row length; page size - 1 and its log2
   int np;                  // pages in the pool, at most 2^31 - 1
   const uint8_t *pool, *zero;
+  int ts2, lmax2;          // the unit after next: as ts and lmax
+  const int32_t *pt2;      // and its page-table row
 };
 
 // The scores of tile half 1, with the half-0 softmax between the products:
@@ -1251,37 +1253,44 @@ __device__ inline void qk01_split_p16(KAddr ka, const QOp<false> &q, const Rope 
       "v_lshrrev_b32 v225, 1, v224\n\t"
       "v_and_b32 v225, 8, v225\n\t"
       "v_and_b32 v226, 15, v224\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q1], v[206:221]\n\t"
       "v_xor_b32 v225, v225, v226\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q1], v[206:221]\n\t"
       "v_lshrrev_b32 v226, 1, v225\n\t"
       "v_xor_b32 v226, v226, v225\n\t"
       "v_and_b32 v226, 4, v226\n\t"
       "v_mul_u32_u24 v226, 3, v226\n\t"
+      "v_xor_b32 v225, v225, v226\n\t"
+      "v_add_u32 v226, %[ts2], v225\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q2], v[206:221]\n\t"
-      "v_xor_b32 v225, v225, v226\n\t"
+      "v_cmp_gt_i32 vcc, %[lmax2], v226\n\t"
+      "v_lshrrev_b32 v226, %[shift], v226\n\t"
+      "v_cndmask_b32 v226, 0, v226, vcc\n\t"
+      "v_mov_b32 v227, 0\n\t"
+      "v_lshl_add_u64 v[228:229], v[226:227], 2, %[pt2]\n\t"
+      "global_load_dword %[pnext], v[228:229], off\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q3], v[206:221]\n\t"
       "v_add_u32 v225, %[ts], v225\n\t"
       "v_cmp_gt_i32 %[inm], %[lmax], v225\n\t"
       "v_and_b32 v226, %[mask], v225\n\t"
       "v_lshl_add_u32 v227, %[page], %[shift], v226\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q3], v[206:221]\n\t"
       "v_and_b32 v224, 0x30, v224\n\t"
       "v_mov_b32 v225, 0\n\t"
-      "v_lshl_add_u64 v[228:229], v[224:225], 0, %[pool]\n\t"
-      "v_mov_b32 v226, 0x240\n\t"
-      "v_mad_u64_u32 v[230:231], vcc, v227, v226, v[228:229]\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q4], v[206:221]\n\t"
+      "v_lshl_add_u64 v[228:229], v[224:225], 0, %[pool]\n\t"
+      "v_mov_b32 v226, 0x240\n\t"
+      "v_mad_u64_u32 v[230:231], vcc, v227, v226, v[228:229]\n\t"
       "v_lshl_add_u64 v[228:229], v[224:225], 0, %[zero]\n\t"
       "v_cmp_gt_u32 vcc, %[np], %[page]\n\t"
       "s_andn2_b64 %[badm], %[inm], vcc\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q5], v[206:221]\n\t"
       "s_and_b64 vcc, %[inm], vcc\n\t"
       "v_cndmask_b32 v230, v228, v230, vcc\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q5], v[206:221]\n\t"
       "v_cndmask_b32 v231, v229, v231, vcc\n\t"
       "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
       "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
@@ -1484,17 +1493,20 @@ __device__ inline void qk01_split_p16(KAddr ka, const QOp<false> &q, const Rope 
       "v_cvt_pk_bf8_f32 %[lo3], v230, v231 op_sel:[0,0,1]\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q17], %[s1]\n\t"
       "s_mov_b32 m0, %[m0s]\n\t"
+      "s_waitcnt vmcnt(9)\n\t"
       "s_nop 15\n\t"
       "s_nop 3\n\t"
       : [s1] "=&v"(o.s1), [ms0] "=&v"(o.ms0), [sf] "+v"(o.sf0), [hi0] "=&v"(o.hi[0]), [hi1] "=&v"(o.hi[1]),
         [hi2] "=&v"(o.hi[2]), [hi3] "=&v"(o.hi[3]), [lo0] "=&v"(o.lo[0]), [lo1] "=&v"(o.lo[1]),
-        [lo2] "=&v"(o.lo[2]), [lo3] "=&v"(o.lo[3]), [m0s] "=&s"(saved), [inm] "=&s"(inm), [badm] "=&s"(o.badm)
+        [lo2] "=&v"(o.lo[2]), [lo3] "=&v"(o.lo[3]), [m0s] "=&s"(saved), [inm] "=&s"(inm), [badm] "=&s"(o.badm),
+        [pnext] "=&v"(o.pnext)
       : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
         [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
         [q8] "v"(q.v[8]), [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]),
         [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(rope.hi), [q17] "v"(rope.lo),
         [page] "v"(nr.page), [ts] "s"(nr.ts), [lmax] "s"(nr.lmax), [mask] "s"(nr.mask), [shift] "s"(nr.shift),
-        [np] "s"(nr.np), [pool] "s"(nr.pool), [zero] "s"(nr.zero), [dst] "s"(dst), [sc2] "v"(sc2)
+        [np] "s"(nr.np), [pool] "s"(nr.pool), [zero] "s"(nr.zero), [ts2] "s"(nr.ts2), [lmax2] "s"(nr.lmax2),
+        [pt2] "s"(nr.pt2), [dst] "s"(dst), [sc2] "v"(sc2)
       : "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218",
         "v219", "v220", "v221", "v222", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232",
         "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245",
@@ -1520,37 +1532,44 @@ __device__ inline void qk01_split_p8(KAddr ka, const QOp<false> &q, const Rope &
       "v_lshrrev_b32 v225, 1, v224\n\t"
       "v_and_b32 v225, 8, v225\n\t"
       "v_and_b32 v226, 15, v224\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q1], v[206:221]\n\t"
       "v_xor_b32 v225, v225, v226\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[240:247], %[q1], v[206:221]\n\t"
       "v_lshrrev_b32 v226, 1, v225\n\t"
       "v_xor_b32 v226, v226, v225\n\t"
       "v_and_b32 v226, 4, v226\n\t"
       "v_mul_u32_u24 v226, 3, v226\n\t"
+      "v_xor_b32 v225, v225, v226\n\t"
+      "v_add_u32 v226, %[ts2], v225\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q2], v[206:221]\n\t"
-      "v_xor_b32 v225, v225, v226\n\t"
+      "v_cmp_gt_i32 vcc, %[lmax2], v226\n\t"
+      "v_lshrrev_b32 v226, %[shift], v226\n\t"
+      "v_cndmask_b32 v226, 0, v226, vcc\n\t"
+      "v_mov_b32 v227, 0\n\t"
+      "v_lshl_add_u64 v[228:229], v[226:227], 2, %[pt2]\n\t"
+      "global_load_dword %[pnext], v[228:229], off\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q3], v[206:221]\n\t"
       "v_add_u32 v225, %[ts], v225\n\t"
       "v_cmp_gt_i32 %[inm], %[lmax], v225\n\t"
       "v_and_b32 v226, %[mask], v225\n\t"
       "v_lshl_add_u32 v227, %[page], %[shift], v226\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q3], v[206:221]\n\t"
       "v_and_b32 v224, 0x30, v224\n\t"
       "v_mov_b32 v225, 0\n\t"
-      "v_lshl_add_u64 v[228:229], v[224:225], 0, %[pool]\n\t"
-      "v_mov_b32 v226, 0x240\n\t"
-      "v_mad_u64_u32 v[230:231], vcc, v227, v226, v[228:229]\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q4], v[206:221]\n\t"
+      "v_lshl_add_u64 v[228:229], v[224:225], 0, %[pool]\n\t"
+      "v_mov_b32 v226, 0x240\n\t"
+      "v_mad_u64_u32 v[230:231], vcc, v227, v226, v[228:229]\n\t"
       "v_lshl_add_u64 v[228:229], v[224:225], 0, %[zero]\n\t"
       "v_cmp_gt_u32 vcc, %[np], %[page]\n\t"
       "s_andn2_b64 %[badm], %[inm], vcc\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q5], v[206:221]\n\t"
       "s_and_b64 vcc, %[inm], vcc\n\t"
       "v_cndmask_b32 v230, v228, v230, vcc\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q5], v[206:221]\n\t"
       "v_cndmask_b32 v231, v229, v231, vcc\n\t"
       "ds_read_b128 v[248:251], %[a0] offset:8192\n\t"
       "ds_read_b128 v[252:255], %[a1] offset:8192\n\t"
@@ -1721,16 +1740,19 @@ __device__ inline void qk01_split_p8(KAddr ka, const QOp<false> &q, const Rope &
       "v_add_f32 %[sf], %[sf], v228\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q17], %[s1]\n\t"
       "s_mov_b32 m0, %[m0s]\n\t"
+      "s_waitcnt vmcnt(9)\n\t"
       "s_nop 15\n\t"
       "s_nop 3\n\t"
       : [s1] "=&v"(o.s1), [ms0] "=&v"(o.ms0), [sf] "+v"(o.sf0), [hi0] "=&v"(o.hi[0]), [hi1] "=&v"(o.hi[1]),
-        [hi2] "=&v"(o.hi[2]), [hi3] "=&v"(o.hi[3]), [m0s] "=&s"(saved), [inm] "=&s"(inm), [badm] "=&s"(o.badm)
+        [hi2] "=&v"(o.hi[2]), [hi3] "=&v"(o.hi[3]), [m0s] "=&s"(saved), [inm] "=&s"(inm), [badm] "=&s"(o.badm),
+        [pnext] "=&v"(o.pnext)
       : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
         [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
         [q8] "v"(q.v[8]), [q9] "v"(q.v[9]), [q10] "v"(q.v[10]), [q11] "v"(q.v[11]), [q12] "v"(q.v[12]),
         [q13] "v"(q.v[13]), [q14] "v"(q.v[14]), [q15] "v"(q.v[15]), [q16] "v"(rope.hi), [q17] "v"(rope.lo),
         [page] "v"(nr.page), [ts] "s"(nr.ts), [lmax] "s"(nr.lmax), [mask] "s"(nr.mask), [shift] "s"(nr.shift),
-        [np] "s"(nr.np), [pool] "s"(nr.pool), [zero] "s"(nr.zero), [dst] "s"(dst), [sc2] "v"(sc2)
+        [np] "s"(nr.np), [pool] "s"(nr.pool), [zero] "s"(nr.zero), [ts2] "s"(nr.ts2), [lmax2] "s"(nr.lmax2),
+        [pt2] "s"(nr.pt2), [dst] "s"(dst), [sc2] "v"(sc2)
       : "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218",
         "v219", "v220", "v221", "v222", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232",
         "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245",
@@ -1760,23 +1782,30 @@ __device__ inline void qk01_fp8q_p16(KAddr ka, const QOp<true> &q, const NextRow
       "v_lshrrev_b32 v226, 1, v225\n\t"
       "v_xor_b32 v226, v226, v225\n\t"
       "v_and_b32 v226, 4, v226\n\t"
+      "v_mul_u32_u24 v226, 3, v226\n\t"
+      "v_xor_b32 v225, v225, v226\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q1], v[206:221]\n\t"
-      "v_mul_u32_u24 v226, 3, v226\n\t"
-      "v_xor_b32 v225, v225, v226\n\t"
+      "v_add_u32 v226, %[ts2], v225\n\t"
+      "v_cmp_gt_i32 vcc, %[lmax2], v226\n\t"
+      "v_lshrrev_b32 v226, %[shift], v226\n\t"
+      "v_cndmask_b32 v226, 0, v226, vcc\n\t"
+      "v_mov_b32 v227, 0\n\t"
+      "v_lshl_add_u64 v[228:229], v[226:227], 2, %[pt2]\n\t"
+      "global_load_dword %[pnext], v[228:229], off\n\t"
       "v_add_u32 v225, %[ts], v225\n\t"
       "v_cmp_gt_i32 %[inm], %[lmax], v225\n\t"
       "v_and_b32 v226, %[mask], v225\n\t"
       "v_lshl_add_u32 v227, %[page], %[shift], v226\n\t"
-      "v_and_b32 v224, 0x30, v224\n\t"
-      "v_mov_b32 v225, 0\n\t"
-      "v_lshl_add_u64 v[228:229], v[224:225], 0, %[pool]\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q2], v[206:221]\n\t"
+      "v_and_b32 v224, 0x30, v224\n\t"
+      "v_mov_b32 v225, 0\n\t"
+      "v_lshl_add_u64 v[228:229], v[224:225], 0, %[pool]\n\t"
       "v_mov_b32 v226, 0x240\n\t"
       "v_mad_u64_u32 v[230:231], vcc, v227, v226, v[228:229]\n\t"
       "v_lshl_add_u64 v[228:229], v[224:225], 0, %[zero]\n\t"
@@ -1971,16 +2000,18 @@ __device__ inline void qk01_fp8q_p16(KAddr ka, const QOp<true> &q, const NextRow
       "v_cvt_pk_bf8_f32 %[lo3], v228, v229\n\t"
       "v_cvt_pk_bf8_f32 %[lo3], v230, v231 op_sel:[0,0,1]\n\t"
       "s_mov_b32 m0, %[m0s]\n\t"
+      "s_waitcnt vmcnt(9)\n\t"
       "s_nop 15\n\t"
       "s_nop 3\n\t"
       : [s1] "=&v"(o.s1), [ms0] "=&v"(o.ms0), [sf] "+v"(o.sf0), [hi0] "=&v"(o.hi[0]), [hi1] "=&v"(o.hi[1]),
         [hi2] "=&v"(o.hi[2]), [hi3] "=&v"(o.hi[3]), [lo0] "=&v"(o.lo[0]), [lo1] "=&v"(o.lo[1]),
-        [lo2] "=&v"(o.lo[2]), [lo3] "=&v"(o.lo[3]), [m0s] "=&s"(saved), [inm] "=&s"(inm), [badm] "=&s"(o.badm)
+        [lo2] "=&v"(o.lo[2]), [lo3] "=&v"(o.lo[3]), [m0s] "=&s"(saved), [inm] "=&s"(inm), [badm] "=&s"(o.badm),
+        [pnext] "=&v"(o.pnext)
       : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
         [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
         [q8] "v"(q.v[8]), [page] "v"(nr.page), [ts] "s"(nr.ts), [lmax] "s"(nr.lmax), [mask] "s"(nr.mask),
-        [shift] "s"(nr.shift), [np] "s"(nr.np), [pool] "s"(nr.pool), [zero] "s"(nr.zero), [dst] "s"(dst),
-        [sc2] "v"(sc2)
+        [shift] "s"(nr.shift), [np] "s"(nr.np), [pool] "s"(nr.pool), [zero] "s"(nr.zero), [ts2] "s"(nr.ts2),
+        [lmax2] "s"(nr.lmax2), [pt2] "s"(nr.pt2), [dst] "s"(dst), [sc2] "v"(sc2)
       : "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218",
         "v219", "v220", "v221", "v222", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232",
         "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245",
@@ -2010,23 +2041,30 @@ __device__ inline void qk01_fp8q_p8(KAddr ka, const QOp<true> &q, const NextRow 
       "v_lshrrev_b32 v226, 1, v225\n\t"
       "v_xor_b32 v226, v226, v225\n\t"
       "v_and_b32 v226, 4, v226\n\t"
+      "v_mul_u32_u24 v226, 3, v226\n\t"
+      "v_xor_b32 v225, v225, v226\n\t"
       "ds_read_b128 v[232:235], %[a0] offset:4096\n\t"
       "ds_read_b128 v[236:239], %[a1] offset:4096\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[248:255], %[q1], v[206:221]\n\t"
-      "v_mul_u32_u24 v226, 3, v226\n\t"
-      "v_xor_b32 v225, v225, v226\n\t"
+      "v_add_u32 v226, %[ts2], v225\n\t"
+      "v_cmp_gt_i32 vcc, %[lmax2], v226\n\t"
+      "v_lshrrev_b32 v226, %[shift], v226\n\t"
+      "v_cndmask_b32 v226, 0, v226, vcc\n\t"
+      "v_mov_b32 v227, 0\n\t"
+      "v_lshl_add_u64 v[228:229], v[226:227], 2, %[pt2]\n\t"
+      "global_load_dword %[pnext], v[228:229], off\n\t"
       "v_add_u32 v225, %[ts], v225\n\t"
       "v_cmp_gt_i32 %[inm], %[lmax], v225\n\t"
       "v_and_b32 v226, %[mask], v225\n\t"
       "v_lshl_add_u32 v227, %[page], %[shift], v226\n\t"
-      "v_and_b32 v224, 0x30, v224\n\t"
-      "v_mov_b32 v225, 0\n\t"
-      "v_lshl_add_u64 v[228:229], v[224:225], 0, %[pool]\n\t"
       "ds_read_b128 v[240:243], %[a0] offset:6144\n\t"
       "ds_read_b128 v[244:247], %[a1] offset:6144\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
       "v_mfma_f32_32x32x64_f8f6f4 v[206:221], v[232:239], %[q2], v[206:221]\n\t"
+      "v_and_b32 v224, 0x30, v224\n\t"
+      "v_mov_b32 v225, 0\n\t"
+      "v_lshl_add_u64 v[228:229], v[224:225], 0, %[pool]\n\t"
       "v_mov_b32 v226, 0x240\n\t"
       "v_mad_u64_u32 v[230:231], vcc, v227, v226, v[228:229]\n\t"
       "v_lshl_add_u64 v[228:229], v[224:225], 0, %[zero]\n\t"
@@ -2189,15 +2227,17 @@ __device__ inline void qk01_fp8q_p8(KAddr ka, const QOp<true> &q, const NextRow 
       "v_add_f32 v228, v228, v229\n\t"
       "v_add_f32 %[sf], %[sf], v228\n\t"
       "s_mov_b32 m0, %[m0s]\n\t"
+      "s_waitcnt vmcnt(9)\n\t"
       "s_nop 15\n\t"
       "s_nop 3\n\t"
       : [s1] "=&v"(o.s1), [ms0] "=&v"(o.ms0), [sf] "+v"(o.sf0), [hi0] "=&v"(o.hi[0]), [hi1] "=&v"(o.hi[1]),
-        [hi2] "=&v"(o.hi[2]), [hi3] "=&v"(o.hi[3]), [m0s] "=&s"(saved), [inm] "=&s"(inm), [badm] "=&s"(o.badm)
+        [hi2] "=&v"(o.hi[2]), [hi3] "=&v"(o.hi[3]), [m0s] "=&s"(saved), [inm] "=&s"(inm), [badm] "=&s"(o.badm),
+        [pnext] "=&v"(o.pnext)
       : [a0] "v"(ka.a0), [a1] "v"(ka.a1), [q0] "v"(q.v[0]), [q1] "v"(q.v[1]), [q2] "v"(q.v[2]),
         [q3] "v"(q.v[3]), [q4] "v"(q.v[4]), [q5] "v"(q.v[5]), [q6] "v"(q.v[6]), [q7] "v"(q.v[7]),
         [q8] "v"(q.v[8]), [page] "v"(nr.page), [ts] "s"(nr.ts), [lmax] "s"(nr.lmax), [mask] "s"(nr.mask),
-        [shift] "s"(nr.shift), [np] "s"(nr.np), [pool] "s"(nr.pool), [zero] "s"(nr.zero), [dst] "s"(dst),
-        [sc2] "v"(sc2)
+        [shift] "s"(nr.shift), [np] "s"(nr.np), [pool] "s"(nr.pool), [zero] "s"(nr.zero), [ts2] "s"(nr.ts2),
+        [lmax2] "s"(nr.lmax2), [pt2] "s"(nr.pt2), [dst] "s"(dst), [sc2] "v"(sc2)
       : "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218",
         "v219", "v220", "v221", "v222", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232",
         "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245",
@@ -2232,6 +2272,514 @@ __device__ inline void qk01(KAddr ka, const QOp<QF8> &q, const Rope &rope, const
 // live across the next stage's score products, where the split query, the
 // scores and the read-ahead tuples already fill the register file.  Chunk c
 // (16 bytes of every lane) sits at 1024 c + 16 lane.
+// What the p.v block hands back: the half-1 probabilities (groups 4..7) and
+// their fp32 sum, the half-1 ceiling ms1, max(ms0, ms1), the updated row
+// reference mref, the halves' offsets above it (delta = the larger) and
+// their clamped E8M0 exponents.
+template <bool P8> struct PvOut;
+template <> struct PvOut<false> { int hi[4], lo[4]; float sf1, ms1, msx, delta, mref; int di0, di1; };
+template <> struct PvOut<true> { int hi[4]; float sf1, ms1, msx, delta, mref; int di0, di1; };
+
+// The pending stage's p.v as one asm block on one-block stages (written by
+// gen_score_blocks.py): the 16 value blocks' products (V^T read transposed
+// two blocks ahead, P^T from the wave's staging area, E8M0 scale epo), with
+// the half-1 softmax and the reference logic of this stage between them.
+__device__ inline void pv_p16(floatx16 (&o)[16], const floatx16 &s1, float ms0, float sc2, int epo,
+                              uint32_t pab, uint32_t vtb, PvOut<false> &r) {
+  uint32_t pa, va;
+  asm volatile(
+      "v_mbcnt_lo_u32_b32 v224, -1, 0\n\t"
+      "v_mbcnt_hi_u32_b32 v224, -1, v224\n\t"
+      "v_lshl_add_u32 %[pa], v224, 4, %[pab]\n\t"
+      "v_lshlrev_b32 %[va], 3, v224\n\t"
+      "v_and_b32 %[va], 0x78, %[va]\n\t"
+      "v_bfe_u32 v225, v224, 4, 1\n\t"
+      "v_lshl_or_b32 %[va], v225, 8, %[va]\n\t"
+      "v_bfe_u32 v226, v224, 5, 1\n\t"
+      "v_xor_b32 v225, v225, v226\n\t"
+      "v_lshl_or_b32 %[va], v225, 7, %[va]\n\t"
+      "v_add_u32 %[va], %[vtb], %[va]\n\t"
+      "ds_read_b128 v[206:209], %[pa]\n\t"
+      "ds_read_b128 v[210:213], %[pa] offset:1024\n\t"
+      "ds_read_b128 v[214:217], %[pa] offset:2048\n\t"
+      "ds_read_b128 v[218:221], %[pa] offset:3072\n\t"
+      "ds_read_b64_tr_b8 v[232:233], %[va]\n\t"
+      "ds_read_b64_tr_b8 v[234:235], %[va] offset:1024\n\t"
+      "ds_read_b64_tr_b8 v[236:237], %[va] offset:18432\n\t"
+      "ds_read_b64_tr_b8 v[238:239], %[va] offset:19456\n\t"
+      "ds_read_b64_tr_b8 v[240:241], %[va] offset:512\n\t"
+      "ds_read_b64_tr_b8 v[242:243], %[va] offset:1536\n\t"
+      "ds_read_b64_tr_b8 v[244:245], %[va] offset:18944\n\t"
+      "ds_read_b64_tr_b8 v[246:247], %[va] offset:19968\n\t"
+      "v_max3_f32 v224, %[s0], %[s1], %[s2]\n\t"
+      "v_max3_f32 v225, %[s3], %[s4], %[s5]\n\t"
+      "v_max3_f32 v226, %[s6], %[s7], %[s8]\n\t"
+      "v_max3_f32 v227, %[s9], %[s10], %[s11]\n\t"
+      "v_max3_f32 v228, %[s12], %[s13], %[s14]\n\t"
+      "v_max3_f32 v224, v224, v225, v226\n\t"
+      "v_max3_f32 v227, v227, v228, %[s15]\n\t"
+      "v_max_f32 v224, v224, v227\n\t"
+      "v_mov_b32 v225, v224\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 v224, v225\n\t"
+      "v_max_f32 v224, v224, v225\n\t"
+      "v_mul_f32 v224, v224, %[sc2]\n\t"
+      "v_ceil_f32 v224, v224\n\t"
+      "v_max_f32 %[ms1], 0xce800000, v224\n\t"
+      "v_sub_f32 v222, 0x41000000, %[ms1]\n\t"
+      "v_max_f32 %[msx], %[ms0], %[ms1]\n\t"
+      "v_cmp_lt_f32 vcc, 0xce800000, %[msx]\n\t"
+      "v_mov_b32 v225, 0xff800000\n\t"
+      "v_cndmask_b32 v225, v225, %[msx], vcc\n\t"
+      "v_cmp_lt_f32 vcc, 0xff800000, %[mref]\n\t"
+      "v_cndmask_b32 %[mref], v225, %[mref], vcc\n\t"
+      "v_cmp_lt_f32 vcc, 0xff800000, %[mref]\n\t"
+      "v_sub_f32 v226, %[ms0], %[mref]\n\t"
+      "v_cndmask_b32 v226, 0, v226, vcc\n\t"
+      "v_sub_f32 v227, %[ms1], %[mref]\n\t"
+      "v_cndmask_b32 v227, 0, v227, vcc\n\t"
+      "v_max_f32 %[delta], v226, v227\n\t"
+      "v_min_f32 v226, 0x42800000, v226\n\t"
+      "v_min_f32 v227, 0x42800000, v227\n\t"
+      "v_max_f32 v226, 0xc2fe0000, v226\n\t"
+      "v_max_f32 v227, 0xc2fe0000, v227\n\t"
+      "v_cvt_i32_f32 %[di0], v226\n\t"
+      "v_cvt_i32_f32 %[di1], v227\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o0], v[232:239], v[206:213], %[o0], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_fma_f32 v224, %[s0], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s1], %[sc2], v222\n\t"
+      "v_fma_f32 v226, %[s2], %[sc2], v222\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o0], v[232:239], v[214:221], %[o0], %[one], %[epo] op_sel_hi:[0,0,0] blgp:1\n\t"
+      "v_fma_f32 v227, %[s3], %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "ds_read_b64_tr_b8 v[248:249], %[va] offset:2048\n\t"
+      "ds_read_b64_tr_b8 v[250:251], %[va] offset:3072\n\t"
+      "ds_read_b64_tr_b8 v[252:253], %[va] offset:20480\n\t"
+      "ds_read_b64_tr_b8 v[254:255], %[va] offset:21504\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o1], v[240:247], v[206:213], %[o1], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o1], v[240:247], v[214:221], %[o1], %[one], %[epo] op_sel_hi:[0,0,0] blgp:1\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi4], v224, v225\n\t"
+      "ds_read_b64_tr_b8 v[232:233], %[va] offset:2560\n\t"
+      "ds_read_b64_tr_b8 v[234:235], %[va] offset:3584\n\t"
+      "ds_read_b64_tr_b8 v[236:237], %[va] offset:20992\n\t"
+      "ds_read_b64_tr_b8 v[238:239], %[va] offset:22016\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o2], v[248:255], v[206:213], %[o2], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_cvt_pk_fp8_f32 %[hi4], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf1], %[sf1], v228\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o2], v[248:255], v[214:221], %[o2], %[one], %[epo] op_sel_hi:[0,0,0] blgp:1\n\t"
+      "v_cvt_pk_f32_fp8 v[228:229], %[hi4]\n\t"
+      "v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi4] src0_sel:WORD_1\n\t"
+      "v_sub_f32 v228, v224, v228\n\t"
+      "ds_read_b64_tr_b8 v[240:241], %[va] offset:4096\n\t"
+      "ds_read_b64_tr_b8 v[242:243], %[va] offset:5120\n\t"
+      "ds_read_b64_tr_b8 v[244:245], %[va] offset:22528\n\t"
+      "ds_read_b64_tr_b8 v[246:247], %[va] offset:23552\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o3], v[232:239], v[206:213], %[o3], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_sub_f32 v229, v225, v229\n\t"
+      "v_sub_f32 v230, v226, v230\n\t"
+      "v_sub_f32 v231, v227, v231\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o3], v[232:239], v[214:221], %[o3], %[one], %[epo] op_sel_hi:[0,0,0] blgp:1\n\t"
+      "v_cvt_pk_bf8_f32 %[lo4], v228, v229\n\t"
+      "v_cvt_pk_bf8_f32 %[lo4], v230, v231 op_sel:[0,0,1]\n\t"
+      "v_fma_f32 v224, %[s4], %[sc2], v222\n\t"
+      "ds_read_b64_tr_b8 v[248:249], %[va] offset:4608\n\t"
+      "ds_read_b64_tr_b8 v[250:251], %[va] offset:5632\n\t"
+      "ds_read_b64_tr_b8 v[252:253], %[va] offset:23040\n\t"
+      "ds_read_b64_tr_b8 v[254:255], %[va] offset:24064\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o4], v[240:247], v[206:213], %[o4], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_fma_f32 v225, %[s5], %[sc2], v222\n\t"
+      "v_fma_f32 v226, %[s6], %[sc2], v222\n\t"
+      "v_fma_f32 v227, %[s7], %[sc2], v222\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o4], v[240:247], v[214:221], %[o4], %[one], %[epo] op_sel_hi:[0,0,0] blgp:1\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "ds_read_b64_tr_b8 v[232:233], %[va] offset:6144\n\t"
+      "ds_read_b64_tr_b8 v[234:235], %[va] offset:7168\n\t"
+      "ds_read_b64_tr_b8 v[236:237], %[va] offset:24576\n\t"
+      "ds_read_b64_tr_b8 v[238:239], %[va] offset:25600\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o5], v[248:255], v[206:213], %[o5], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o5], v[248:255], v[214:221], %[o5], %[one], %[epo] op_sel_hi:[0,0,0] blgp:1\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi5], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi5], v226, v227 op_sel:[0,0,1]\n\t"
+      "ds_read_b64_tr_b8 v[240:241], %[va] offset:6656\n\t"
+      "ds_read_b64_tr_b8 v[242:243], %[va] offset:7680\n\t"
+      "ds_read_b64_tr_b8 v[244:245], %[va] offset:25088\n\t"
+      "ds_read_b64_tr_b8 v[246:247], %[va] offset:26112\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o6], v[232:239], v[206:213], %[o6], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf1], %[sf1], v228\n\t"
+      "v_cvt_pk_f32_fp8 v[228:229], %[hi5]\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o6], v[232:239], v[214:221], %[o6], %[one], %[epo] op_sel_hi:[0,0,0] blgp:1\n\t"
+      "v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi5] src0_sel:WORD_1\n\t"
+      "v_sub_f32 v228, v224, v228\n\t"
+      "v_sub_f32 v229, v225, v229\n\t"
+      "ds_read_b64_tr_b8 v[248:249], %[va] offset:8192\n\t"
+      "ds_read_b64_tr_b8 v[250:251], %[va] offset:9216\n\t"
+      "ds_read_b64_tr_b8 v[252:253], %[va] offset:26624\n\t"
+      "ds_read_b64_tr_b8 v[254:255], %[va] offset:27648\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o7], v[240:247], v[206:213], %[o7], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_sub_f32 v230, v226, v230\n\t"
+      "v_sub_f32 v231, v227, v231\n\t"
+      "v_cvt_pk_bf8_f32 %[lo5], v228, v229\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o7], v[240:247], v[214:221], %[o7], %[one], %[epo] op_sel_hi:[0,0,0] blgp:1\n\t"
+      "v_cvt_pk_bf8_f32 %[lo5], v230, v231 op_sel:[0,0,1]\n\t"
+      "v_fma_f32 v224, %[s8], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s9], %[sc2], v222\n\t"
+      "ds_read_b64_tr_b8 v[232:233], %[va] offset:8704\n\t"
+      "ds_read_b64_tr_b8 v[234:235], %[va] offset:9728\n\t"
+      "ds_read_b64_tr_b8 v[236:237], %[va] offset:27136\n\t"
+      "ds_read_b64_tr_b8 v[238:239], %[va] offset:28160\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o8], v[248:255], v[206:213], %[o8], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_fma_f32 v226, %[s10], %[sc2], v222\n\t"
+      "v_fma_f32 v227, %[s11], %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o8], v[248:255], v[214:221], %[o8], %[one], %[epo] op_sel_hi:[0,0,0] blgp:1\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "ds_read_b64_tr_b8 v[240:241], %[va] offset:10240\n\t"
+      "ds_read_b64_tr_b8 v[242:243], %[va] offset:11264\n\t"
+      "ds_read_b64_tr_b8 v[244:245], %[va] offset:28672\n\t"
+      "ds_read_b64_tr_b8 v[246:247], %[va] offset:29696\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o9], v[232:239], v[206:213], %[o9], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o9], v[232:239], v[214:221], %[o9], %[one], %[epo] op_sel_hi:[0,0,0] blgp:1\n\t"
+      "v_cvt_pk_fp8_f32 %[hi6], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi6], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "ds_read_b64_tr_b8 v[248:249], %[va] offset:10752\n\t"
+      "ds_read_b64_tr_b8 v[250:251], %[va] offset:11776\n\t"
+      "ds_read_b64_tr_b8 v[252:253], %[va] offset:29184\n\t"
+      "ds_read_b64_tr_b8 v[254:255], %[va] offset:30208\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o10], v[240:247], v[206:213], %[o10], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_add_f32 %[sf1], %[sf1], v228\n\t"
+      "v_cvt_pk_f32_fp8 v[228:229], %[hi6]\n\t"
+      "v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi6] src0_sel:WORD_1\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o10], v[240:247], v[214:221], %[o10], %[one], %[epo] op_sel_hi:[0,0,0] blgp:1\n\t"
+      "v_sub_f32 v228, v224, v228\n\t"
+      "v_sub_f32 v229, v225, v229\n\t"
+      "v_sub_f32 v230, v226, v230\n\t"
+      "ds_read_b64_tr_b8 v[232:233], %[va] offset:12288\n\t"
+      "ds_read_b64_tr_b8 v[234:235], %[va] offset:13312\n\t"
+      "ds_read_b64_tr_b8 v[236:237], %[va] offset:30720\n\t"
+      "ds_read_b64_tr_b8 v[238:239], %[va] offset:31744\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o11], v[248:255], v[206:213], %[o11], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_sub_f32 v231, v227, v231\n\t"
+      "v_cvt_pk_bf8_f32 %[lo6], v228, v229\n\t"
+      "v_cvt_pk_bf8_f32 %[lo6], v230, v231 op_sel:[0,0,1]\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o11], v[248:255], v[214:221], %[o11], %[one], %[epo] op_sel_hi:[0,0,0] blgp:1\n\t"
+      "v_fma_f32 v224, %[s12], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s13], %[sc2], v222\n\t"
+      "v_fma_f32 v226, %[s14], %[sc2], v222\n\t"
+      "ds_read_b64_tr_b8 v[240:241], %[va] offset:12800\n\t"
+      "ds_read_b64_tr_b8 v[242:243], %[va] offset:13824\n\t"
+      "ds_read_b64_tr_b8 v[244:245], %[va] offset:31232\n\t"
+      "ds_read_b64_tr_b8 v[246:247], %[va] offset:32256\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o12], v[232:239], v[206:213], %[o12], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_fma_f32 v227, %[s15], %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o12], v[232:239], v[214:221], %[o12], %[one], %[epo] op_sel_hi:[0,0,0] blgp:1\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "ds_read_b64_tr_b8 v[248:249], %[va] offset:14336\n\t"
+      "ds_read_b64_tr_b8 v[250:251], %[va] offset:15360\n\t"
+      "ds_read_b64_tr_b8 v[252:253], %[va] offset:32768\n\t"
+      "ds_read_b64_tr_b8 v[254:255], %[va] offset:33792\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o13], v[240:247], v[206:213], %[o13], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi7], v224, v225\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o13], v[240:247], v[214:221], %[o13], %[one], %[epo] op_sel_hi:[0,0,0] blgp:1\n\t"
+      "v_cvt_pk_fp8_f32 %[hi7], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf1], %[sf1], v228\n\t"
+      "ds_read_b64_tr_b8 v[232:233], %[va] offset:14848\n\t"
+      "ds_read_b64_tr_b8 v[234:235], %[va] offset:15872\n\t"
+      "ds_read_b64_tr_b8 v[236:237], %[va] offset:33280\n\t"
+      "ds_read_b64_tr_b8 v[238:239], %[va] offset:34304\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o14], v[248:255], v[206:213], %[o14], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_cvt_pk_f32_fp8 v[228:229], %[hi7]\n\t"
+      "v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi7] src0_sel:WORD_1\n\t"
+      "v_sub_f32 v228, v224, v228\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o14], v[248:255], v[214:221], %[o14], %[one], %[epo] op_sel_hi:[0,0,0] blgp:1\n\t"
+      "v_sub_f32 v229, v225, v229\n\t"
+      "v_sub_f32 v230, v226, v230\n\t"
+      "v_sub_f32 v231, v227, v231\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o15], v[232:239], v[206:213], %[o15], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_cvt_pk_bf8_f32 %[lo7], v228, v229\n\t"
+      "v_cvt_pk_bf8_f32 %[lo7], v230, v231 op_sel:[0,0,1]\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o15], v[232:239], v[214:221], %[o15], %[one], %[epo] op_sel_hi:[0,0,0] blgp:1\n\t"
+      : [o0] "+a"(o[0]), [o1] "+a"(o[1]), [o2] "+a"(o[2]), [o3] "+a"(o[3]), [o4] "+a"(o[4]), [o5] "+a"(o[5]),
+        [o6] "+a"(o[6]), [o7] "+a"(o[7]), [o8] "+a"(o[8]), [o9] "+a"(o[9]), [o10] "+a"(o[10]),
+        [o11] "+a"(o[11]), [o12] "+a"(o[12]), [o13] "+a"(o[13]), [o14] "+a"(o[14]), [o15] "+a"(o[15]),
+        [hi4] "=&v"(r.hi[0]), [hi5] "=&v"(r.hi[1]), [hi6] "=&v"(r.hi[2]), [hi7] "=&v"(r.hi[3]),
+        [lo4] "=&v"(r.lo[0]), [lo5] "=&v"(r.lo[1]), [lo6] "=&v"(r.lo[2]), [lo7] "=&v"(r.lo[3]),
+        [sf1] "+v"(r.sf1), [ms1] "=&v"(r.ms1), [msx] "=&v"(r.msx), [delta] "=&v"(r.delta), [di0] "=&v"(r.di0),
+        [di1] "=&v"(r.di1), [mref] "+v"(r.mref), [pa] "=&v"(pa), [va] "=&v"(va)
+      : [s0] "v"(s1[0]), [s1] "v"(s1[1]), [s2] "v"(s1[2]), [s3] "v"(s1[3]), [s4] "v"(s1[4]), [s5] "v"(s1[5]),
+        [s6] "v"(s1[6]), [s7] "v"(s1[7]), [s8] "v"(s1[8]), [s9] "v"(s1[9]), [s10] "v"(s1[10]),
+        [s11] "v"(s1[11]), [s12] "v"(s1[12]), [s13] "v"(s1[13]), [s14] "v"(s1[14]), [s15] "v"(s1[15]),
+        [ms0] "v"(ms0), [sc2] "v"(sc2), [epo] "v"(epo), [one] "v"(kScaleOne), [pab] "s"(pab), [vtb] "s"(vtb)
+      : "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218",
+        "v219", "v220", "v221", "v222", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232",
+        "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245",
+        "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "vcc");
+}
+__device__ inline void pv_p8(floatx16 (&o)[16], const floatx16 &s1, float ms0, float sc2, int epo,
+                             uint32_t pab, uint32_t vtb, PvOut<true> &r) {
+  uint32_t pa, va;
+  asm volatile(
+      "v_mbcnt_lo_u32_b32 v224, -1, 0\n\t"
+      "v_mbcnt_hi_u32_b32 v224, -1, v224\n\t"
+      "v_lshl_add_u32 %[pa], v224, 4, %[pab]\n\t"
+      "v_lshlrev_b32 %[va], 3, v224\n\t"
+      "v_and_b32 %[va], 0x78, %[va]\n\t"
+      "v_bfe_u32 v225, v224, 4, 1\n\t"
+      "v_lshl_or_b32 %[va], v225, 8, %[va]\n\t"
+      "v_bfe_u32 v226, v224, 5, 1\n\t"
+      "v_xor_b32 v225, v225, v226\n\t"
+      "v_lshl_or_b32 %[va], v225, 7, %[va]\n\t"
+      "v_add_u32 %[va], %[vtb], %[va]\n\t"
+      "ds_read_b128 v[206:209], %[pa]\n\t"
+      "ds_read_b128 v[210:213], %[pa] offset:1024\n\t"
+      "ds_read_b64_tr_b8 v[232:233], %[va]\n\t"
+      "ds_read_b64_tr_b8 v[234:235], %[va] offset:1024\n\t"
+      "ds_read_b64_tr_b8 v[236:237], %[va] offset:18432\n\t"
+      "ds_read_b64_tr_b8 v[238:239], %[va] offset:19456\n\t"
+      "ds_read_b64_tr_b8 v[240:241], %[va] offset:512\n\t"
+      "ds_read_b64_tr_b8 v[242:243], %[va] offset:1536\n\t"
+      "ds_read_b64_tr_b8 v[244:245], %[va] offset:18944\n\t"
+      "ds_read_b64_tr_b8 v[246:247], %[va] offset:19968\n\t"
+      "v_max3_f32 v224, %[s0], %[s1], %[s2]\n\t"
+      "v_max3_f32 v225, %[s3], %[s4], %[s5]\n\t"
+      "v_max3_f32 v226, %[s6], %[s7], %[s8]\n\t"
+      "v_max3_f32 v227, %[s9], %[s10], %[s11]\n\t"
+      "v_max3_f32 v228, %[s12], %[s13], %[s14]\n\t"
+      "v_max3_f32 v224, v224, v225, v226\n\t"
+      "v_max3_f32 v227, v227, v228, %[s15]\n\t"
+      "v_max_f32 v224, v224, v227\n\t"
+      "v_mov_b32 v225, v224\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 v224, v225\n\t"
+      "v_max_f32 v224, v224, v225\n\t"
+      "v_mul_f32 v224, v224, %[sc2]\n\t"
+      "v_ceil_f32 v224, v224\n\t"
+      "v_max_f32 %[ms1], 0xce800000, v224\n\t"
+      "v_sub_f32 v222, 0x41000000, %[ms1]\n\t"
+      "v_max_f32 %[msx], %[ms0], %[ms1]\n\t"
+      "v_cmp_lt_f32 vcc, 0xce800000, %[msx]\n\t"
+      "v_mov_b32 v225, 0xff800000\n\t"
+      "v_cndmask_b32 v225, v225, %[msx], vcc\n\t"
+      "v_cmp_lt_f32 vcc, 0xff800000, %[mref]\n\t"
+      "v_cndmask_b32 %[mref], v225, %[mref], vcc\n\t"
+      "v_cmp_lt_f32 vcc, 0xff800000, %[mref]\n\t"
+      "v_sub_f32 v226, %[ms0], %[mref]\n\t"
+      "v_cndmask_b32 v226, 0, v226, vcc\n\t"
+      "v_sub_f32 v227, %[ms1], %[mref]\n\t"
+      "v_cndmask_b32 v227, 0, v227, vcc\n\t"
+      "v_max_f32 %[delta], v226, v227\n\t"
+      "v_min_f32 v226, 0x42800000, v226\n\t"
+      "v_min_f32 v227, 0x42800000, v227\n\t"
+      "v_max_f32 v226, 0xc2fe0000, v226\n\t"
+      "v_max_f32 v227, 0xc2fe0000, v227\n\t"
+      "v_cvt_i32_f32 %[di0], v226\n\t"
+      "v_cvt_i32_f32 %[di1], v227\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o0], v[232:239], v[206:213], %[o0], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_fma_f32 v224, %[s0], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s1], %[sc2], v222\n\t"
+      "v_fma_f32 v226, %[s2], %[sc2], v222\n\t"
+      "v_fma_f32 v227, %[s3], %[sc2], v222\n\t"
+      "ds_read_b64_tr_b8 v[248:249], %[va] offset:2048\n\t"
+      "ds_read_b64_tr_b8 v[250:251], %[va] offset:3072\n\t"
+      "ds_read_b64_tr_b8 v[252:253], %[va] offset:20480\n\t"
+      "ds_read_b64_tr_b8 v[254:255], %[va] offset:21504\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o1], v[240:247], v[206:213], %[o1], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "ds_read_b64_tr_b8 v[232:233], %[va] offset:2560\n\t"
+      "ds_read_b64_tr_b8 v[234:235], %[va] offset:3584\n\t"
+      "ds_read_b64_tr_b8 v[236:237], %[va] offset:20992\n\t"
+      "ds_read_b64_tr_b8 v[238:239], %[va] offset:22016\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o2], v[248:255], v[206:213], %[o2], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi4], v224, v225\n\t"
+      "ds_read_b64_tr_b8 v[240:241], %[va] offset:4096\n\t"
+      "ds_read_b64_tr_b8 v[242:243], %[va] offset:5120\n\t"
+      "ds_read_b64_tr_b8 v[244:245], %[va] offset:22528\n\t"
+      "ds_read_b64_tr_b8 v[246:247], %[va] offset:23552\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o3], v[232:239], v[206:213], %[o3], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_cvt_pk_fp8_f32 %[hi4], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf1], %[sf1], v228\n\t"
+      "v_fma_f32 v224, %[s4], %[sc2], v222\n\t"
+      "ds_read_b64_tr_b8 v[248:249], %[va] offset:4608\n\t"
+      "ds_read_b64_tr_b8 v[250:251], %[va] offset:5632\n\t"
+      "ds_read_b64_tr_b8 v[252:253], %[va] offset:23040\n\t"
+      "ds_read_b64_tr_b8 v[254:255], %[va] offset:24064\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o4], v[240:247], v[206:213], %[o4], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_fma_f32 v225, %[s5], %[sc2], v222\n\t"
+      "v_fma_f32 v226, %[s6], %[sc2], v222\n\t"
+      "v_fma_f32 v227, %[s7], %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "ds_read_b64_tr_b8 v[232:233], %[va] offset:6144\n\t"
+      "ds_read_b64_tr_b8 v[234:235], %[va] offset:7168\n\t"
+      "ds_read_b64_tr_b8 v[236:237], %[va] offset:24576\n\t"
+      "ds_read_b64_tr_b8 v[238:239], %[va] offset:25600\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o5], v[248:255], v[206:213], %[o5], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "ds_read_b64_tr_b8 v[240:241], %[va] offset:6656\n\t"
+      "ds_read_b64_tr_b8 v[242:243], %[va] offset:7680\n\t"
+      "ds_read_b64_tr_b8 v[244:245], %[va] offset:25088\n\t"
+      "ds_read_b64_tr_b8 v[246:247], %[va] offset:26112\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o6], v[232:239], v[206:213], %[o6], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi5], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi5], v226, v227 op_sel:[0,0,1]\n\t"
+      "ds_read_b64_tr_b8 v[248:249], %[va] offset:8192\n\t"
+      "ds_read_b64_tr_b8 v[250:251], %[va] offset:9216\n\t"
+      "ds_read_b64_tr_b8 v[252:253], %[va] offset:26624\n\t"
+      "ds_read_b64_tr_b8 v[254:255], %[va] offset:27648\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o7], v[240:247], v[206:213], %[o7], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf1], %[sf1], v228\n\t"
+      "v_fma_f32 v224, %[s8], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s9], %[sc2], v222\n\t"
+      "ds_read_b64_tr_b8 v[232:233], %[va] offset:8704\n\t"
+      "ds_read_b64_tr_b8 v[234:235], %[va] offset:9728\n\t"
+      "ds_read_b64_tr_b8 v[236:237], %[va] offset:27136\n\t"
+      "ds_read_b64_tr_b8 v[238:239], %[va] offset:28160\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o8], v[248:255], v[206:213], %[o8], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_fma_f32 v226, %[s10], %[sc2], v222\n\t"
+      "v_fma_f32 v227, %[s11], %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "ds_read_b64_tr_b8 v[240:241], %[va] offset:10240\n\t"
+      "ds_read_b64_tr_b8 v[242:243], %[va] offset:11264\n\t"
+      "ds_read_b64_tr_b8 v[244:245], %[va] offset:28672\n\t"
+      "ds_read_b64_tr_b8 v[246:247], %[va] offset:29696\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o9], v[232:239], v[206:213], %[o9], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "ds_read_b64_tr_b8 v[248:249], %[va] offset:10752\n\t"
+      "ds_read_b64_tr_b8 v[250:251], %[va] offset:11776\n\t"
+      "ds_read_b64_tr_b8 v[252:253], %[va] offset:29184\n\t"
+      "ds_read_b64_tr_b8 v[254:255], %[va] offset:30208\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o10], v[240:247], v[206:213], %[o10], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "v_cvt_pk_fp8_f32 %[hi6], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi6], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "ds_read_b64_tr_b8 v[232:233], %[va] offset:12288\n\t"
+      "ds_read_b64_tr_b8 v[234:235], %[va] offset:13312\n\t"
+      "ds_read_b64_tr_b8 v[236:237], %[va] offset:30720\n\t"
+      "ds_read_b64_tr_b8 v[238:239], %[va] offset:31744\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o11], v[248:255], v[206:213], %[o11], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_add_f32 %[sf1], %[sf1], v228\n\t"
+      "v_fma_f32 v224, %[s12], %[sc2], v222\n\t"
+      "v_fma_f32 v225, %[s13], %[sc2], v222\n\t"
+      "v_fma_f32 v226, %[s14], %[sc2], v222\n\t"
+      "ds_read_b64_tr_b8 v[240:241], %[va] offset:12800\n\t"
+      "ds_read_b64_tr_b8 v[242:243], %[va] offset:13824\n\t"
+      "ds_read_b64_tr_b8 v[244:245], %[va] offset:31232\n\t"
+      "ds_read_b64_tr_b8 v[246:247], %[va] offset:32256\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o12], v[232:239], v[206:213], %[o12], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_fma_f32 v227, %[s15], %[sc2], v222\n\t"
+      "v_exp_f32 v224, v224\n\t"
+      "v_exp_f32 v225, v225\n\t"
+      "v_exp_f32 v226, v226\n\t"
+      "ds_read_b64_tr_b8 v[248:249], %[va] offset:14336\n\t"
+      "ds_read_b64_tr_b8 v[250:251], %[va] offset:15360\n\t"
+      "ds_read_b64_tr_b8 v[252:253], %[va] offset:32768\n\t"
+      "ds_read_b64_tr_b8 v[254:255], %[va] offset:33792\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o13], v[240:247], v[206:213], %[o13], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_exp_f32 v227, v227\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32 v228, v224, v225\n\t"
+      "v_add_f32 v229, v226, v227\n\t"
+      "ds_read_b64_tr_b8 v[232:233], %[va] offset:14848\n\t"
+      "ds_read_b64_tr_b8 v[234:235], %[va] offset:15872\n\t"
+      "ds_read_b64_tr_b8 v[236:237], %[va] offset:33280\n\t"
+      "ds_read_b64_tr_b8 v[238:239], %[va] offset:34304\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o14], v[248:255], v[206:213], %[o14], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      "v_cvt_pk_fp8_f32 %[hi7], v224, v225\n\t"
+      "v_cvt_pk_fp8_f32 %[hi7], v226, v227 op_sel:[0,0,1]\n\t"
+      "v_add_f32 v228, v228, v229\n\t"
+      "v_add_f32 %[sf1], %[sf1], v228\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %[o15], v[232:239], v[206:213], %[o15], %[one], %[epo] op_sel_hi:[0,0,0]\n\t"
+      : [o0] "+a"(o[0]), [o1] "+a"(o[1]), [o2] "+a"(o[2]), [o3] "+a"(o[3]), [o4] "+a"(o[4]), [o5] "+a"(o[5]),
+        [o6] "+a"(o[6]), [o7] "+a"(o[7]), [o8] "+a"(o[8]), [o9] "+a"(o[9]), [o10] "+a"(o[10]),
+        [o11] "+a"(o[11]), [o12] "+a"(o[12]), [o13] "+a"(o[13]), [o14] "+a"(o[14]), [o15] "+a"(o[15]),
+        [hi4] "=&v"(r.hi[0]), [hi5] "=&v"(r.hi[1]), [hi6] "=&v"(r.hi[2]), [hi7] "=&v"(r.hi[3]),
+        [sf1] "+v"(r.sf1), [ms1] "=&v"(r.ms1), [msx] "=&v"(r.msx), [delta] "=&v"(r.delta), [di0] "=&v"(r.di0),
+        [di1] "=&v"(r.di1), [mref] "+v"(r.mref), [pa] "=&v"(pa), [va] "=&v"(va)
+      : [s0] "v"(s1[0]), [s1] "v"(s1[1]), [s2] "v"(s1[2]), [s3] "v"(s1[3]), [s4] "v"(s1[4]), [s5] "v"(s1[5]),
+        [s6] "v"(s1[6]), [s7] "v"(s1[7]), [s8] "v"(s1[8]), [s9] "v"(s1[9]), [s10] "v"(s1[10]),
+        [s11] "v"(s1[11]), [s12] "v"(s1[12]), [s13] "v"(s1[13]), [s14] "v"(s1[14]), [s15] "v"(s1[15]),
+        [ms0] "v"(ms0), [sc2] "v"(sc2), [epo] "v"(epo), [one] "v"(kScaleOne), [pab] "s"(pab), [vtb] "s"(vtb)
+      : "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218",
+        "v219", "v220", "v221", "v222", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232",
+        "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245",
+        "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory", "vcc");
+}
+
 template <bool P8>
 __device__ inline void put_p(uint8_t *area, const POp<P8> &p) {
   int4v *d = (int4v *)(area + 16 * fresh_lane_id());
@@ -2523,6 +3071,15 @@ attention_fp8_kernel(AttnArgs a) {
       const int lim = rlen - s * kStage - 4 * hh;
       const KAddr ka0 = k_addr(tile);
       const bool more1 = uu + 1 < hi;
+      // the cursor of the unit after next (its page id is loaded in this
+      // stage: inside the one-block score phase, else after the scores); the
+      // next unit's cursor and page id stay for this stage's tile loads
+      const Cursor nx1 = nx;
+      const int32_t page1 = page;
+      if (more1) {
+        if (k == nst - 1) following = nx;
+        if (uu + 2 < hi) nx = wk.advance(nx, uu + 2);
+      }
       // tile uu has landed (this wave's share: the wait; every wave's: the
       // barrier), and every wave is done with the tile of unit uu - 2
       wait_direct_loads();
@@ -2537,68 +3094,33 @@ attention_fp8_kernel(AttnArgs a) {
       h0.sf0 = 0.f;
       if (more1 && !edge) {
         NextRow nr;
-        nr.page = page;
-        nr.ts = nx.s * kStage + 32 * load_half(wave) + 16 * (wave & 1);
-        nr.lmax = nx.lmax;
+        nr.page = page1;
+        nr.ts = nx1.s * kStage + 32 * load_half(wave) + 16 * (wave & 1);
+        nr.lmax = nx1.lmax;
         nr.mask = (1 << a.page_shift) - 1;
         nr.shift = a.page_shift;
         nr.np = npages;
         nr.pool = a.pool;
         nr.zero = a.zero_row;
+        nr.ts2 = nx.s * kStage + 32 * load_half(wave) + 16 * (wave & 1);
+        nr.lmax2 = nx.lmax;
+        nr.pt2 = pt_of(nx);
         qk01<QF8, P8>(ka0, q, rope, nr, ndst, sc2, h0);
         bad = bad || h0.badm != 0;
+        page = h0.pnext;
       } else {
-        const uint8_t *nrow = more1 ? stage_row(a, page, nx.s, nx.lmax, wave, &bad) : a.zero_row;
+        const uint8_t *nrow = more1 ? stage_row(a, page1, nx1.s, nx1.lmax, wave, &bad) : a.zero_row;
         floatx16 s0 = more1 ? scores_dma<QF8>(ka0, q, rope, nrow, ndst) : scores<QF8>(ka0, q, rope);
         if (edge) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) s0[r] = 8 * (r >> 2) + (r & 3) < lim ? s0[r] : kNegInf;
         }
         qk1<QF8, P8>(k_addr(tile + Tile8::kHalfBytes), q, rope, s0, sc2, h0);
+        if (more1 && uu + 2 < hi) page = page_of(nx);
       }
-      // the cursor of the unit two ahead and its page id (loaded now, used by
-      // the next stage's row address): in the p.v phase after its first chunk
-      // when there is one, where its issue overlaps the products
-      auto advance_next = [&]() __attribute__((always_inline)) {
-        if (more1) {
-          if (k == nst - 1) following = nx;
-          if (uu + 2 < hi) {
-            nx = wk.advance(nx, uu + 2);
-            page = page_of(nx);
-          }
-        }
-      };
-      if constexpr (!PREV) advance_next();
-      floatx16 s1 = h0.s1;
-      // the pending stage's probabilities and first value blocks: their LDS
-      // latency runs under the half-1 maximum
-      const uint32_t vt = prev_tile();
-      const VOff vo = v_offsets(fresh_lane_id());
-      POp<P8> pp;
-      int8v va[3];
-      if constexpr (PREV) {
-        pp = get_p<P8>(parea);
-        va[0] = lds_v(vt, vo, 0);
-        va[1] = lds_v(vt, vo, 1);
-      }
-      if (edge) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s1[r] = 8 * (r >> 2) + (r & 3) + 32 < lim ? s1[r] : kNegInf;
-      }
-      // half-1 ceiling; the reference starts only with a visible half
-      float m1 = half_max(s1);
-      m1 = __builtin_fmaxf(m1, other_half(m1, hh));
       const float ms0 = h0.ms0;
-      const float ms1 = __builtin_fmaxf(__builtin_ceilf(m1 * sc2), kHidden);
-      const float msx = __builtin_fmaxf(ms0, ms1);
-      const bool started = mref > kNegInf;
-      mref = started ? mref : (msx > kHidden ? msx : kNegInf);   // nothing accumulated yet
-      const bool ref = mref > kNegInf;
-      const float d0 = ref ? ms0 - mref : 0.f;
-      const float d1 = ref ? ms1 - mref : 0.f;
-      const float delta = __builtin_fmaxf(d0, d1);
-      const float msub1 = ms1 - kPShift;
-      float sf1 = 0.f;
+      float ms1, msx, delta, sf1 = 0.f;
+      int di0, di1;
       POp<P8> pc;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -2606,25 +3128,53 @@ attention_fp8_kernel(AttnArgs a) {
         if constexpr (!P8) pc.lo[g] = h0.lo[g];
       }
       if constexpr (PREV) {
-        // the pending p.v in eight chunks of two value blocks, V read two
-        // blocks ahead; the odd chunks carry groups 4..7 of this stage's
-        // probabilities, the first the half-1 maximum above
+        // the pending p.v and this stage's half-1 softmax as one block
+        floatx16 s1 = h0.s1;
+        if (edge) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          if (c & 1) p_group<P8>(s1, s1, 4 + (c >> 1), sc2, msub1, pc, sf1);
+          for (int r = 0; r < 16; ++r) s1[r] = 8 * (r >> 2) + (r & 3) + 32 < lim ? s1[r] : kNegInf;
+        }
+        PvOut<P8> r;
+        r.sf1 = 0.f;
+        r.mref = mref;
+        const uint32_t pab = lds_base + kBufs * Tile8::kBytes + wave * Stage8::kWaveBytes;
+        if constexpr (P8) pv_p8(oacc, s1, ms0, sc2, epend, pab, prev_tile(), r);
+        else pv_p16(oacc, s1, ms0, sc2, epend, pab, prev_tile(), r);
+        mref = r.mref;
+        ms1 = r.ms1;
+        msx = r.msx;
+        delta = r.delta;
+        di0 = r.di0;
+        di1 = r.di1;
+        sf1 = r.sf1;
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int d = 2 * c + j;
-            if (d + 2 < kDv / 32) va[(d + 2) % 3] = lds_v(vt, vo, d + 2);
-            oacc[d] = mma_pv_hi(va[d % 3], pp.hi, oacc[d], epend);
-            if constexpr (!P8) oacc[d] = mma_pv_lo(va[d % 3], pp.lo, oacc[d], epend);
-          }
-          chunk_order<P8>();
-          if (c == 0) advance_next();
+        for (int g = 0; g < 4; ++g) {
+          pc.hi[4 + g] = r.hi[g];
+          if constexpr (!P8) pc.lo[4 + g] = r.lo[g];
         }
       } else {
+        // the first stage of a piece: no pending p.v
+        floatx16 s1 = h0.s1;
+        if (edge) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s1[r] = 8 * (r >> 2) + (r & 3) + 32 < lim ? s1[r] : kNegInf;
+        }
+        // half-1 ceiling; the reference starts only with a visible half
+        float m1 = half_max(s1);
+        m1 = __builtin_fmaxf(m1, other_half(m1, hh));
+        ms1 = __builtin_fmaxf(__builtin_ceilf(m1 * sc2), kHidden);
+        msx = __builtin_fmaxf(ms0, ms1);
+        const bool started = mref > kNegInf;
+        mref = started ? mref : (msx > kHidden ? msx : kNegInf);   // nothing accumulated yet
+        const bool ref = mref > kNegInf;
+        const float d0 = ref ? ms0 - mref : 0.f;
+        const float d1 = ref ? ms1 - mref : 0.f;
+        delta = __builtin_fmaxf(d0, d1);
+        const float msub1 = ms1 - kPShift;
 #pragma unroll
         for (int g = 4; g < 8; ++g) p_group<P8>(s1, s1, g, sc2, msub1, pc, sf1);
+        di0 = (int)__builtin_fmaxf(__builtin_fminf(d0, kMaxUp), -127.f);
+        di1 = (int)__builtin_fmaxf(__builtin_fminf(d1, kMaxUp), -127.f);
       }
       put_p<P8>(parea, pc);
       // the stage sums join the row sums in the reference frame, each half
@@ -2633,13 +3183,13 @@ attention_fp8_kernel(AttnArgs a) {
       // scale block 0 (lanes 0..31) covers half 0, block 1 (lanes 32..63)
       // half 1.
       const float lf_old = lsum_f;
-      const int di0 = (int)__builtin_fmaxf(__builtin_fminf(d0, kMaxUp), -127.f);
-      const int di1 = (int)__builtin_fmaxf(__builtin_fminf(d1, kMaxUp), -127.f);
       epend = kScaleOne + (hh ? di1 : di0);
       lsum_f += __builtin_ldexpf(h0.sf0, di0) + __builtin_ldexpf(sf1, di1);
       const bool move = PREV && delta > kMaxUp;
       if (PREV && __any(move)) {
-        // exact power of two; the pending product is already in oacc
+        // exact power of two; the pending product is already in oacc (the
+        // p.v block's last products may still be writing it: drain them)
+        asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
         const float alpha = move ? __builtin_ldexpf(1.0f, -(int)__builtin_fminf(delta, 1024.f)) : 1.0f;
         rescale_o(oacc, alpha);
         if (move) {

@@ -165,7 +165,9 @@ def one_half(terms, dma_steps=(), softmax=None):
 def row_ops():
     """The next tile's row address for this lane's loads, into v[230:231],
     spread over the first steps' products (v224..v231 are free until the
-    half-0 softmax).  The lane loads token t = ts + tok_slot(slot) of the next
+    half-0 softmax); on the way, the load of this lane's page id of the unit
+    after next (token ts2 + tok_slot(slot) of the table row at pt2, entry 0
+    past lmax2), as fetch_page does.  The lane loads token t = ts + tok_slot(slot) of the next
     unit, slot = (l & 15) ^ 8 l4 (ts: that unit's stage start plus the wave's
     half and slot-block offset), 16 bytes at 16 (l >> 4) of its row: page
     (page << shift) + (t & mask) of the pool, or the zero row when t is past
@@ -183,6 +185,15 @@ def row_ops():
         "v_and_b32 v226, 4, v226",
         "v_mul_u32_u24 v226, 3, v226",
         "v_xor_b32 v225, v225, v226",
+        # the page id of the unit after next for the same slot (its table row
+        # at pt2), loaded before the tile loads so vmcnt(9) waits for it alone
+        "v_add_u32 v226, %[ts2], v225",
+        "v_cmp_gt_i32 vcc, %[lmax2], v226",
+        "v_lshrrev_b32 v226, %[shift], v226",
+        "v_cndmask_b32 v226, 0, v226, vcc",
+        "v_mov_b32 v227, 0",
+        "v_lshl_add_u64 v[228:229], v[226:227], 2, %[pt2]",
+        "global_load_dword %[pnext], v[228:229], off",
         "v_add_u32 v225, %[ts], v225",            # t
         "v_cmp_gt_i32 %[inm], %[lmax], v225",     # t < lmax
         "v_and_b32 v226, %[mask], v225",
@@ -258,9 +269,167 @@ def both_halves(terms, p8):
             reads(gs + 2)
     assert k == len(ops) and ld == 9 and not rops
     e(q("s_mov_b32 m0, %[m0s]"))
+    e(q("s_waitcnt vmcnt(9)"))       # the page id (the tile loads may still run)
     e(q("s_nop 15"))
     e(q("s_nop 3"))
     return out
+
+
+VT = ["v[232:239]", "v[240:247]", "v[248:255]"]   # value operand tuples, block % 3
+PP_HI, PP_LO = "v[206:213]", "v[214:221]"        # the pending stage's P operand
+
+
+def half1_ops(p8):
+    """The half-1 softmax of the p.v block: row maximum of s1 over the lane and
+    its partner, ceiling ms1, the reference logic (mref starts with the first
+    visible half; d0, d1 the halves' ceilings above it and their E8M0
+    exponents di, clamped to [-127, 64]), then groups 4..7 of
+    p' = 2^(s1 * sc2 - ms1 + 8).  Temps v222, v224..v231."""
+    ops = [
+        "v_max3_f32 v224, %[s0], %[s1], %[s2]",
+        "v_max3_f32 v225, %[s3], %[s4], %[s5]",
+        "v_max3_f32 v226, %[s6], %[s7], %[s8]",
+        "v_max3_f32 v227, %[s9], %[s10], %[s11]",
+        "v_max3_f32 v228, %[s12], %[s13], %[s14]",
+        "v_max3_f32 v224, v224, v225, v226",
+        "v_max3_f32 v227, v227, v228, %[s15]",
+        "v_max_f32 v224, v224, v227",
+        "v_mov_b32 v225, v224",
+        "s_nop 1",
+        "v_permlane32_swap_b32 v224, v225",
+        "v_max_f32 v224, v224, v225",
+        "v_mul_f32 v224, v224, %[sc2]",
+        "v_ceil_f32 v224, v224",
+        f"v_max_f32 %[ms1], {NEG_2_30}, v224",
+        "v_sub_f32 v222, 0x41000000, %[ms1]",       # 8 - ms1
+        "v_max_f32 %[msx], %[ms0], %[ms1]",
+        f"v_cmp_lt_f32 vcc, {NEG_2_30}, %[msx]",
+        "v_mov_b32 v225, 0xff800000",                    # (a literal and vcc both need the constant bus)
+        "v_cndmask_b32 v225, v225, %[msx], vcc",         # a visible half: msx, else -inf
+        "v_cmp_lt_f32 vcc, 0xff800000, %[mref]",
+        "v_cndmask_b32 %[mref], v225, %[mref], vcc",     # keep a started reference
+        "v_cmp_lt_f32 vcc, 0xff800000, %[mref]",
+        "v_sub_f32 v226, %[ms0], %[mref]",
+        "v_cndmask_b32 v226, 0, v226, vcc",              # d0
+        "v_sub_f32 v227, %[ms1], %[mref]",
+        "v_cndmask_b32 v227, 0, v227, vcc",              # d1
+        "v_max_f32 %[delta], v226, v227",
+        "v_min_f32 v226, 0x42800000, v226",
+        "v_min_f32 v227, 0x42800000, v227",
+        "v_max_f32 v226, 0xc2fe0000, v226",
+        "v_max_f32 v227, 0xc2fe0000, v227",
+        "v_cvt_i32_f32 %[di0], v226",
+        "v_cvt_i32_f32 %[di1], v227",
+    ]
+    for g in range(4, 8):
+        for i in range(4):
+            ops.append(f"v_fma_f32 v{224 + i}, %[s{4 * (g - 4) + i}], %[sc2], v222")
+        for i in range(4):
+            ops.append(f"v_exp_f32 v{224 + i}, v{224 + i}")
+        ops += ["s_nop 0",
+                "v_add_f32 v228, v224, v225",
+                "v_add_f32 v229, v226, v227",
+                f"v_cvt_pk_fp8_f32 %[hi{g}], v224, v225",
+                f"v_cvt_pk_fp8_f32 %[hi{g}], v226, v227 op_sel:[0,0,1]",
+                "v_add_f32 v228, v228, v229",
+                "v_add_f32 %[sf1], %[sf1], v228"]
+        if not p8:
+            ops += [f"v_cvt_pk_f32_fp8 v[228:229], %[hi{g}]",
+                    f"v_cvt_pk_f32_fp8_sdwa v[230:231], %[hi{g}] src0_sel:WORD_1",
+                    "v_sub_f32 v228, v224, v228",
+                    "v_sub_f32 v229, v225, v229",
+                    "v_sub_f32 v230, v226, v230",
+                    "v_sub_f32 v231, v227, v231",
+                    f"v_cvt_pk_bf8_f32 %[lo{g}], v228, v229",
+                    f"v_cvt_pk_bf8_f32 %[lo{g}], v230, v231 op_sel:[0,0,1]"]
+    return ops
+
+
+def v_reads(e, d):
+    base = (d >> 1) * STEP + (d & 1) * 512
+    lo = int(VT[d % 3][2:].split(":")[0])
+    for i, off in enumerate((0, 1024, HALF, HALF + 1024)):
+        o = base + off
+        e(q(f"ds_read_b64_tr_b8 v[{lo + 2 * i}:{lo + 2 * i + 1}], %[va]" + (f" offset:{o}" if o else "")))
+
+
+def pv_body(p8):
+    """The pending stage's p.v (16 value blocks of the tile at vtb, the P
+    operand from the wave's staging area at pab, scale epo) with the half-1
+    softmax and the reference logic between the products."""
+    out = []
+    e = out.append
+    e(q("v_mbcnt_lo_u32_b32 v224, -1, 0"))
+    e(q("v_mbcnt_hi_u32_b32 v224, -1, v224"))
+    e(q("v_lshl_add_u32 %[pa], v224, 4, %[pab]"))
+    # value block 0 offset of lane l = (l0, k = l1..l3, l4, l5): 8 l0 + 16 k + 128 (l4 ^ l5) + 256 l4
+    for op in ["v_lshlrev_b32 %[va], 3, v224",
+               "v_and_b32 %[va], 0x78, %[va]",
+               "v_bfe_u32 v225, v224, 4, 1",
+               "v_lshl_or_b32 %[va], v225, 8, %[va]",
+               "v_bfe_u32 v226, v224, 5, 1",
+               "v_xor_b32 v225, v225, v226",
+               "v_lshl_or_b32 %[va], v225, 7, %[va]",
+               "v_add_u32 %[va], %[vtb], %[va]"]:
+        e(q(op))
+    e(q(f"ds_read_b128 v[206:209], %[pa]"))
+    e(q(f"ds_read_b128 v[210:213], %[pa] offset:1024"))
+    if not p8:
+        e(q(f"ds_read_b128 v[214:217], %[pa] offset:2048"))
+        e(q(f"ds_read_b128 v[218:221], %[pa] offset:3072"))
+    v_reads(e, 0)
+    v_reads(e, 1)
+    ops = half1_ops(p8)
+    # the maximum and the reference logic run under the reads' latency
+    head = next(i for i, op in enumerate(ops) if op.startswith("v_fma_f32"))
+    for op in ops[:head]:
+        e(q(op))
+    ops = ops[head:]
+    terms = 1 if p8 else 2
+    per = -(-len(ops) // (16 * terms - 1))
+    k = 0
+    for d in range(16):
+        e(q("s_waitcnt lgkmcnt(4)") if d < 15 else q("s_waitcnt lgkmcnt(0)"))
+        e(q(f"v_mfma_scale_f32_32x32x64_f8f6f4 %[o{d}], {VT[d % 3]}, {PP_HI}, %[o{d}], %[one], %[epo] op_sel_hi:[0,0,0]"))
+        n = per if (d, 0) != (15, terms - 1) else len(ops) - k
+        for op in ops[k:k + n]:
+            e(q(op))
+        k += n
+        if not p8:
+            e(q(f"v_mfma_scale_f32_32x32x64_f8f6f4 %[o{d}], {VT[d % 3]}, {PP_LO}, %[o{d}], %[one], %[epo] op_sel_hi:[0,0,0] blgp:1"))
+            n = per if d < 15 else len(ops) - k
+            for op in ops[k:k + n]:
+                e(q(op))
+            k += n
+        if d + 2 < 16:
+            v_reads(e, d + 2)
+    assert k == len(ops)
+    return out
+
+
+def pv_function(p8):
+    name = f"pv_{'p8' if p8 else 'p16'}"
+    parts = ["floatx16 (&o)[16]", "const floatx16 &s1", "float ms0", "float sc2", "int epo", "uint32_t pab",
+             "uint32_t vtb", f"PvOut<{'true' if p8 else 'false'}> &r"]
+    outs = [f'[o{d}] "+a"(o[{d}])' for d in range(16)]
+    outs += [f'[hi{g}] "=&v"(r.hi[{g - 4}])' for g in range(4, 8)]
+    if not p8:
+        outs += [f'[lo{g}] "=&v"(r.lo[{g - 4}])' for g in range(4, 8)]
+    outs += ['[sf1] "+v"(r.sf1)', '[ms1] "=&v"(r.ms1)', '[msx] "=&v"(r.msx)', '[delta] "=&v"(r.delta)',
+             '[di0] "=&v"(r.di0)', '[di1] "=&v"(r.di1)', '[mref] "+v"(r.mref)', '[pa] "=&v"(pa)',
+             '[va] "=&v"(va)']
+    ins = [f'[s{i}] "v"(s1[{i}])' for i in range(16)]
+    ins += ['[ms0] "v"(ms0)', '[sc2] "v"(sc2)', '[epo] "v"(epo)', '[one] "v"(kScaleOne)', '[pab] "s"(pab)',
+            '[vtb] "s"(vtb)']
+    clob = [f'"v{r}"' for r in list(range(206, 223)) + list(range(224, 256))] + ['"memory"', '"vcc"']
+    s = signature(f"__device__ inline void {name}(", parts)
+    s += "  uint32_t pa, va;\n"
+    s += "  asm volatile(\n" + "\n".join("      " + l for l in pv_body(p8)) + "\n"
+    s += "      : " + wrap(outs) + "\n"
+    s += "      : " + wrap(ins) + "\n"
+    s += "      : " + wrap(clob) + ");\n"
+    s += "}\n"
+    return name, s
 
 
 def function(kind, split, p8=False):
@@ -298,9 +467,11 @@ def function(kind, split, p8=False):
         if not p8:
             outs += [f'[lo{g}] "=&v"(o.lo[{g}])' for g in range(4)]
         outs += ['[m0s] "=&s"(saved)', '[inm] "=&s"(inm)', '[badm] "=&s"(o.badm)']
+        outs.append('[pnext] "=&v"(o.pnext)')
         ins += ['[page] "v"(nr.page)', '[ts] "s"(nr.ts)', '[lmax] "s"(nr.lmax)', '[mask] "s"(nr.mask)',
                 '[shift] "s"(nr.shift)', '[np] "s"(nr.np)', '[pool] "s"(nr.pool)', '[zero] "s"(nr.zero)',
-                '[dst] "s"(dst)', '[sc2] "v"(sc2)']
+                '[ts2] "s"(nr.ts2)', '[lmax2] "s"(nr.lmax2)', '[pt2] "s"(nr.pt2)', '[dst] "s"(dst)',
+                '[sc2] "v"(sc2)']
         body = both_halves(terms, p8)
         clob_regs = list(range(S0, S0 + 16)) + [222] + list(range(224, 256))
         flags.append('"scc"')
@@ -324,7 +495,7 @@ def function(kind, split, p8=False):
 
 
 def all_functions():
-    out = []
+    out = [pv_function(False), pv_function(True)]
     for split in (True, False):
         out.append(function("scores", split))
         out.append(function("scores_dma", split))

@@ -93,3 +93,17 @@ def test_score_blocks_match_their_generator():
     gen = os.path.join(CSRC, "gen_score_blocks.py")
     res = subprocess.run([sys.executable, gen, "--check"], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0, res.stdout + res.stderr
+
+
+def test_asm_blocks_assemble(tmp_path):
+    # the -S output above is not run through the assembler's operand checks
+    # (constant-bus limits, operand kinds); an object build is
+    hipcc = _hipcc()
+    if hipcc is None:
+        pytest.skip("hipcc not available")
+    from decode_context_parallelism_amd import build
+    flags = [f for f in build.HIPCC_FLAGS if f != "-fPIC"]
+    cmd = [hipcc, *flags, "-c", "--cuda-device-only", os.path.join(CSRC, "attention_fp8.hip"),
+           "-o", str(tmp_path / "attention_fp8.o")]
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stderr[-3000:]

@@ -1,9 +1,11 @@
 """The merged score block of the FP8-cache kernel computes the next tile's
-row addresses in inline asm (gen_score_blocks.row_ops).  This emulates that
-instruction sequence lane by lane on the host and checks it against the
-rules the C++ path (stage_row) applies: token t of the lane's load slot, the
-zero row past the row length or for a page outside the pool, the page-range
-flag only for tokens inside the row.  No GPU needed."""
+row addresses, and loads the page ids of the unit after next, in inline asm
+(gen_score_blocks.row_ops).  This emulates that instruction sequence lane by
+lane on the host and checks it against the rules the C++ path applies
+(stage_row, fetch_page): token t of the lane's load slot, the zero row past
+the row length or for a page outside the pool, the page-range flag only for
+tokens inside the row, the page-table entry of the token (entry 0 past the
+row).  No GPU needed."""
 import os
 import random
 import re
@@ -24,6 +26,14 @@ def tok_slot(t):
 
 def load_slot(wave, lane):
     return (16 * (wave & 1) + (lane & 15)) ^ (8 * ((lane >> 4) & 1))
+
+
+def page_addresses(wave, s2, lmax2, shift, pt2):
+    out = []
+    for lane in range(64):
+        t = s2 * 64 + 32 * (wave >> 1) + tok_slot(load_slot(wave, lane))
+        out.append(pt2 + 4 * ((t >> shift) if t < lmax2 else 0))
+    return out
 
 
 def reference(wave, s, lmax, pages, shift, num_pages, pool, zero):
@@ -51,6 +61,7 @@ def emulate(ops, sregs):
     %[page] is per lane (a list)."""
     v = [dict() for _ in range(64)]          # per-lane VGPRs
     masks = {}                               # SGPR pairs / vcc as 64-bit lane masks
+    loads = []                               # per-lane addresses of each global load
 
     def val(lane, x):
         x = x.strip()
@@ -79,6 +90,9 @@ def emulate(ops, sregs):
             x, y = masks[a[1].strip("%[]")], masks[a[2].strip("%[]")]
             masks[a[0].strip("%[]")] = (x & ~y) & M64 if name == "s_andn2_b64" else x & y
             continue
+        if name == "global_load_dword":
+            loads.append([val(lane, a[1]) for lane in range(64)])
+            continue
         if name.startswith("v_cmp"):
             m = 0
             for lane in range(64):
@@ -93,7 +107,7 @@ def emulate(ops, sregs):
             elif name == "v_mbcnt_hi_u32_b32":    # plus those of the high half
                 put(lane, a[0], val(lane, a[2]) + max(lane - 32, 0))
             elif name == "v_lshrrev_b32":
-                put(lane, a[0], (val(lane, a[2]) & M32) >> val(lane, a[1]))
+                put(lane, a[0], (val(lane, a[2]) & M32) >> (val(lane, a[1]) & 31))
             elif name == "v_and_b32":
                 put(lane, a[0], val(lane, a[1]) & val(lane, a[2]))
             elif name == "v_xor_b32":
@@ -116,22 +130,27 @@ def emulate(ops, sregs):
             else:
                 raise AssertionError(f"unemulated instruction {name}")
     rows = [v[lane][230] | (v[lane][231] << 32) for lane in range(64)]
-    return rows, masks["badm"] != 0
+    return rows, masks["badm"] != 0, loads
 
 
-def _case(rng, wave, shift, s, lmax, num_pages, bad_pages):
+def _case(rng, wave, shift, s, lmax, num_pages, bad_pages, s2=None, lmax2=None):
     pages = [rng.randrange(num_pages) for _ in range(64)]
     for lane in rng.sample(range(64), bad_pages):
         pages[lane] = rng.choice([-1, -7, num_pages, num_pages + 123, 0x7FFFFFFF])
     pool, zero = 0x7F3A_0000_0000 + 256 * rng.randrange(1 << 20), 0x7F00_1234_5600
     ts = s * 64 + 32 * (wave >> 1) + 16 * (wave & 1)
     np_ = min(num_pages, 0x7FFFFFFF)
+    s2 = s + 1 if s2 is None else s2
+    lmax2 = lmax + 64 if lmax2 is None else lmax2
+    pt2 = 0x7E00_0000_0000 + 4 * rng.randrange(1 << 20)
     sregs = {"page": [p & M32 for p in pages], "ts": ts, "lmax": lmax, "mask": (1 << shift) - 1,
-             "shift": shift, "np": np_, "pool": pool, "zero": zero}
-    got_rows, got_bad = emulate(G.row_ops(), sregs)
+             "shift": shift, "np": np_, "pool": pool, "zero": zero,
+             "ts2": s2 * 64 + 32 * (wave >> 1) + 16 * (wave & 1), "lmax2": lmax2, "pt2": pt2}
+    got_rows, got_bad, loads = emulate(G.row_ops(), sregs)
     want_rows, want_bad = reference(wave, s, lmax, pages, shift, num_pages, pool, zero)
     assert got_rows == want_rows
     assert got_bad == want_bad
+    assert loads == [page_addresses(wave, s2, lmax2, shift, pt2)]
 
 
 def test_row_ops_match_stage_row_rules():
@@ -142,7 +161,9 @@ def test_row_ops_match_stage_row_rules():
         s = rng.randrange(4096)
         lmax = s * 64 + rng.randrange(-8, 72)          # row ends before, inside or after the stage
         num_pages = rng.choice([1, 17, 5000, 1 << 20])
-        _case(rng, wave, shift, s, lmax, num_pages, rng.choice([0, 0, 1, 5]))
+        s2 = rng.choice([s + 1, rng.randrange(4096)])      # the unit after next: any row position
+        lmax2 = s2 * 64 + rng.randrange(-8, 72)
+        _case(rng, wave, shift, s, lmax, num_pages, rng.choice([0, 0, 1, 5]), s2, lmax2)
 
 
 def test_row_ops_flag_only_visible_bad_pages():

@@ -593,10 +593,11 @@ template <> struct Half0<false> { floatx16 s1; float ms0, sf0; int hi[4], lo[4];
 template <> struct Half0<true> { floatx16 s1; float ms0, sf0; int hi[4]; uint64_t badm; int32_t pnext; };
 
 // The one-block score phase computes the next tile's row addresses itself
-// (the same token, page and zero-row rules as stage_row), while its first
-// key reads are in flight: this lane's page id of the next unit and the
-// wave-uniform rest.  Row indices are 32-bit: a pool of 2^32 rows would be
-// 2.4 TB.
+// (the same token, page and zero-row rules as stage_row) under its first
+// steps' products, and loads the page ids of the unit after next (as
+// fetch_page does): this lane's page id of the next unit and the
+// wave-uniform rest.  Row indices are 32-bit: the geometry check keeps a pool
+// below 2^31 token rows.
 struct NextRow {
   int32_t page;            // this lane's page id (vector)
   int ts;                  // 64 s + 32 (wave's half) + 16 (wave & 1): the lane's token less its slot part

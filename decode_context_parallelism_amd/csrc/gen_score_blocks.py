@@ -20,7 +20,11 @@ are written by this script rather than by hand:
                             products) and then its loads, half 1 with the
                             half-0 softmax, the key reads two steps ahead
                             across the halves; the half-0 scores stay in
-                            v[206:221].
+                            v[206:221];
+  pv_{p16,p8}               the pending stage's p.v: 16 value blocks' scaled
+                            products (transposing reads two blocks ahead in
+                            v[232:255], P in v[206:221]) with the half-1
+                            softmax and the reference logic between them.
 
 python gen_score_blocks.py --write   rewrite those functions in attention_fp8.hip
 python gen_score_blocks.py --check   exit 1 if the source differs from the generator
@@ -165,14 +169,14 @@ def one_half(terms, dma_steps=(), softmax=None):
 def row_ops():
     """The next tile's row address for this lane's loads, into v[230:231],
     spread over the first steps' products (v224..v231 are free until the
-    half-0 softmax); on the way, the load of this lane's page id of the unit
-    after next (token ts2 + tok_slot(slot) of the table row at pt2, entry 0
-    past lmax2), as fetch_page does.  The lane loads token t = ts + tok_slot(slot) of the next
-    unit, slot = (l & 15) ^ 8 l4 (ts: that unit's stage start plus the wave's
-    half and slot-block offset), 16 bytes at 16 (l >> 4) of its row: page
-    (page << shift) + (t & mask) of the pool, or the zero row when t is past
-    the row length (lmax) or the page is outside the pool (also reported in
-    badm)."""
+    half-0 softmax).  The lane loads token t = ts + tok_slot(slot) of the
+    next unit, slot = (l & 15) ^ 8 l4 (ts: that unit's stage start plus the
+    wave's half and slot-block offset), 16 bytes at 16 (l >> 4) of its row:
+    row (page << shift) + (t & mask) of the pool, or the zero row when t is
+    past the row length (lmax) or the page is outside the pool (also reported
+    in badm).  On the way, the load of this lane's page id of the unit after
+    next, as fetch_page does: entry (ts2 + tok_slot(slot)) >> shift of the
+    table row at pt2, entry 0 past lmax2."""
     return [
         "v_mbcnt_lo_u32_b32 v224, -1, 0",
         "v_mbcnt_hi_u32_b32 v224, -1, v224",

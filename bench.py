@@ -43,6 +43,8 @@ PEAK_MFMA_BF16_TFLOPS = 2500.0
 PEAK_MFMA_FP8_TFLOPS = 5000.0
 # flops per clock per CU of dense BF16 MFMA on gfx950 (4 SIMDs x 1024)
 BF16_FLOPS_PER_CLK_CU = 4096
+# the chip's peak engine clock
+MAX_CLOCK_GHZ = 2.4
 INFINITY_CACHE_BYTES = 256 << 20
 # sources that fix the attention kernel's code and work partition: the counter
 # summaries under profiles/ record their digest
@@ -197,6 +199,14 @@ def read_mfma_busy(workload, digest):
         return None, "counter summary incomplete"
     if "mfma_busy_frac_at_2_4_ghz" in kv:
         busy["mfma_busy_frac_at_2_4_ghz"] = float(kv["mfma_busy_frac_at_2_4_ghz"])
+    if busy["clock_ghz"] > MAX_CLOCK_GHZ:
+        # the GPU-active counter's window outlasts a launch of a few tens of
+        # microseconds, so a clock above the chip's peak marks both figures
+        # derived from it as unusable; the busy share at the peak clock
+        # divides by the launch's own duration and stands
+        busy["clock_ghz"] = busy["mfma_busy_frac"] = None
+        busy["note"] = (f"counted clock {float(kv['clock_ghz']):.3f} GHz exceeds the chip's "
+                        f"{MAX_CLOCK_GHZ} GHz: launch shorter than the counter window")
     busy["source"] = src
     return busy, src
 

@@ -50,6 +50,12 @@ def test_traffic_scales_both_counters(bench, tmp_path, monkeypatch):
     _write(prof / "attention_kernel_wl_mfma.md", "ee" * 32, mfma_busy_frac="0.5044", clock_ghz="2.001")
     busy, _ = bench.read_mfma_busy("wl", "ee" * 32)
     assert busy["mfma_busy_frac"] == 0.5044 and busy["clock_ghz"] == 2.001
+    # a counted clock above the chip's peak voids the figures derived from it
+    _write(prof / "attention_kernel_wl_mfma.md", "ee" * 32, mfma_busy_frac="0.0831",
+           clock_ghz="4.715", mfma_busy_frac_at_2_4_ghz="0.1633")
+    busy, _ = bench.read_mfma_busy("wl", "ee" * 32)
+    assert busy["mfma_busy_frac"] is None and busy["clock_ghz"] is None
+    assert busy["mfma_busy_frac_at_2_4_ghz"] == 0.1633 and "exceeds" in busy["note"]
 
 
 def test_committed_counter_summaries_parse(bench):

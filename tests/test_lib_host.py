@@ -67,6 +67,27 @@ def test_validate_rejects(field, value):
     assert ops.validate(_geom(**{field: value})) == _lib.E_INVALID
 
 
+@pytest.mark.parametrize("ok,bad", [
+    # pool token rows (num_blocks x block_size) stay below 2^31: the kernels
+    # index token rows and pages with 32-bit integers
+    (dict(block_size=64, num_blocks=(1 << 25) - 1), dict(block_size=64, num_blocks=1 << 25)),
+    # a row's local capacity (max_local_pages x subpage size) stays below 2^31 tokens
+    (dict(max_local_pages=(1 << 27) - 1), dict(max_local_pages=1 << 27)),
+    # work units (sequences x head-row tiles x 32-token stages of that capacity)
+    (dict(batch=256, qlen=8, num_heads=128, max_local_pages=(1 << 21) - 2),
+     dict(batch=256, qlen=8, num_heads=128, max_local_pages=1 << 21)),
+    # head-rows x 576 query elements
+    (dict(batch=3728269, qlen=1, num_heads=1), dict(batch=3728270, qlen=1, num_heads=1)),
+    # block-table entries
+    (dict(batch=1 << 16, max_blocks_per_seq=(1 << 15) - 1), dict(batch=1 << 16, max_blocks_per_seq=1 << 15)),
+])
+def test_validate_size_limits(ok, bad):
+    # each limit of 32-bit device index arithmetic: the largest geometry below
+    # it is accepted, the first one at it refused before any launch
+    assert ops.validate(_geom(**ok)) == _lib.OK
+    assert ops.validate(_geom(**bad)) == _lib.E_INVALID
+
+
 def test_validate_rejects_bad_dtype():
     g = _geom().c()
     g.kv_dtype = 7

@@ -143,7 +143,7 @@ __global__ void __launch_bounds__(256) merge_segments_dense_kernel(
 // Persistent layout: finish every (sequence, head-row tile) whose stages were
 // split over several workgroups, and give sequences with no rank-local token
 // their empty result.  Tiles finished inside one workgroup are left alone.
-// One workgroup per (sequence, tile, group of 4 rpw rows), rows wave, wave + 4,
+// One workgroup per (sequence, tile, group of 4 RPW rows), rows wave, wave + 4,
 // ... of the group on each wave; the partials of a row are requested
 // kMergeBatch at a time, their base-2 LSEs with them, and merged against a
 // running maximum, so a row costs one dependent memory round trip per batch
